@@ -1,0 +1,202 @@
+/*
+ * qgemm.h -- C ABI of libqgemm.so: the quantized linear layer of LLM decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   W4A16     symmetric INT4 weights, zero offset 8, one bf16 scale per 128
+ *             consecutive input rows ("group 128"), bf16 activations, bf16
+ *             MFMA with fp32 accumulation, bf16 output.
+ *   W8A8-FP8  per-output-channel e4m3 weights with fp32 scales, dynamic
+ *             per-token e4m3 activations with fp32 scales, fp8 MFMA with fp32
+ *             accumulation, bf16 output.
+ *
+ * Sources of the operations (page title, then section):
+ *   [P1] "When quantization pays -- and when it does not" (mlinterviewnotes,
+ *        inference course ch. 04, section 4.4)
+ *   [P2] "Give Me BF16 or Give Me Death? Accuracy-Performance Trade-Offs in
+ *        LLM Quantization" (paper-graph-ui summary), section 3.4
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Matrices are row-major.  Weights are [K, N] (K = input dimension, the
+ * dimension the 128-row groups run along), activations [M, K], outputs
+ * [M, N].  bf16 values travel as their uint16 bit patterns.
+ *
+ * Every pointer argument is a DEVICE pointer (memory the caller allocated on
+ * the GPU, e.g. a torch tensor), except where stated.  The library never
+ * allocates, frees or keeps a pointer after returning; the caller owns every
+ * buffer.  Buffers passed to one call must not overlap unless stated.
+ *
+ * Every call validates its arguments on the host, synchronously, before it
+ * launches anything, and returns:
+ *   QG_ERR_NULL       a required pointer is NULL
+ *   QG_ERR_SHAPE      M < 0, N <= 0 or K <= 0, K % 128 != 0, N % 16 != 0,
+ *                     or a size too large for 32-bit indexing of one matrix
+ *                     (shapes are rejected, never padded)
+ *   QG_ERR_ALIGN      a matrix pointer is not 16-byte aligned (scale and
+ *                     per-row / per-column vectors: 4-byte aligned)
+ *   QG_ERR_WORKSPACE  the workspace is smaller than the size query returns
+ *   QG_ERR_HIP        the kernel launch itself failed (hipGetLastError)
+ * M == 0 is valid and launches nothing.  On success the work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream) and the call returns
+ * QG_OK without waiting for it.  Device-side data conditions are not checked:
+ * non-finite inputs are outside the contract.  Calls are thread-safe; the
+ * library holds no state.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_NULL = 1,
+    QG_ERR_SHAPE = 2,
+    QG_ERR_ALIGN = 3,
+    QG_ERR_WORKSPACE = 4,
+    QG_ERR_HIP = 5
+} qg_status;
+
+/* Opaque stream handle: a hipStream_t. */
+typedef void *qg_stream;
+
+/* Static, human-readable text for a status code (host only). */
+const char *qg_status_string(int status);
+
+/* Library version string (host only). */
+const char *qg_version(void);
+
+/*
+ * Size queries (host only, no device access).
+ * INT4 g128 storage is K*N/2 bytes of codes plus 2 bytes per group and column:
+ * 4.125 bits per weight [P1, opening and "The three regimes"; P2 3.4,
+ * "W4A16-INT", group-wise granularity].  Returns 0 for an invalid shape.
+ */
+size_t qg_int4_g128_packed_bytes(int64_t K, int64_t N);
+size_t qg_int4_g128_scale_bytes(int64_t K, int64_t N);
+
+/* Workspace bytes qgemm_w4a16 / qgemm_w8a8_fp8 need for this shape (may be 0). */
+size_t qg_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t qg_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * pack_int4_g128 -- offline RTN abs-max INT4 quantization in groups of 128
+ * rows, written in the native (MFMA fragment) order.
+ * [P2 3.4 "W4A16-INT": s = max|x| / 7 per group of 128 consecutive input-dim
+ *  weights, range [-7, 7]; P1 "Counting c": stored code = signed code + 8.]
+ *
+ *   w_bf16  in   [K, N] bf16 weights.
+ *   packed  out  K*N/8 uint32 words (qg_int4_g128_packed_bytes).
+ *   scales  out  (K/128)*N bf16 scales (qg_int4_g128_scale_bytes).
+ *
+ * Per group g and column n: s = bf16_rne(float(amax) / 7.0f); code =
+ * clamp(rne(w / s), -8, 7) + 8 with an IEEE fp32 quotient; s == 0 gives
+ * code 8 for the whole group.
+ *
+ * Native order.  G = K/128, NT = N/16.  The words form NT*G tiles of 256
+ * words; tile (nt, g) starts at word (nt*G + g)*256.  Word lane*4 + t of a tile
+ * (lane < 64, t < 4) holds column n = 16*nt + lane%16 at rows
+ * k = 128*g + 32*(lane/16) + 8*t + i, i < 8; nibble slot p (bits 4p..4p+3)
+ * holds i = 2p for p < 4 and i = 2(p-4)+1 for p >= 4, so that
+ * ((word >> 4j) & 0x000F000F) | 0x43004300 is the bf16 pair
+ * (128 + code[2j], 128 + code[2j+1]).  Scale (nt, g, c) sits at
+ * (nt*G + g)*16 + c.
+ */
+qg_status pack_int4_g128(const uint16_t *w_bf16, int K, int N,
+                         uint32_t *packed, uint16_t *scales, qg_stream stream);
+
+/*
+ * dequant_int4_g128 -- reconstruct the bf16 weights from the native buffers
+ * with the same device unpack code the GEMM uses (test / debug export).
+ * [P2 3.4 "Inference with W4A16": w_hat = s_g * w_int4; P1 "Counting c": the
+ *  offset is removed and the scale applied to the unpacked bf16 pair.]
+ *
+ *   w_bf16_out  out  [K, N]: bf16_rne((code - 8) * s), the exact fp32 product
+ *                    rounded once.
+ *   codes_out   out  [K, N] uint8 stored codes (0..15), or NULL to skip.
+ */
+qg_status dequant_int4_g128(const uint32_t *packed, const uint16_t *scales,
+                            int K, int N, uint16_t *w_bf16_out,
+                            uint8_t *codes_out, qg_stream stream);
+
+/*
+ * qgemm_w4a16 -- y[M, N] = a[M, K] . w_hat[K, N], bf16 in and out, fp32
+ * accumulation.
+ * [P2 3.4 "Inference with W4A16"; P1 "Counting c" and "The three regimes".]
+ *
+ *   a_bf16     in   [M, K] activations.
+ *   packed     in   native INT4 words from pack_int4_g128.
+ *   scales     in   native bf16 scales from pack_int4_g128.
+ *   y_bf16     out  [M, N].
+ *   workspace  scratch of qg_w4a16_workspace_bytes(M, N, K) bytes (may be
+ *              NULL when that is 0); its contents are overwritten.
+ *
+ * Numerics (folded offset): the MFMA multiplies the bf16 activations with the
+ * exact bf16 values 128 + code; per group and row the kernel adds
+ * -136 * sum(a) and multiplies the fp32 group sum by the group scale, i.e. it
+ * computes sum_g s_g * sum_{k in g} a_k (code_k - 8) in fp32 -- the product
+ * with the exact fp32 dequantized weight -- and rounds the result to bf16.
+ */
+qg_status qgemm_w4a16(const uint16_t *a_bf16, const uint32_t *packed,
+                      const uint16_t *scales, uint16_t *y_bf16,
+                      int M, int N, int K,
+                      void *workspace, size_t workspace_bytes,
+                      qg_stream stream);
+
+/*
+ * quant_act_per_token -- dynamic per-token e4m3 quantization.
+ * [P2 3.4 "W8A8-FP", activation quantization: Q(a_i) = s_i * rnd(a_i / s_i),
+ *  s_i = max|a_i| / q_max, computed on the fly per row.]
+ *
+ *   a_bf16   in   [M, K] activations (K % 128 == 0 is not required here,
+ *                 K % 8 == 0 is).
+ *   a_e4m3   out  [M, K] OCP e4m3fn codes.
+ *   a_scale  out  [M] fp32 scales s = float(amax) / 448.0f (IEEE division).
+ * Codes are e4m3(rne(a / s)) of the IEEE fp32 quotient, saturated at +-448;
+ * an all-zero row gives s = 0 and codes 0.
+ */
+qg_status quant_act_per_token(const uint16_t *a_bf16, int M, int K,
+                              uint8_t *a_e4m3, float *a_scale, qg_stream stream);
+
+/*
+ * quant_weight_fp8_per_channel -- offline per-output-channel e4m3 weight
+ * quantization into the native fp8 order.
+ * [P2 3.4 "W8A8-FP", weight quantization: per-output-channel symmetric RTN,
+ *  s = max|x| / q_max, Q(x) = s * rnd(x / s).]
+ *
+ *   w_bf16   in   [K, N]; output channel n is column n.
+ *   w_e4m3   out  N*K bytes, native order: KT = K/128, NT = N/16 tiles of
+ *                 2048 bytes, tile (nt, kt) at byte (nt*KT + kt)*2048; byte
+ *                 lane*32 + i (lane < 64, i < 32) is column 16*nt + lane%16 at
+ *                 row 128*kt + 32*(lane/16) + i.
+ *   w_scale  out  [N] fp32, s = float(amax) / 448.0f; zero column -> 0.
+ */
+qg_status quant_weight_fp8_per_channel(const uint16_t *w_bf16, int K, int N,
+                                       uint8_t *w_e4m3, float *w_scale,
+                                       qg_stream stream);
+
+/*
+ * qgemm_w8a8_fp8 -- y[m, n] = bf16(s_a[m] * s_w[n] * sum_k qa[m,k] qw[k,n])
+ * with e4m3 operands on the fp8 MFMA and fp32 accumulation.
+ * [P2 3.4 "W8A8-FP"; P1 deployment B: a native fp8 GEMM.]
+ *
+ *   a_e4m3, a_scale   in  from quant_act_per_token ([M, K], [M]).
+ *   w_e4m3, w_scale   in  from quant_weight_fp8_per_channel.
+ *   y_bf16            out [M, N].
+ *   workspace         scratch of qg_w8a8_workspace_bytes(M, N, K) bytes.
+ */
+qg_status qgemm_w8a8_fp8(const uint8_t *a_e4m3, const float *a_scale,
+                         const uint8_t *w_e4m3, const float *w_scale,
+                         uint16_t *y_bf16, int M, int N, int K,
+                         void *workspace, size_t workspace_bytes,
+                         qg_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,140 @@
+"""GPU parity of the W8A8-FP8 path against the CPU oracle.
+
+Activation codes and scales, weight codes (native order) and scales:
+bit-exact.  GEMM: max |err| <= 2e-2 x RMS of the fp64 oracle output.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import announce, assert_close_rms, dev_bf16, host_bits16, host_u8
+from oracle import fp8_e4m3 as f8
+from oracle.bf16 import f32_to_bf16_bits
+from weight_only_quantized_w4a16_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from weight_only_quantized_w4a16_amd import ops as _ops
+    return _ops
+
+
+def _act_quant(ops, a_bits):
+    qa, sa = ops.quantize_activations(dev_bf16(a_bits))
+    torch.cuda.synchronize()
+    return host_u8(qa), sa.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (4, 4096), (16, 14336), (37, 1000), (256, 4096)])
+def test_act_quant_bit_exact(ops, M, K):
+    announce(f"quant_act_per_token M={M} K={K}")
+    a = synth.activations(M, K, seed=M + K)
+    q, s = _act_quant(ops, a)
+    q_ref, s_ref = f8.quant_act_per_token(a)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q, q_ref)
+
+
+def test_act_quant_ties_subnormals_and_zero_rows(ops):
+    """Rows with amax 448 (scale exactly 1): every e4m3 value, every midpoint
+    between neighbours (ties to even), the subnormal range, signs, and zero rows."""
+    announce("quant_act_per_token ties / subnormals / zero rows")
+    pos = f8.e4m3_decode_table()[:127]
+    mids = (pos[1:] + pos[:-1]) / 2
+    vals = np.concatenate([pos, mids, -pos, -mids, [0.0, -0.0, 1e-6, -1e-6, 2.0 ** -11, 3 * 2.0 ** -11]])
+    K = 512
+    rows = []
+    for start in range(0, vals.size, K - 1):
+        r = np.zeros(K)
+        chunk = vals[start:start + K - 1]
+        r[:chunk.size] = chunk
+        r[-1] = 448.0
+        rows.append(r)
+    rows.append(np.zeros(K))                       # an all-zero row
+    small = np.zeros(K)
+    small[:5] = [3e-3, -7e-4, 1e-5, 2.5e-3, -1e-6]  # a row of tiny values (scale ~ 7e-6)
+    rows.append(small)
+    a = f32_to_bf16_bits(np.array(rows, dtype=np.float32))
+    q, s = _act_quant(ops, a)
+    q_ref, s_ref = f8.quant_act_per_token(a)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q, q_ref)
+
+
+@pytest.mark.parametrize("K,N", [(128, 16), (384, 48), (4096, 4096), (14336, 4096)])
+def test_weight_quant_bit_exact(ops, K, N):
+    announce(f"quant_weight_fp8_per_channel K={K} N={N}")
+    w = synth.weights(K, N, seed=K * 3 + N)
+    fw = ops.Fp8Weight.from_bf16(dev_bf16(w))
+    torch.cuda.synchronize()
+    qw_ref, sw_ref = f8.quant_weight_per_channel(w)
+    assert np.array_equal(fw.scales.cpu().numpy().view(np.uint32), sw_ref.view(np.uint32))
+    got = host_u8(fw.codes)
+    if K * N <= 4096 * 4096:
+        assert np.array_equal(got, f8.pack_native(qw_ref))
+    else:
+        assert np.array_equal(f8.unpack_native(got, K, N)[:, :64], qw_ref[:, :64])
+        rng = np.random.default_rng(0)
+        k = rng.integers(0, K, 200000)
+        n = rng.integers(0, N, 200000)
+        idx = ((n // 16) * (K // 128) + k // 128) * 2048 + (16 * ((k % 128) // 32) + n % 16) * 32 + k % 32
+        assert np.array_equal(got[idx], qw_ref[k, n])
+
+
+def _fp8_gemm(ops, a_bits, w_bits):
+    fw = ops.Fp8Weight.from_bf16(dev_bf16(w_bits))
+    lin = ops.W8A8Fp8Linear(fw)
+    y = lin(dev_bf16(a_bits))
+    torch.cuda.synchronize()
+    return host_bits16(y)
+
+
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 64), (1280, 144), (1024, 272)])
+@pytest.mark.parametrize("M", [1, 3, 4, 16, 17, 33, 64, 65, 100, 256, 300])
+def test_fp8_gemm_parity(ops, M, K, N):
+    announce(f"qgemm_w8a8_fp8 M={M} K={K} N={N}")
+    w = synth.weights(K, N, seed=5 + K + N)
+    a = synth.activations(M, K, seed=7 + M)
+    qa, sa = f8.quant_act_per_token(a)
+    qw, sw = f8.quant_weight_per_channel(w)
+    y = _fp8_gemm(ops, a, w)
+    assert_close_rms(y, f8.gemm_ref(qa, sa, qw, sw), what=f"fp8 M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("B", [1, 16, 128, 512, 1024])
+@pytest.mark.parametrize("j,name,K,N", [(1, "o", 4096, 4096), (3, "down", 14336, 4096)])
+def test_fp8_gemm_llama3_8b_shapes(ops, B, j, name, K, N):
+    announce(f"qgemm_w8a8_fp8 8B {name} B={B}")
+    w = synth.weights(K, N, seed=synth.weight_seed(0, j))
+    a = synth.activations(1024, K, seed=synth.activation_seed(0, j))[:B]
+    y = _fp8_gemm(ops, a, w)
+    rows = np.unique(np.random.default_rng(B).integers(0, B, 32))
+    qa, sa = f8.quant_act_per_token(a[rows])
+    qw, sw = f8.quant_weight_per_channel(w)
+    assert_close_rms(y[rows], f8.gemm_ref(qa, sa, qw, sw), what=f"fp8 {name} B={B}")
+
+
+def test_fp8_all_ones_exact(ops):
+    announce("qgemm_w8a8_fp8 all-ones")
+    K, N = 4096, 32
+    ones_w = f32_to_bf16_bits(np.ones((K, N), dtype=np.float32))
+    for M in (2, 100):
+        a = f32_to_bf16_bits(np.ones((M, K), dtype=np.float32))
+        y = _fp8_gemm(ops, a, ones_w)
+        yf = (y.astype(np.uint32) << 16).view(np.float32)
+        assert np.all(yf == 4096.0)
+
+
+@pytest.mark.parametrize("M", [4, 300])
+def test_fp8_deterministic(ops, M):
+    announce(f"qgemm_w8a8_fp8 determinism M={M}")
+    K, N = 4096, 1024
+    fw = ops.Fp8Weight.from_bf16(dev_bf16(synth.weights(K, N, seed=8)))
+    lin = ops.W8A8Fp8Linear(fw)
+    a = dev_bf16(synth.activations(M, K, seed=9))
+    y1 = host_bits16(lin(a))
+    y2 = host_bits16(lin(a))
+    assert np.array_equal(y1, y2)

@@ -1,0 +1,149 @@
+// C ABI of libqgemm (declared in include/qgemm.h): argument validation on the
+// host, before anything is launched, then dispatch to the gfx950 launchers.
+#include <hip/hip_runtime.h>
+
+#include "../../include/qgemm.h"
+#include "launch.h"
+
+namespace {
+
+// Limits that keep every index the kernels form inside its integer type.
+constexpr int64_t kMaxDim = int64_t(1) << 24;        // M, N
+constexpr int64_t kMaxK = int64_t(1) << 20;          // K
+constexpr int64_t kMaxElems = int64_t(1) << 38;      // elements of one matrix
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// K % 128, N % 16, bounds.  M may be 0.
+bool shape_ok(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N <= 0 || K <= 0) return false;
+    if (K % 128 != 0 || N % 16 != 0) return false;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxK) return false;
+    if (N * K > kMaxElems || M * K > kMaxElems || M * N > kMaxElems) return false;
+    return true;
+}
+
+qg_status launched() {
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_HIP;
+}
+
+hipStream_t as_stream(qg_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_string(int status) {
+    switch (status) {
+        case QG_OK: return "ok";
+        case QG_ERR_NULL: return "a required pointer is NULL";
+        case QG_ERR_SHAPE:
+            return "invalid shape (need M >= 0, N > 0, K > 0, K % 128 == 0, N % 16 == 0, within "
+                   "size limits)";
+        case QG_ERR_ALIGN: return "a pointer is not aligned (matrices 16 bytes, vectors 4 bytes)";
+        case QG_ERR_WORKSPACE: return "workspace smaller than the size query requires";
+        case QG_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* qg_version(void) { return "qgemm-gfx950 0.1.0"; }
+
+size_t qg_int4_g128_packed_bytes(int64_t K, int64_t N) {
+    if (!shape_ok(0, N, K)) return 0;
+    return (size_t)(K * N / 2);
+}
+
+size_t qg_int4_g128_scale_bytes(int64_t K, int64_t N) {
+    if (!shape_ok(0, N, K)) return 0;
+    return (size_t)(K / 128 * N * 2);
+}
+
+size_t qg_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!shape_ok(M, N, K)) return 0;
+    return qg::w4a16_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+size_t qg_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!shape_ok(M, N, K)) return 0;
+    return qg::w8a8_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+qg_status pack_int4_g128(const uint16_t* w_bf16, int K, int N, uint32_t* packed,
+                         uint16_t* scales, qg_stream stream) {
+    if (!w_bf16 || !packed || !scales) return QG_ERR_NULL;
+    if (!shape_ok(0, N, K)) return QG_ERR_SHAPE;
+    if (!aligned(w_bf16, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return QG_ERR_ALIGN;
+    qg::launch_pack_int4_g128(w_bf16, K, N, packed, scales, as_stream(stream));
+    return launched();
+}
+
+qg_status dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, int K, int N,
+                            uint16_t* w_bf16_out, uint8_t* codes_out, qg_stream stream) {
+    if (!packed || !scales || !w_bf16_out) return QG_ERR_NULL;
+    if (!shape_ok(0, N, K)) return QG_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(w_bf16_out, 16) ||
+        (codes_out && !aligned(codes_out, 16)))
+        return QG_ERR_ALIGN;
+    qg::launch_dequant_int4_g128(packed, scales, K, N, w_bf16_out, codes_out, as_stream(stream));
+    return launched();
+}
+
+qg_status qgemm_w4a16(const uint16_t* a_bf16, const uint32_t* packed, const uint16_t* scales,
+                      uint16_t* y_bf16, int M, int N, int K, void* workspace,
+                      size_t workspace_bytes, qg_stream stream) {
+    if (!shape_ok(M, N, K)) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    if (!a_bf16 || !packed || !scales || !y_bf16) return QG_ERR_NULL;
+    if (!aligned(a_bf16, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y_bf16, 16))
+        return QG_ERR_ALIGN;
+    const size_t need = qg::w4a16_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace) return QG_ERR_NULL;
+        if (workspace_bytes < need) return QG_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QG_ERR_ALIGN;
+    }
+    qg::launch_qgemm_w4a16(a_bf16, packed, scales, y_bf16, M, N, K, workspace, as_stream(stream));
+    return launched();
+}
+
+qg_status quant_act_per_token(const uint16_t* a_bf16, int M, int K, uint8_t* a_e4m3,
+                              float* a_scale, qg_stream stream) {
+    if (M < 0 || K <= 0 || K % 8 != 0 || M > kMaxDim || K > kMaxK) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    if (!a_bf16 || !a_e4m3 || !a_scale) return QG_ERR_NULL;
+    if (!aligned(a_bf16, 16) || !aligned(a_e4m3, 16) || !aligned(a_scale, 4)) return QG_ERR_ALIGN;
+    qg::launch_quant_act_per_token(a_bf16, M, K, a_e4m3, a_scale, as_stream(stream));
+    return launched();
+}
+
+qg_status quant_weight_fp8_per_channel(const uint16_t* w_bf16, int K, int N, uint8_t* w_e4m3,
+                                       float* w_scale, qg_stream stream) {
+    if (!w_bf16 || !w_e4m3 || !w_scale) return QG_ERR_NULL;
+    if (!shape_ok(0, N, K)) return QG_ERR_SHAPE;
+    if (!aligned(w_bf16, 16) || !aligned(w_e4m3, 16) || !aligned(w_scale, 4)) return QG_ERR_ALIGN;
+    qg::launch_quant_weight_fp8(w_bf16, K, N, w_e4m3, w_scale, as_stream(stream));
+    return launched();
+}
+
+qg_status qgemm_w8a8_fp8(const uint8_t* a_e4m3, const float* a_scale, const uint8_t* w_e4m3,
+                         const float* w_scale, uint16_t* y_bf16, int M, int N, int K,
+                         void* workspace, size_t workspace_bytes, qg_stream stream) {
+    if (!shape_ok(M, N, K)) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    if (!a_e4m3 || !a_scale || !w_e4m3 || !w_scale || !y_bf16) return QG_ERR_NULL;
+    if (!aligned(a_e4m3, 16) || !aligned(a_scale, 4) || !aligned(w_e4m3, 16) ||
+        !aligned(w_scale, 4) || !aligned(y_bf16, 16))
+        return QG_ERR_ALIGN;
+    const size_t need = qg::w8a8_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace) return QG_ERR_NULL;
+        if (workspace_bytes < need) return QG_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QG_ERR_ALIGN;
+    }
+    qg::launch_qgemm_w8a8_fp8(a_e4m3, a_scale, w_e4m3, w_scale, y_bf16, M, N, K, workspace,
+                              as_stream(stream));
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels of libqgemm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- bf16 <-> fp32 --------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+    return __uint_as_float(bits << 16);
+}
+
+// IEEE round-to-nearest-even fp32 -> bf16 bit pattern; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---- INT4 unpack ------------------------------------------------------------
+// A native word holds eight 4-bit codes; nibble slots j and j+4 hold the rows
+// 2j and 2j+1 of the word's 8-row slice.  Masking both nibbles into the low
+// mantissa bits of the bf16 pattern 0x4300 (= 128.0) makes the exact bf16 pair
+// (128 + code[2j], 128 + code[2j+1]): one shift and one AND-OR per two weights
+// ("When quantization pays", section "Counting c": the same masks).
+__device__ __forceinline__ uint32_t int4_pair_biased_bf16x2(uint32_t word, int j) {
+    return ((word >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Eight weights of one word -> MFMA operand (rows 0..7 in order), values 128 + code.
+__device__ __forceinline__ bf16x8 int4_word_biased_bf16x8(uint32_t word) {
+    u32x4 v;
+    v.x = int4_pair_biased_bf16x2(word, 0);
+    v.y = int4_pair_biased_bf16x2(word, 1);
+    v.z = int4_pair_biased_bf16x2(word, 2);
+    v.w = int4_pair_biased_bf16x2(word, 3);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- MFMA wrappers ------------------------------------------------------------
+// 16x16x32 bf16, fp32 accumulate.  A: lane l holds row l%16, 8 consecutive k of
+// the 32-wide step; B: lane l holds column l%16, the same 8 k.  D: lane l holds
+// column l%16, rows 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 OCP e4m3 x e4m3, fp32 accumulate (block scales fixed at 2^0).
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {
+    i32x8 r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace qg

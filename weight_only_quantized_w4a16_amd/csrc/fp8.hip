@@ -1,0 +1,378 @@
+// W8A8-FP8 on gfx950: per-token activation quantization, per-channel weight
+// quantization and the e4m3 x e4m3 GEMM on the fp8 MFMA.
+//
+// Formulas from "Give Me BF16 or Give Me Death", section 3.4 "W8A8-FP":
+// symmetric, no zero point, Q(x) = s * rnd(x / s) with s = max|x| / q_max, one
+// scale per output channel for weights and one per token (row) for
+// activations, computed on the fly.  q_max = 448 (OCP e4m3fn, the fp8 format
+// gfx950 converts to and multiplies natively).  Quotients are IEEE fp32
+// divisions; the hardware conversion rounds to nearest-even and the value is
+// clamped to +-448 first, so the code saturates instead of becoming NaN.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace qg {
+
+// Two fp32 values -> two e4m3 bytes (low byte = first value).
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// ---------------------------------------------------------------------------
+// quant_act_per_token: one workgroup per row; pass 1 finds the row's amax,
+// pass 2 re-reads the row (L2 resident) and writes codes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_act_per_token_kernel(const uint16_t* __restrict__ a,
+                                                                  int K, uint8_t* __restrict__ q,
+                                                                  float* __restrict__ sa) {
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const u32x4* row = reinterpret_cast<const u32x4*>(a + (size_t)m * K);
+    const int chunks = K >> 3;   // 8 bf16 per 16-byte chunk
+
+    float amax = 0.0f;
+    for (int c = tid; c < chunks; c += 256) {
+        const u32x4 v = row[c];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32(w4[j] & 0xffffu)));
+            amax = fmaxf(amax, fabsf(bf16_to_f32(w4[j] >> 16)));
+        }
+    }
+    __shared__ float red[4];
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 448.0f;                           // IEEE fp32 quotient
+    if (tid == 0) sa[m] = s;
+
+    uint2* out = reinterpret_cast<uint2*>(q + (size_t)m * K);
+    for (int c = tid; c < chunks; c += 256) {
+        uint2 o = make_uint2(0u, 0u);
+        if (s != 0.0f) {
+            const u32x4 v = row[c];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            uint32_t b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = e4m3x2(bf16_to_f32(w4[j] & 0xffffu) / s, bf16_to_f32(w4[j] >> 16) / s);
+            o.x = b[0] | (b[1] << 16);
+            o.y = b[2] | (b[3] << 16);
+        }
+        out[c] = o;
+    }
+}
+
+void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, float* s,
+                                hipStream_t st) {
+    hipLaunchKernelGGL(quant_act_per_token_kernel, dim3(M), dim3(256), 0, st, a, K, q, s);
+}
+
+// ---------------------------------------------------------------------------
+// quant_weight_fp8_per_channel: one workgroup per 16-column tile.  Pass 1:
+// column amax over K; pass 2: each lane writes its 32-byte slot of a native
+// 2 KiB tile (column 16*nt + l%16, rows 128*kt + 32*(l/16) .. +31).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* __restrict__ w,
+                                                               int K, int N,
+                                                               uint8_t* __restrict__ q,
+                                                               float* __restrict__ sw) {
+    const int nt = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int c = tid & 15;
+    const int r = tid >> 4;
+    const int n = nt * 16 + c;
+
+    float amax = 0.0f;
+    for (int k = r; k < K; k += 16) amax = fmaxf(amax, fabsf(bf16_to_f32(w[(size_t)k * N + n])));
+    __shared__ float red[16][16];
+    __shared__ float scol[16];
+    red[r][c] = amax;
+    __syncthreads();
+    if (r == 0) {
+        float m = 0.0f;
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, red[i][c]);
+        const float s = m / 448.0f;
+        scol[c] = s;
+        sw[n] = s;
+    }
+    __syncthreads();
+
+    const int KT = K >> 7;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ln = nt * 16 + (lane & 15);
+    const float s = scol[lane & 15];
+    for (int kt = wave; kt < KT; kt += 4) {
+        const int k0 = kt * 128 + (lane >> 4) * 32;
+        uint32_t b[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t v = 0u;
+            if (s != 0.0f)
+                v = e4m3x2(bf16_to_f32(w[(size_t)(k0 + 2 * i) * N + ln]) / s,
+                           bf16_to_f32(w[(size_t)(k0 + 2 * i + 1) * N + ln]) / s);
+            b[i] = v;
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(q + ((size_t)nt * KT + kt) * 2048 + lane * 32);
+        u32x4 lo, hi;
+        lo.x = b[0] | (b[1] << 16);   lo.y = b[2] | (b[3] << 16);
+        lo.z = b[4] | (b[5] << 16);   lo.w = b[6] | (b[7] << 16);
+        hi.x = b[8] | (b[9] << 16);   hi.y = b[10] | (b[11] << 16);
+        hi.z = b[12] | (b[13] << 16); hi.w = b[14] | (b[15] << 16);
+        dst[0] = lo;
+        dst[1] = hi;
+    }
+}
+
+void launch_quant_weight_fp8(const uint16_t* w, int K, int N, uint8_t* q, float* s,
+                             hipStream_t st) {
+    hipLaunchKernelGGL(quant_weight_fp8_kernel, dim3(N / 16), dim3(256), 0, st, w, K, N, q, s);
+}
+
+// ---------------------------------------------------------------------------
+// Small M (M <= 64): split-K inside the workgroup, as in the W4A16 kernel.
+// One 16x16x128 fp8 MFMA per (column tile, m-tile, 128-row k-tile); each lane
+// loads 32 contiguous bytes of A and of the weight tile.
+// ---------------------------------------------------------------------------
+template <int MT, int CT, int NWAVE, int U>
+__global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
+    const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
+    const int KT = K >> 7;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int nt0 = blockIdx.x * CT;
+    const int k_begin = (KT * wave) / NWAVE;
+    const int k_end = (KT * (wave + 1)) / NWAVE;
+
+    f32x4 total[CT][MT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) total[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const u32x4* arow[MT];
+    bool rowok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + col;
+        rowok[mt] = m < M;
+        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)(rowok[mt] ? m : 0) * K + kq * 32);
+    }
+    const u32x4* wtile = reinterpret_cast<const u32x4*>(wq);
+
+    for (int k0 = k_begin; k0 < k_end; k0 += U) {
+        u32x4 wv[U][CT][2];
+        u32x4 av[U][MT][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kt = k0 + u;
+            if (kt < k_end) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const size_t tile = (size_t)(nt0 + ct) * KT + kt;
+                    wv[u][ct][0] = wtile[tile * 128 + lane * 2];
+                    wv[u][ct][1] = wtile[tile * 128 + lane * 2 + 1];
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    av[u][mt][0] = rowok[mt] ? arow[mt][kt * 8] : u32x4{0u, 0u, 0u, 0u};
+                    av[u][mt][1] = rowok[mt] ? arow[mt][kt * 8 + 1] : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (k0 + u < k_end) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const i32x8 bfr = cat_i32x8(wv[u][ct][0], wv[u][ct][1]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        total[ct][mt] = mfma_fp8_16x16x128(cat_i32x8(av[u][mt][0], av[u][mt][1]), bfr,
+                                                           total[ct][mt]);
+                }
+            }
+        }
+    }
+
+    __shared__ f32x4 red[NWAVE][CT][MT][64];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[wave][ct][mt][lane] = total[ct][mt];
+    __syncthreads();
+
+    for (int e = threadIdx.x; e < CT * MT * 256; e += NWAVE * 64) {
+        const int i = e & 3;
+        const int l = (e >> 2) & 63;
+        const int cm = e >> 8;
+        const int mt = cm % MT;
+        const int ct = cm / MT;
+        const int m = mt * 16 + 4 * (l >> 4) + i;
+        if (m >= M) continue;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) sum += red[w][ct][mt][l][i];
+        const int n = (nt0 + ct) * 16 + (l & 15);
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum * sa[m] * sw[n]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large M (M > 64): 256 x 128 output tile per workgroup, 4 waves in a 2 x 2
+// grid of 128 x 64.  The fp8 activation tile of one 128-row k-tile (256 rows
+// x 128 bytes) is staged in LDS, double buffered, with the 16-byte chunk
+// swizzle c ^ ((r / 2) % 8) (two 128-byte rows share one pass over the 64
+// banks); weight tiles go straight to registers.
+// ---------------------------------------------------------------------------
+constexpr int F8_BM = 256;
+constexpr int F8_BN = 128;
+
+__global__ __launch_bounds__(256) void w8a8_large_m_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
+    const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
+    __shared__ u32x4 As[2][F8_BM][8];   // 2 x 32 KiB
+
+    const int KT = K >> 7;
+    const int NT = N >> 4;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int m0 = blockIdx.y * F8_BM;
+    const int n0 = blockIdx.x * F8_BN;
+
+    // loader: thread -> row tid (256 rows), 8 chunks of 16 bytes
+    const bool lrow_ok = (m0 + tid) < M;
+    const u32x4* asrc = reinterpret_cast<const u32x4*>(a + (size_t)(lrow_ok ? m0 + tid : 0) * K);
+
+    const u32x4* wsrc[4];
+    bool tok[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int nt = (n0 >> 4) + wn * 4 + ni;
+        tok[ni] = nt < NT;
+        wsrc[ni] = reinterpret_cast<const u32x4*>(wq) + (size_t)(tok[ni] ? nt : 0) * KT * 128 +
+                   lane * 2;
+    }
+
+    f32x4 total[8][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 areg[8];
+    u32x4 wreg[4][2];
+    auto load_a = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            areg[i] = lrow_ok ? asrc[(size_t)kt * 8 + i] : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) As[buf][tid][i ^ ((tid >> 1) & 7)] = areg[i];
+    };
+    auto load_w = [&](int kt) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            wreg[ni][0] = tok[ni] ? wsrc[ni][(size_t)kt * 128] : u32x4{0u, 0u, 0u, 0u};
+            wreg[ni][1] = tok[ni] ? wsrc[ni][(size_t)kt * 128 + 1] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    load_a(0);
+    load_w(0);
+    store_a(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        i32x8 bfr[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) bfr[ni] = cat_i32x8(wreg[ni][0], wreg[ni][1]);
+        if (kt + 1 < KT) {
+            load_a(kt + 1);
+            load_w(kt + 1);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+            const int r = wm * 128 + mi * 16 + col;
+            const int sw8 = (r >> 1) & 7;
+            const i32x8 af = cat_i32x8(As[buf][r][(kq * 2) ^ sw8], As[buf][r][(kq * 2 + 1) ^ sw8]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) total[mi][ni] = mfma_fp8_16x16x128(af, bfr[ni], total[mi][ni]);
+        }
+        if (kt + 1 < KT) store_a(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        if (!tok[ni]) continue;
+        const int n = n0 + wn * 64 + ni * 16 + col;
+        const float swn = sw[n];
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + wm * 128 + mi * 16 + 4 * kq + i;
+                if (m < M)
+                    y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i] * sa[m] * swn);
+            }
+        }
+    }
+}
+
+size_t w8a8_workspace_bytes(int M, int N, int K) {
+    (void)M; (void)N; (void)K;
+    return 0;
+}
+
+template <int MT, int CT>
+static void launch_small(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                         uint16_t* y, int M, int N, int K, hipStream_t st) {
+    constexpr int NWAVE = 8;
+    constexpr int U = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
+    hipLaunchKernelGGL((w8a8_small_m_kernel<MT, CT, NWAVE, U>), dim3(N / 16 / CT), dim3(NWAVE * 64),
+                       0, st, a, sa, w, sw, y, M, N, K);
+}
+
+template <int MT>
+static void launch_small_ct(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                            uint16_t* y, int M, int N, int K, hipStream_t st) {
+    const int NT = N / 16;
+    if (NT % 2 == 0 && NT >= 1024)
+        launch_small<MT, 2>(a, sa, w, sw, y, M, N, K, st);
+    else
+        launch_small<MT, 1>(a, sa, w, sw, y, M, N, K, st);
+}
+
+void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                           uint16_t* y, int M, int N, int K, void* ws, hipStream_t st) {
+    (void)ws;
+    if (M <= 16) {
+        launch_small_ct<1>(a, sa, w, sw, y, M, N, K, st);
+    } else if (M <= 32) {
+        launch_small_ct<2>(a, sa, w, sw, y, M, N, K, st);
+    } else if (M <= 64) {
+        launch_small_ct<4>(a, sa, w, sw, y, M, N, K, st);
+    } else {
+        dim3 grid((N + F8_BN - 1) / F8_BN, (M + F8_BM - 1) / F8_BM);
+        hipLaunchKernelGGL(w8a8_large_m_kernel, grid, dim3(256), 0, st, a, sa, w, sw, y, M, N, K);
+    }
+}
+
+}  // namespace qg

@@ -1,0 +1,30 @@
+// Host-side launchers of the gfx950 kernels (private to libqgemm).  Shapes and
+// pointers are validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+// W4A16 path (w4a16.hip)
+void launch_pack_int4_g128(const uint16_t* w, int K, int N, uint32_t* packed,
+                           uint16_t* scales, hipStream_t s);
+void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, int K,
+                              int N, uint16_t* w_out, uint8_t* codes_out, hipStream_t s);
+size_t w4a16_workspace_bytes(int M, int N, int K);
+void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
+                        uint16_t* y, int M, int N, int K, void* ws, hipStream_t s);
+
+// W8A8-FP8 path (fp8.hip)
+void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, float* s,
+                                hipStream_t st);
+void launch_quant_weight_fp8(const uint16_t* w, int K, int N, uint8_t* q, float* s,
+                             hipStream_t st);
+size_t w8a8_workspace_bytes(int M, int N, int K);
+void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w,
+                           const float* sw, uint16_t* y, int M, int N, int K, void* ws,
+                           hipStream_t st);
+
+}  // namespace qg

@@ -1,0 +1,475 @@
+// W4A16 on gfx950: INT4 g128 packing, dequantization and the mixed-precision GEMM.
+//
+// Weight format (symmetric INT4, zero offset 8, one bf16 scale per 128 input
+// rows) from "Give Me BF16 or Give Me Death", section 3.4 "W4A16-INT", and the
+// bf16 / uint4-bias-8 unpack of "When quantization pays", section "Counting c".
+// The native order puts the 16 columns x 128 rows of one group into one 1 KiB
+// tile laid out as the B operand of v_mfma_f32_16x16x32_bf16 over four k-steps,
+// so one 128-bit load per lane fetches a lane's whole share of a group.
+//
+// Numerics of the GEMM (the "folded offset"): the MFMA consumes the exact bf16
+// values 128 + code straight out of the AND-OR unpack; per group and row the
+// accumulator starts at -136 * sum_k a[m, k], and the group's fp32 sum is
+// multiplied by the group scale on the accumulators.  This is
+// sum_g s_g * sum_k a (code - 8), the product with the exact fp32 dequantized
+// weight, at 7 VALU instructions per 8 weights for the unpack plus one FMA per
+// accumulator per group for the scale.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace qg {
+
+// ---------------------------------------------------------------------------
+// pack_int4_g128: one 64-lane workgroup per (column tile, group) tile.  Lane l
+// owns column 16*nt + l%16 and the 32 rows 32*(l/16) .. +31 of the group, which
+// is exactly the lane's 16-byte slot of the native tile.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void pack_int4_g128_kernel(
+    const uint16_t* __restrict__ w, int K, int N, uint32_t* __restrict__ packed,
+    uint16_t* __restrict__ scales) {
+    const int G = K >> 7;
+    const int tile = blockIdx.x;
+    const int nt = tile / G;
+    const int g = tile - nt * G;
+    const int lane = threadIdx.x;
+    const int c = lane & 15;
+    const int q = lane >> 4;
+    const int n = nt * 16 + c;
+    const int k0 = g * 128 + q * 32;
+
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        v[i] = bf16_to_f32(w[(size_t)(k0 + i) * N + n]);
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    // the four lanes of one column hold its four 32-row quarters
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+
+    const uint32_t sbits = f32_to_bf16_rne(amax / 7.0f);   // IEEE fp32 quotient
+    const float s = bf16_to_f32(sbits);
+
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        int code = 8;
+        if (s != 0.0f) {
+            float r = rintf(v[i] / s);                       // half-even of the IEEE quotient
+            r = fminf(fmaxf(r, -8.0f), 7.0f);
+            code = (int)r + 8;
+        }
+        const int t = i >> 3;
+        const int ii = i & 7;
+        const int slot = (ii & 1) ? 4 + (ii >> 1) : (ii >> 1);
+        words[t] |= (uint32_t)code << (4 * slot);
+    }
+    u32x4 out;
+    out.x = words[0]; out.y = words[1]; out.z = words[2]; out.w = words[3];
+    reinterpret_cast<u32x4*>(packed)[(size_t)tile * 64 + lane] = out;
+    if (q == 0) scales[(size_t)tile * 16 + c] = (uint16_t)sbits;
+}
+
+void launch_pack_int4_g128(const uint16_t* w, int K, int N, uint32_t* packed,
+                           uint16_t* scales, hipStream_t s) {
+    const int tiles = (N / 16) * (K / 128);
+    hipLaunchKernelGGL(pack_int4_g128_kernel, dim3(tiles), dim3(64), 0, s, w, K, N, packed,
+                       scales);
+}
+
+// ---------------------------------------------------------------------------
+// dequant_int4_g128: same tiling as the packer, same unpack as the GEMM.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void dequant_int4_g128_kernel(
+    const uint32_t* __restrict__ packed, const uint16_t* __restrict__ scales, int K, int N,
+    uint16_t* __restrict__ w_out, uint8_t* __restrict__ codes_out) {
+    const int G = K >> 7;
+    const int tile = blockIdx.x;
+    const int nt = tile / G;
+    const int g = tile - nt * G;
+    const int lane = threadIdx.x;
+    const int n = nt * 16 + (lane & 15);
+    const int kq = g * 128 + (lane >> 4) * 32;
+    const u32x4 wv = reinterpret_cast<const u32x4*>(packed)[(size_t)tile * 64 + lane];
+    const float s = bf16_to_f32(scales[(size_t)tile * 16 + (lane & 15)]);
+    const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t pair = int4_pair_biased_bf16x2(words[t], j);   // (128+c_lo, 128+c_hi)
+            const int k = kq + 8 * t + 2 * j;
+            const float lo = (bf16_to_f32(pair & 0xffffu) - 136.0f) * s;  // exact
+            const float hi = (bf16_to_f32(pair >> 16) - 136.0f) * s;
+            w_out[(size_t)k * N + n] = (uint16_t)f32_to_bf16_rne(lo);
+            w_out[(size_t)(k + 1) * N + n] = (uint16_t)f32_to_bf16_rne(hi);
+            if (codes_out) {
+                codes_out[(size_t)k * N + n] = (uint8_t)(pair & 0xfu);
+                codes_out[(size_t)(k + 1) * N + n] = (uint8_t)((pair >> 16) & 0xfu);
+            }
+        }
+    }
+}
+
+void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, int K, int N,
+                              uint16_t* w_out, uint8_t* codes_out, hipStream_t s) {
+    const int tiles = (N / 16) * (K / 128);
+    hipLaunchKernelGGL(dequant_int4_g128_kernel, dim3(tiles), dim3(64), 0, s, packed, scales,
+                       K, N, w_out, codes_out);
+}
+
+// ---------------------------------------------------------------------------
+// Small M (decode, M <= 64): split-K inside the workgroup.
+//
+// A workgroup owns CT column tiles (16 columns each) over the whole K; its
+// NWAVE waves split the groups into contiguous ranges, so each wave streams
+// contiguous 1 KiB tiles.  MT 16-row m-tiles cover M.  Per group a wave loads
+// its A fragments once (64 contiguous bytes per lane and m-tile), computes the
+// offset term -136 * sum(a) with four MFMAs against a constant B, then for each
+// column tile unpacks one 128-bit word load and runs four MFMAs starting from
+// that offset term; the group sum is scaled into the running total.  The
+// waves' totals are reduced in LDS in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+template <int MT, int CT, int NWAVE, int U>
+__global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
+    const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K) {
+    const int G = K >> 7;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int nt0 = blockIdx.x * CT;
+    const int g_begin = (G * wave) / NWAVE;
+    const int g_end = (G * (wave + 1)) / NWAVE;
+
+    f32x4 total[CT][MT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) total[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 negc_u;
+    negc_u.x = negc_u.y = negc_u.z = negc_u.w = 0xC308C308u;     // bf16 -136 everywhere
+    const bf16x8 negc = as_bf16x8(negc_u);
+
+    const u32x4* arow[MT];
+    bool rowok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + col;
+        rowok[mt] = m < M;
+        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)(rowok[mt] ? m : 0) * K + kq * 32);
+    }
+    const u32x4* wtile = reinterpret_cast<const u32x4*>(wq);
+
+    for (int g0 = g_begin; g0 < g_end; g0 += U) {
+        u32x4 wv[U][CT];
+        uint32_t sv[U][CT];
+        u32x4 av[U][MT][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + u;
+            if (g < g_end) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const size_t tile = (size_t)(nt0 + ct) * G + g;
+                    wv[u][ct] = wtile[tile * 64 + lane];
+                    sv[u][ct] = sc[tile * 16 + col];
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        av[u][mt][t] = rowok[mt] ? arow[mt][g * 16 + t] : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (g0 + u < g_end) {
+                f32x4 corr[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    corr[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        corr[mt] = mfma_bf16_16x16x32(as_bf16x8(av[u][mt][t]), negc, corr[mt]);
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const float s = bf16_to_f32(sv[u][ct]);
+                    bf16x8 bfr[4];
+                    bfr[0] = int4_word_biased_bf16x8(wv[u][ct].x);
+                    bfr[1] = int4_word_biased_bf16x8(wv[u][ct].y);
+                    bfr[2] = int4_word_biased_bf16x8(wv[u][ct].z);
+                    bfr[3] = int4_word_biased_bf16x8(wv[u][ct].w);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        f32x4 acc = corr[mt];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            acc = mfma_bf16_16x16x32(as_bf16x8(av[u][mt][t]), bfr[t], acc);
+                        total[ct][mt][0] = fmaf(s, acc[0], total[ct][mt][0]);
+                        total[ct][mt][1] = fmaf(s, acc[1], total[ct][mt][1]);
+                        total[ct][mt][2] = fmaf(s, acc[2], total[ct][mt][2]);
+                        total[ct][mt][3] = fmaf(s, acc[3], total[ct][mt][3]);
+                    }
+                }
+            }
+        }
+    }
+
+    __shared__ f32x4 red[NWAVE][CT][MT][64];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[wave][ct][mt][lane] = total[ct][mt];
+    __syncthreads();
+
+    for (int e = threadIdx.x; e < CT * MT * 256; e += NWAVE * 64) {
+        const int i = e & 3;
+        const int l = (e >> 2) & 63;
+        const int cm = e >> 8;
+        const int mt = cm % MT;
+        const int ct = cm / MT;
+        const int m = mt * 16 + 4 * (l >> 4) + i;
+        if (m >= M) continue;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) sum += red[w][ct][mt][l][i];
+        const int n = (nt0 + ct) * 16 + (l & 15);
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large M: -136 * (row sum over each group) for every row, once per call, into
+// the workspace as corr[g][m] (rows padded to a multiple of 128 with zeros).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t* __restrict__ a,
+                                                                 int M, int Mp, int K,
+                                                                 float* __restrict__ corr) {
+    const int G = K >> 7;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)G * Mp) return;
+    const int m = (int)(idx % Mp);
+    const int g = (int)(idx / Mp);
+    float s = 0.0f;
+    if (m < M) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(a + (size_t)m * K + (size_t)g * 128);
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const u32x4 v = p[i];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s += bf16_to_f32(w4[j] & 0xffffu);
+                s += bf16_to_f32(w4[j] >> 16);
+            }
+        }
+    }
+    corr[idx] = -136.0f * s;
+}
+
+// ---------------------------------------------------------------------------
+// Large M (M > 64): 128 x 128 output tile per workgroup, 4 waves in a 2 x 2
+// grid of 64 x 64.  The activation tile of one group (128 rows x 128 k) is
+// staged in LDS, double buffered, with a 16-byte XOR swizzle (chunk c of row r
+// stored at c ^ (r % 16)) so the fragment reads are conflict free.  Each wave
+// loads its four weight tiles straight into registers (they are already in
+// fragment order), unpacks them once per group and reuses them over its four
+// m-tiles.  Every (m-tile, n-tile) group sum starts at the precomputed offset
+// term and is scaled into the total.
+// ---------------------------------------------------------------------------
+constexpr int LM_BM = 128;
+constexpr int LM_BN = 128;
+
+__global__ __launch_bounds__(256) void w4a16_large_m_kernel(
+    const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
+    int M, int Mp, int N, int K) {
+    __shared__ u32x4 As[2][LM_BM][16];   // 2 x 32 KiB
+
+    const int G = K >> 7;
+    const int NT = N >> 4;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int m0 = blockIdx.y * LM_BM;
+    const int n0 = blockIdx.x * LM_BN;
+
+    // activation tile loader: thread -> row lr, chunks 8*lh .. 8*lh+7
+    const int lr = tid >> 1;
+    const int lh = tid & 1;
+    const bool lrow_ok = (m0 + lr) < M;
+    const u32x4* asrc =
+        reinterpret_cast<const u32x4*>(a + (size_t)(lrow_ok ? m0 + lr : 0) * K) + lh * 8;
+
+    // weight tiles of this wave
+    const u32x4* wsrc[4];
+    const uint16_t* ssrc[4];
+    bool tok[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int nt = (n0 >> 4) + wn * 4 + ni;
+        tok[ni] = nt < NT;
+        const size_t ntc = tok[ni] ? nt : 0;
+        wsrc[ni] = reinterpret_cast<const u32x4*>(wq) + ntc * G * 64 + lane;
+        ssrc[ni] = sc + ntc * G * 16 + col;
+    }
+    // offset-term rows of this wave: m0 + wm*64 + mi*16 + 4*kq + (0..3)
+    const float* csrc = corr + m0 + wm * 64 + 4 * kq;
+
+    f32x4 total[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 areg[8];
+    u32x4 wreg[4];
+    uint32_t sreg[4];
+
+    auto load_a = [&](int g) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            areg[i] = lrow_ok ? asrc[(size_t)g * 16 + i] : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) As[buf][lr][(lh * 8 + i) ^ (lr & 15)] = areg[i];
+    };
+    auto load_w = [&](int g) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            wreg[ni] = tok[ni] ? wsrc[ni][(size_t)g * 64] : u32x4{0u, 0u, 0u, 0u};
+            sreg[ni] = tok[ni] ? ssrc[ni][(size_t)g * 16] : 0u;
+        }
+    };
+
+    load_a(0);
+    load_w(0);
+    store_a(0);
+    __syncthreads();
+
+    for (int g = 0; g < G; ++g) {
+        const int buf = g & 1;
+        u32x4 wcur[4];
+        float scur[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            wcur[ni] = wreg[ni];
+            scur[ni] = bf16_to_f32(sreg[ni]);
+        }
+        f32x4 cr[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            cr[mi] = *reinterpret_cast<const f32x4*>(csrc + (size_t)g * Mp + mi * 16);
+        if (g + 1 < G) {
+            load_a(g + 1);
+            load_w(g + 1);
+        }
+        bf16x8 af[4][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int r = wm * 64 + mi * 16 + col;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) af[mi][t] = as_bf16x8(As[buf][r][(kq * 4 + t) ^ col]);
+        }
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            bf16x8 bfr[4];
+            bfr[0] = int4_word_biased_bf16x8(wcur[ni].x);
+            bfr[1] = int4_word_biased_bf16x8(wcur[ni].y);
+            bfr[2] = int4_word_biased_bf16x8(wcur[ni].z);
+            bfr[3] = int4_word_biased_bf16x8(wcur[ni].w);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                f32x4 acc = cr[mi];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc = mfma_bf16_16x16x32(af[mi][t], bfr[t], acc);
+                total[mi][ni][0] = fmaf(scur[ni], acc[0], total[mi][ni][0]);
+                total[mi][ni][1] = fmaf(scur[ni], acc[1], total[mi][ni][1]);
+                total[mi][ni][2] = fmaf(scur[ni], acc[2], total[mi][ni][2]);
+                total[mi][ni][3] = fmaf(scur[ni], acc[3], total[mi][ni][3]);
+            }
+        }
+        if (g + 1 < G) store_a(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            if (!tok[ni]) continue;
+            const int n = n0 + wn * 64 + ni * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + wm * 64 + mi * 16 + 4 * kq + i;
+                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+size_t w4a16_workspace_bytes(int M, int N, int K) {
+    (void)N;
+    if (M <= 64) return 0;
+    return (size_t)(K / 128) * (size_t)round_up(M, LM_BM) * sizeof(float);
+}
+
+template <int MT, int CT>
+static void launch_small(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
+                         int M, int N, int K, hipStream_t s) {
+    constexpr int NWAVE = 8;
+    constexpr int U = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
+    const int NT = N / 16;
+    hipLaunchKernelGGL((w4a16_small_m_kernel<MT, CT, NWAVE, U>), dim3(NT / CT), dim3(NWAVE * 64),
+                       0, s, a, wq, sc, y, M, N, K);
+}
+
+template <int MT>
+static void launch_small_ct(const uint16_t* a, const uint32_t* wq, const uint16_t* sc,
+                            uint16_t* y, int M, int N, int K, hipStream_t s) {
+    const int NT = N / 16;
+    if (NT % 2 == 0 && NT >= 1024)
+        launch_small<MT, 2>(a, wq, sc, y, M, N, K, s);
+    else
+        launch_small<MT, 1>(a, wq, sc, y, M, N, K, s);
+}
+
+void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
+                        uint16_t* y, int M, int N, int K, void* ws, hipStream_t s) {
+    if (M <= 16) {
+        launch_small_ct<1>(a, packed, scales, y, M, N, K, s);
+    } else if (M <= 32) {
+        launch_small_ct<2>(a, packed, scales, y, M, N, K, s);
+    } else if (M <= 64) {
+        launch_small_ct<4>(a, packed, scales, y, M, N, K, s);
+    } else {
+        const int Mp = round_up(M, LM_BM);
+        const int G = K / 128;
+        float* corr = static_cast<float*>(ws);
+        const size_t n = (size_t)G * Mp;
+        hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, s, a, M, Mp, K, corr);
+        dim3 grid((N + LM_BN - 1) / LM_BN, Mp / LM_BM);
+        hipLaunchKernelGGL(w4a16_large_m_kernel, grid, dim3(256), 0, s, a, packed, scales, corr, y,
+                           M, Mp, N, K);
+    }
+}
+
+}  // namespace qg

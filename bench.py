@@ -1,0 +1,502 @@
+"""Benchmark: Llama-3-8B W4A16 decode step (129 quantized linears) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
+                    [--workload decode|large-batch|fp8|70b]
+
+One step is one pass of the whole hot path over one batch: the 129 W4A16
+GEMMs of a Llama-3-8B decode step (32 layers of qkv 4096->6144, o 4096->4096,
+gate_up 4096->28672, down 14336->4096, plus the LM head 4096->128256), each with
+its own INT4 g128 weight (3.87 GB in total, far beyond every cache) and its own
+bf16 activations, all resident in HBM before timing starts.  The step is
+captured once in a HIP graph and replayed; HIP events on the launch stream
+bracket exactly `--steps` replays after `--warmup` untimed ones.
+
+Default workload "decode": B in {1, 2, 4, 8, 16}; the JSON line's value is
+the algorithmic HBM throughput at --batch (default 16), the other batches are
+listed under "by_batch".  Other workloads (one line each):
+  large-batch  the same stack at B in {32 .. 1024} against a dense bf16 stack
+               (hipBLASLt through torch.matmul), MFMA utilisation and crossover
+  fp8          the W8A8-FP8 stack (per-token activation quantization + fp8 GEMM)
+  70b          the Llama-3-70B W4A16 stack on one GPU
+
+Algorithmic bytes of one W4A16 GEMM: K*N/2 (codes) + 2*N*K/128 (scales) +
+2*M*K (activations) + 2*M*N (outputs); flops: 2*M*N*K.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+DOMINANT_SRC = os.path.join(ROOT, "weight_only_quantized_w4a16_amd", "csrc", "w4a16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_stream_kernel_llama3_8b_decode_B16_traffic.txt")
+
+
+def w4a16_bytes(M, K, N):
+    return K * N // 2 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
+
+
+def fp8_bytes(M, K, N):
+    # weights + channel scales + fp8 activations + row scales + bf16 outputs
+    return K * N + 4 * N + M * K + 4 * M + 2 * M * N
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--batch", type=int, default=16)
+    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "70b"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only-batch", action="store_true",
+                   help="decode workload: time only --batch (short profiled runs)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    p.add_argument("--summarize-stats", metavar="CSV",
+                   help="print a text summary of a rocprofv3 *_kernel_stats.csv and exit")
+    p.add_argument("--summarize-traffic", nargs=4,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="derive HBM bytes per dominant-kernel launch from four rocprofv3 --pmc "
+                        "runs and write the traffic summary under profiles/, then exit")
+    p.add_argument("--command", default="", help="command line recorded in summaries")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- GPU side
+
+class Stack:
+    """The packed weights, activations and outputs of one decode step."""
+
+    def __init__(self, ops, synth, torch, model, batches, fp8=False):
+        self.torch = torch
+        self.ops = ops
+        self.shapes = synth.stack_shapes(model)
+        self.batches = batches
+        self.fp8 = fp8
+        dev = torch.device("cuda:0")
+        self.layers = []
+        maxb = max(batches)
+        for idx, (name, K, N) in enumerate(self.shapes):
+            layer, j = divmod(idx, 4)
+            seed = synth.weight_seed(layer, j)
+            w = synth.normal_bf16_device((K, N), seed, synth.WEIGHT_STD, dev)
+            wt = ops.Fp8Weight.from_bf16(w) if fp8 else ops.Int4G128Weight.from_bf16(w)
+            del w
+            a = synth.normal_bf16_device((maxb, K), synth.activation_seed(layer, j), 1.0, dev)
+            y = torch.empty((maxb, N), dtype=torch.bfloat16, device=dev)
+            lin = ops.W8A8Fp8Linear(wt) if fp8 else ops.W4A16Linear(wt)
+            rec = {"name": name, "K": K, "N": N, "w": wt, "a": a, "y": y, "lin": lin}
+            if fp8:
+                rec["qa"] = torch.empty((maxb, K), dtype=torch.uint8, device=dev)
+                rec["sa"] = torch.empty(maxb, dtype=torch.float32, device=dev)
+            else:
+                ws, _ = lin.workspace(maxb)      # allocate the largest workspace up front
+            self.layers.append(rec)
+        torch.cuda.synchronize()
+
+    def step(self, B, only=None):
+        ops = self.ops
+        for r in self.layers:
+            if only is not None and not only(r):
+                continue
+            a = r["a"][:B]
+            y = r["y"][:B]
+            if self.fp8:
+                ops.quant_act_per_token(a, B, r["K"], r["qa"][:B], r["sa"][:B])
+                ops.qgemm_w8a8_fp8(r["qa"][:B], r["sa"][:B], r["w"].codes, r["w"].scales, y,
+                                   B, r["N"], r["K"])
+            else:
+                ws, nb = r["lin"].workspace(B)
+                ops.qgemm_w4a16(a, r["w"].packed, r["w"].scales, y, B, r["N"], r["K"], ws, nb)
+
+    def bytes(self, B, only=None):
+        f = fp8_bytes if self.fp8 else w4a16_bytes
+        return sum(f(B, r["K"], r["N"]) for r in self.layers if only is None or only(r))
+
+    def flops(self, B):
+        return sum(2 * B * r["K"] * r["N"] for r in self.layers)
+
+
+def graph_of(torch, fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                   # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, steps, warmup):
+    """Replay `warmup` times untimed, then time exactly `steps` replays with HIP
+    events on the replay stream; returns ms per replay."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+DOMINANT_KERNEL = "w4a16_stream_kernel"
+
+
+def dominant_rule(ops, M, K, N):
+    """Launches that run the dominant kernel: the kernel the library selects for
+    the wide GEMMs (gate_up and the LM head), which carry the largest share of
+    the step's bytes at B <= 16."""
+    return ops.w4a16_kernel_for(M, N, K) == DOMINANT_KERNEL
+
+
+def read_traffic(kernel_sha):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(B):
+    """The oracle (numpy fp32 dequant + fp64 matmul) on the host cores, on a bounded
+    sample of the decode step: one decoder layer's four GEMMs plus 1/8 of the LM
+    head's columns, each timed REPS times, scaled to the full 129-GEMM step."""
+    REPS = 8
+    from oracle import int4_g128 as q4
+    from weight_only_quantized_w4a16_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    total = 0.0
+    parts = []
+    for j, (name, K, N) in enumerate(synth.LLAMA3_8B_LAYER):
+        w = synth.weights(K, N, seed=synth.weight_seed(0, j))
+        a = synth.activations(B, K, seed=synth.activation_seed(0, j))
+        codes, s = q4.quantize(w)                   # offline: not timed
+        del w
+        t = time.perf_counter()
+        for _ in range(REPS):
+            q4.gemm_ref(a, codes, s)
+        dt = (time.perf_counter() - t) / REPS
+        total += 32 * dt
+        parts.append(f"{name} {dt:.2f}s")
+        del codes, s
+    K, N = synth.LLAMA3_8B_HEAD[1:]
+    cols = N // 8
+    w = synth.weights(K, cols, seed=synth.weight_seed(32, 0))
+    a = synth.activations(B, K, seed=synth.activation_seed(32, 0))
+    codes, s = q4.quantize(w)
+    del w
+    t = time.perf_counter()
+    for _ in range(REPS):
+        q4.gemm_ref(a, codes, s)
+    dt = (time.perf_counter() - t) / REPS
+    total += 8 * dt
+    parts.append(f"lm_head[:, :{cols}] {dt:.2f}s")
+    return total, threads, parts
+
+
+# ----------------------------------------------------------------------------- main
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of 1 GiB, run 3 times: the counters of these
+    dispatches read COPY_BYTES fetched and COPY_BYTES written per dispatch."""
+    x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 3}))
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_traffic(dirs, command):
+    """KiB per dispatch of FETCH_SIZE / WRITE_SIZE for the dominant kernel, scaled
+    by what the same counters read for the calibration copy."""
+    fetch_dir, write_dir, cf_dir, cw_dir = dirs
+
+    def per_dispatch(d, counter, match):
+        vals = [float(r["Counter_Value"]) for r in _pmc_rows(d)
+                if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+        return sum(vals) / len(vals) if vals else None, len(vals)
+
+    is_dom = lambda n: DOMINANT_KERNEL in n
+    is_copy = lambda n: "copy" in n.lower() and "qg::" not in n
+    f_kib, nf = per_dispatch(fetch_dir, "FETCH_SIZE", is_dom)
+    w_kib, nw = per_dispatch(write_dir, "WRITE_SIZE", is_dom)
+    cf_kib, ncf = per_dispatch(cf_dir, "FETCH_SIZE", is_copy)
+    cw_kib, ncw = per_dispatch(cw_dir, "WRITE_SIZE", is_copy)
+    f_scale = (COPY_BYTES / 1024) / cf_kib
+    w_scale = (COPY_BYTES / 1024) / cw_kib
+    hbm = f_kib * 1024 * f_scale + w_kib * 1024 * w_scale
+    sha = hashlib.sha256(open(DOMINANT_SRC, "rb").read()).hexdigest()
+    lines = [
+        f"# HBM traffic of {DOMINANT_KERNEL}, Llama-3-8B W4A16 decode step, B=16",
+        f"# command: {command}",
+        "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) averaged over the kernel's",
+        "# dispatches, each scaled by copy_bytes / counter of a 1 GiB device copy.",
+        f"kernel: {DOMINANT_KERNEL}",
+        f"dispatches_fetch: {nf}",
+        f"dispatches_write: {nw}",
+        f"fetch_kib_per_dispatch_raw: {f_kib:.1f}",
+        f"write_kib_per_dispatch_raw: {w_kib:.1f}",
+        f"copy_fetch_kib_raw: {cf_kib:.1f}  (dispatches {ncf})",
+        f"copy_write_kib_raw: {cw_kib:.1f}  (dispatches {ncw})",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+        f"kernel_source_sha256: {sha}",
+    ]
+    out = TRAFFIC_FILE
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_stats(csv_path, command):
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    print(f"# rocprofv3 --kernel-trace --stats summary")
+    print(f"# command: {command}")
+    print(f"{'kernel':70s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_ms':>9s} {'pct':>6s}")
+    for r in rows:
+        name = r["Name"].split("(")[0][:70]
+        print(f"{name:70s} {int(r['Calls']):7d} {float(r['AverageNs'])/1e3:9.2f} "
+              f"{float(r['MinNs'])/1e3:9.2f} {float(r['MaxNs'])/1e3:9.2f} "
+              f"{float(r['TotalDurationNs'])/1e6:9.2f} {float(r['Percentage']):6.2f}")
+
+
+def main():
+    args = parse()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.command)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the quantized "
+                          "linear layer is measured on one GPU's share (see the sharding notes); "
+                          "--gpus N > 1 is not supported"}))
+        sys.exit(2)
+
+    import torch
+    from weight_only_quantized_w4a16_amd import ops, synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    if args.workload == "decode":
+        run_decode(args, torch, ops, synth)
+    elif args.workload == "large-batch":
+        run_large_batch(args, torch, ops, synth)
+    elif args.workload == "fp8":
+        run_fp8(args, torch, ops, synth)
+    else:
+        run_70b(args, torch, ops, synth)
+
+
+def run_decode(args, torch, ops, synth):
+    batches = [args.batch] if args.only_batch else sorted({1, 2, 4, 8, 16, args.batch})
+    stack = Stack(ops, synth, torch, "8b", batches)
+    print(f"[bench] packed {len(stack.layers)} GEMMs, {stack.bytes(0) / 1e9:.3f} GB of weights+scales",
+          file=sys.stderr, flush=True)
+    by_batch = {}
+    for B in batches:
+        g = graph_of(torch, lambda: stack.step(B))
+        ms = time_graph(torch, g, args.steps, args.warmup)
+        nbytes = stack.bytes(B)
+        by_batch[str(B)] = {"ms_per_step": round(ms, 4), "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3),
+                            "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+        print(f"[bench] B={B}: {ms:.4f} ms/step, {by_batch[str(B)]['TB_s']} TB/s",
+              file=sys.stderr, flush=True)
+        del g
+    B = args.batch
+    ms = by_batch[str(B)]["ms_per_step"]
+    nbytes = stack.bytes(B)
+
+    # dominant kernel: its launches alone, replayed as a graph; HIP events give the
+    # average launch duration on the stream the kernel runs on
+    dom = lambda r: dominant_rule(ops, B, r["K"], r["N"])
+    launches = sum(1 for r in stack.layers if dom(r))
+    g = graph_of(torch, lambda: stack.step(B, only=dom))
+    dom_ms = time_graph(torch, g, args.steps, args.warmup)
+    del g
+    dom_bytes_per_launch = stack.bytes(B, only=dom) / launches
+    dom_avg_us = dom_ms * 1e3 / launches
+    achieved = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9
+    sha = hashlib.sha256(open(DOMINANT_SRC, "rb").read()).hexdigest()
+    traffic = read_traffic(sha)
+
+    out = {
+        "metric": "Llama-3-8B W4A16 decode-step ms & HBM TB/s vs batch; MFMA util at B>=512",
+        "value": round(nbytes / (ms * 1e-3) / 1e12, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)",
+        "data": "synthetic: weights N(0, 0.02^2) bf16 RTN-quantized on the GPU, activations N(0,1) bf16",
+        "config": {"workload": "Llama-3-8B decode linear stack, W4A16 g128, 129 GEMMs "
+                               "(32 x qkv/o/gate_up/down + LM head), one HIP graph per step",
+                   "batch": B, "streamed_params": synth.stack_params("8b"),
+                   "algorithmic_bytes_per_step": nbytes, "parallelism": "single GPU"},
+        "by_batch": by_batch,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": DOMINANT_KERNEL + " (gate_up x32 + lm_head)",
+                     "launches_per_step": launches,
+                     "algorithmic_bytes_per_launch": round(dom_bytes_per_launch),
+                     "avg_launch_us": round(dom_avg_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        sec, threads, parts = cpu_baseline(B)
+        out["cpu_baseline"] = {
+            "value": round(nbytes / sec / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_step": round(sec, 2),
+            "sample": (f"B={B}: layer-0 qkv/o/gate_up/down (each x32) + LM head columns "
+                       f"[0, 16032) (x8), mean of 8 timed runs each; numpy fp32 dequant + fp64 matmul; "
+                       + ", ".join(parts))}
+    print(json.dumps(out), flush=True)
+
+
+def run_large_batch(args, torch, ops, synth):
+    batches = [32, 64, 128, 256, 384, 512, 1024]
+    stack = Stack(ops, synth, torch, "8b", batches)
+    dev = torch.device("cuda:0")
+    # the dense bf16 baseline: the same shapes, fresh bf16 weights (15.0 GB)
+    dense = []
+    for idx, (name, K, N) in enumerate(stack.shapes):
+        layer, j = divmod(idx, 4)
+        dense.append(synth.normal_bf16_device((K, N), synth.weight_seed(layer, j), synth.WEIGHT_STD, dev))
+    res = {}
+    for B in batches:
+        g = graph_of(torch, lambda: stack.step(B))
+        ms4 = time_graph(torch, g, args.steps, args.warmup)
+        del g
+
+        def dense_step():
+            for r, w in zip(stack.layers, dense):
+                torch.matmul(r["a"][:B], w, out=r["y"][:B])
+        g = graph_of(torch, dense_step)
+        ms16 = time_graph(torch, g, args.steps, args.warmup)
+        del g
+        fl = stack.flops(B)
+        res[str(B)] = {"w4a16_ms": round(ms4, 4), "bf16_ms": round(ms16, 4),
+                       "w4a16_mfma_frac": round(fl / (ms4 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                       "bf16_mfma_frac": round(fl / (ms16 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                       "w4a16_TB_s": round(stack.bytes(B) / (ms4 * 1e-3) / 1e12, 3)}
+        print(f"[bench] B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
+    cross = next((int(b) for b in res if res[b]["w4a16_ms"] >= res[b]["bf16_ms"]), None)
+    B = 512
+    out = {"metric": "Llama-3-8B W4A16 decode-step ms & HBM TB/s vs batch; MFMA util at B>=512",
+           "value": res["512"]["w4a16_mfma_frac"], "unit": "fraction of bf16 MFMA peak at B=512",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": res["512"]["w4a16_ms"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)",
+           "data": "synthetic", "config": {"workload": "Llama-3-8B W4A16 stack vs dense bf16 stack (torch.matmul)",
+                                           "batch": B},
+           "by_batch": res, "crossover_batch_w4a16_not_faster": cross}
+    print(json.dumps(out), flush=True)
+
+
+def run_fp8(args, torch, ops, synth):
+    batches = [1, 16, 128, 512, 1024]
+    stack = Stack(ops, synth, torch, "8b", batches, fp8=True)
+    res = {}
+    for B in batches:
+        g = graph_of(torch, lambda: stack.step(B))
+        ms = time_graph(torch, g, args.steps, args.warmup)
+        del g
+        res[str(B)] = {"ms_per_step": round(ms, 4),
+                       "TB_s": round(stack.bytes(B) / (ms * 1e-3) / 1e12, 3),
+                       "fp8_mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (FP8_PEAK_TFLOPS * 1e12), 4)}
+        print(f"[bench] fp8 B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
+    out = {"metric": "Llama-3-8B W8A8-FP8 decode-step ms vs batch", "value": res["16"]["TB_s"],
+           "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": res["16"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "e4m3 x e4m3 -> fp32 acc (fp8 MFMA)", "data": "synthetic",
+           "config": {"workload": "Llama-3-8B W8A8-FP8 stack incl. per-token activation quantization",
+                      "batch": 16}, "by_batch": res}
+    print(json.dumps(out), flush=True)
+
+
+def run_70b(args, torch, ops, synth):
+    batches = [1, 8, 64, 256]
+    stack = Stack(ops, synth, torch, "70b", batches)
+    res = {}
+    for B in batches:
+        g = graph_of(torch, lambda: stack.step(B))
+        ms = time_graph(torch, g, args.steps, args.warmup)
+        del g
+        res[str(B)] = {"ms_per_step": round(ms, 4),
+                       "TB_s": round(stack.bytes(B) / (ms * 1e-3) / 1e12, 3),
+                       "mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+        print(f"[bench] 70b B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
+    out = {"metric": "Llama-3-70B W4A16 decode-step ms vs batch (one GPU)", "value": res["1"]["TB_s"],
+           "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": res["1"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)", "data": "synthetic",
+           "config": {"workload": "Llama-3-70B decode linear stack, W4A16 g128, 321 GEMMs", "batch": 1},
+           "by_batch": res}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -79,6 +79,14 @@ const char *qg_version(void);
 size_t qg_int4_g128_packed_bytes(int64_t K, int64_t N);
 size_t qg_int4_g128_scale_bytes(int64_t K, int64_t N);
 
+/*
+ * Name of the kernel qgemm_w4a16 / qgemm_w8a8_fp8 launches for this shape on
+ * the current device (host only; static string; "" for an invalid shape).
+ * Useful to match profiler records to calls.
+ */
+const char *qg_w4a16_kernel_for(int64_t M, int64_t N, int64_t K);
+const char *qg_w8a8_kernel_for(int64_t M, int64_t N, int64_t K);
+
 /* Workspace bytes qgemm_w4a16 / qgemm_w8a8_fp8 need for this shape (may be 0). */
 size_t qg_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t qg_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -100,7 +108,7 @@ size_t qg_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Native order.  G = K/128, NT = N/16.  The words form NT*G tiles of 256
  * words; tile (nt, g) starts at word (nt*G + g)*256.  Word lane*4 + t of a tile
  * (lane < 64, t < 4) holds column n = 16*nt + lane%16 at rows
- * k = 128*g + 32*(lane/16) + 8*t + i, i < 8; nibble slot p (bits 4p..4p+3)
+ * k = 128*g + 32*t + 8*(lane/16) + i, i < 8; nibble slot p (bits 4p..4p+3)
  * holds i = 2p for p < 4 and i = 2(p-4)+1 for p >= 4, so that
  * ((word >> 4j) & 0x000F000F) | 0x43004300 is the bf16 pair
  * (128 + code[2j], 128 + code[2j+1]).  Scale (nt, g, c) sits at
@@ -172,7 +180,7 @@ qg_status quant_act_per_token(const uint16_t *a_bf16, int M, int K,
  *   w_e4m3   out  N*K bytes, native order: KT = K/128, NT = N/16 tiles of
  *                 2048 bytes, tile (nt, kt) at byte (nt*KT + kt)*2048; byte
  *                 lane*32 + i (lane < 64, i < 32) is column 16*nt + lane%16 at
- *                 row 128*kt + 32*(lane/16) + i.
+ *                 row 128*kt + 64*(i/16) + 16*(lane/16) + i%16.
  *   w_scale  out  [N] fp32, s = float(amax) / 448.0f; zero column -> 0.
  */
 qg_status quant_weight_fp8_per_channel(const uint16_t *w_bf16, int K, int N,

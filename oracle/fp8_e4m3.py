@@ -35,7 +35,9 @@ Requires K % 128 == 0 and N % 16 == 0.  KT = K/128, NT = N/16.  The buffer is
 N*K bytes in NT*KT tiles of 2048 bytes; tile (nt, kt) starts at byte
 (nt*KT + kt)*2048.  Byte lane*32 + i of a tile, lane in [0, 64), i in [0, 32),
 is the code of column n = 16*nt + lane%16 at input row
-k = 128*kt + 32*(lane//16) + i.
+k = 128*kt + 16*(lane//16) + i for i < 16 and k = 128*kt + 64 + 16*(lane//16) + (i-16)
+for i >= 16: each 16-byte half of a lane's slot covers 16 consecutive rows, and
+the four lane quarters tile 64 consecutive rows per half.
 """
 import numpy as np
 
@@ -127,7 +129,7 @@ def pack_native(qw):
         for kt in range(KT):
             base = (nt * KT + kt) * 2048
             for i in range(32):
-                rows = 128 * kt + 32 * (lane // 16) + i
+                rows = 128 * kt + 64 * (i // 16) + 16 * (lane // 16) + i % 16
                 out[base + lane * 32 + i] = qw[rows, cols]
     return out
 
@@ -142,7 +144,7 @@ def unpack_native(buf, K, N):
         for kt in range(KT):
             base = (nt * KT + kt) * 2048
             for i in range(32):
-                rows = 128 * kt + 32 * (lane // 16) + i
+                rows = 128 * kt + 64 * (i // 16) + 16 * (lane // 16) + i % 16
                 qw[rows, cols] = buf[base + lane * 32 + i]
     return qw
 

@@ -40,7 +40,8 @@ tiles.  The packed buffer is K*N/8 uint32 words made of NT*G tiles of 256
 words (1 KiB); tile (nt, g) starts at word (nt*G + g)*256.  Word
 (lane, t) of a tile, lane in [0, 64), t in [0, 4), sits at lane*4 + t and holds
 the eight codes of column n = 16*nt + lane%16 at input rows
-k = 128*g + 32*(lane//16) + 8*t + i, i in [0, 8).  Nibble slot p (bits 4p..4p+3)
+k = 128*g + 32*t + 8*(lane//16) + i, i in [0, 8): word t feeds MFMA k-step t,
+whose 32 rows the four lane quarters split into consecutive 8-row pieces.  Nibble slot p (bits 4p..4p+3)
 holds row offset i = SLOT_TO_ROW[p] = (0, 2, 4, 6, 1, 3, 5, 7)[p], so that
 slots p and p+4 hold the consecutive rows (2p, 2p+1).
 The native scales are NT*G*16 bf16 values; entry (nt, g, c) at
@@ -140,7 +141,7 @@ def pack_native(codes, scale_bits):
         for g in range(G):
             base = (nt * G + g) * 256
             for t in range(4):
-                kb = GROUP * g + 32 * (lane // 16) + 8 * t       # [64]
+                kb = GROUP * g + 32 * t + 8 * (lane // 16)       # [64]
                 word = np.zeros(64, dtype=np.uint32)
                 for p in range(8):
                     code = codes[kb + SLOT_TO_ROW[p], cols].astype(np.uint32)
@@ -166,7 +167,7 @@ def unpack_native(packed, scales, K, N):
         for g in range(G):
             base = (nt * G + g) * 256
             for t in range(4):
-                kb = GROUP * g + 32 * (lane // 16) + 8 * t
+                kb = GROUP * g + 32 * t + 8 * (lane // 16)
                 word = packed[base + lane * 4 + t]
                 for p in range(8):
                     codes[kb + SLOT_TO_ROW[p], cols] = (word >> np.uint32(4 * p)) & np.uint32(0xF)

@@ -80,7 +80,9 @@ def test_weight_quant_bit_exact(ops, K, N):
         rng = np.random.default_rng(0)
         k = rng.integers(0, K, 200000)
         n = rng.integers(0, N, 200000)
-        idx = ((n // 16) * (K // 128) + k // 128) * 2048 + (16 * ((k % 128) // 32) + n % 16) * 32 + k % 32
+        r = k % 128
+        idx = ((n // 16) * (K // 128) + k // 128) * 2048 + (16 * ((r % 64) // 16) + n % 16) * 32 \
+            + 16 * (r // 64) + r % 16
         assert np.array_equal(got[idx], qw_ref[k, n])
 
 

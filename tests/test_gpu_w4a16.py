@@ -55,8 +55,8 @@ def _native_nibbles(packed, k, n, K):
     G = K // 128
     nt, c = n // 16, n % 16
     g, r = k // 128, k % 128
-    j, r = r // 32, r % 32
-    t, i = r // 8, r % 8
+    t, r = r // 32, r % 32
+    j, i = r // 8, r % 8
     slot = np.where(i % 2 == 0, i // 2, 4 + i // 2)
     word = (nt * G + g) * 256 + (16 * j + c) * 4 + t
     return (packed[word] >> (4 * slot).astype(np.uint32)) & np.uint32(0xF)
@@ -254,3 +254,16 @@ def test_gemm_deterministic(ops, M):
     y2 = host_bits16(lin(a))
     torch.cuda.synchronize()
     assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("K,N", [(1024, 9600), (2048, 8208), (1280, 8192)])
+def test_gemm_wide_small_m(ops, M, K, N):
+    """Wide outputs at small M take the LDS-staged streaming kernel (tile ranges
+    that do not divide evenly over workgroups and waves; K = 1280 falls back)."""
+    announce(f"qgemm_w4a16 wide M={M} K={K} N={N}")
+    w = synth.weights(K, N, seed=31 + K + N)
+    a = synth.activations(M, K, seed=37 + M)
+    codes, s = q4.quantize(w)
+    y = _gemm(ops, _pack(ops, w), a)
+    assert_close_rms(y, q4.gemm_ref(a, codes, s), what=f"wide M={M} K={K} N={N}")

@@ -131,6 +131,7 @@ def test_native_order_direct_formula():
     for k, n in zip(rng.integers(0, K, 1000), rng.integers(0, N, 1000)):
         nt, c = divmod(int(n), 16)
         kt, r = divmod(int(k), 128)
-        j, i = divmod(r, 32)
-        assert buf[(nt * (K // 128) + kt) * 2048 + (16 * j + c) * 32 + i] == qw[k, n]
+        half, r = divmod(r, 64)
+        j, i = divmod(r, 16)
+        assert buf[(nt * (K // 128) + kt) * 2048 + (16 * j + c) * 32 + 16 * half + i] == qw[k, n]
     assert np.array_equal(f8.unpack_native(buf, K, N), qw)

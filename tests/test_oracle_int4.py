@@ -180,8 +180,8 @@ def _native_position(k, n, K):
     G = K // 128
     nt, c = divmod(n, 16)
     g, r = divmod(k, 128)
-    j, r = divmod(r, 32)
-    t, i = divmod(r, 8)
+    t, r = divmod(r, 32)
+    j, i = divmod(r, 8)
     lane = 16 * j + c
     slot = i // 2 if i % 2 == 0 else 4 + i // 2
     return (nt * G + g) * 256 + lane * 4 + t, 4 * slot
@@ -209,7 +209,7 @@ def test_native_word_yields_consecutive_bf16_pairs():
     for lane in range(64):
         for t in range(4):
             word = int(packed[lane * 4 + t])
-            kb = 32 * (lane // 16) + 8 * t
+            kb = 32 * t + 8 * (lane // 16)
             n = lane % 16
             for j in range(4):
                 pair = (word >> (4 * j)) & 0x000F000F

@@ -59,6 +59,16 @@ size_t qg_int4_g128_scale_bytes(int64_t K, int64_t N) {
     return (size_t)(K / 128 * N * 2);
 }
 
+const char* qg_w4a16_kernel_for(int64_t M, int64_t N, int64_t K) {
+    if (!shape_ok(M, N, K)) return "";
+    return qg::w4a16_kernel_for((int)M, (int)N, (int)K);
+}
+
+const char* qg_w8a8_kernel_for(int64_t M, int64_t N, int64_t K) {
+    if (!shape_ok(M, N, K)) return "";
+    return qg::w8a8_kernel_for((int)M, (int)N, (int)K);
+}
+
 size_t qg_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (!shape_ok(M, N, K)) return 0;
     return qg::w4a16_workspace_bytes((int)M, (int)N, (int)K);

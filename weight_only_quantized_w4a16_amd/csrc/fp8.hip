@@ -76,7 +76,8 @@ void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, flo
 // ---------------------------------------------------------------------------
 // quant_weight_fp8_per_channel: one workgroup per 16-column tile.  Pass 1:
 // column amax over K; pass 2: each lane writes its 32-byte slot of a native
-// 2 KiB tile (column 16*nt + l%16, rows 128*kt + 32*(l/16) .. +31).
+// 2 KiB tile: column 16*nt + l%16, rows 128*kt + 16*(l/16) .. +15 in the first
+// 16 bytes and rows 128*kt + 64 + 16*(l/16) .. +15 in the second.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* __restrict__ w,
                                                                int K, int N,
@@ -109,14 +110,15 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* _
     const int ln = nt * 16 + (lane & 15);
     const float s = scol[lane & 15];
     for (int kt = wave; kt < KT; kt += 4) {
-        const int k0 = kt * 128 + (lane >> 4) * 32;
-        uint32_t b[16];
+        const int k0 = kt * 128 + (lane >> 4) * 16;
+        uint32_t b[16];               // b[i] holds slot bytes 2i, 2i+1
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+            const int k = k0 + 64 * (i >> 3) + 2 * (i & 7);
             uint32_t v = 0u;
             if (s != 0.0f)
-                v = e4m3x2(bf16_to_f32(w[(size_t)(k0 + 2 * i) * N + ln]) / s,
-                           bf16_to_f32(w[(size_t)(k0 + 2 * i + 1) * N + ln]) / s);
+                v = e4m3x2(bf16_to_f32(w[(size_t)k * N + ln]) / s,
+                           bf16_to_f32(w[(size_t)(k + 1) * N + ln]) / s);
             b[i] = v;
         }
         u32x4* dst = reinterpret_cast<u32x4*>(q + ((size_t)nt * KT + kt) * 2048 + lane * 32);
@@ -138,7 +140,9 @@ void launch_quant_weight_fp8(const uint16_t* w, int K, int N, uint8_t* q, float*
 // ---------------------------------------------------------------------------
 // Small M (M <= 64): split-K inside the workgroup, as in the W4A16 kernel.
 // One 16x16x128 fp8 MFMA per (column tile, m-tile, 128-row k-tile); each lane
-// loads 32 contiguous bytes of A and of the weight tile.
+// loads its 32-byte slot of the weight tile and the matching two 16-byte
+// pieces of its A row (k = 16q .. +15 and 64 + 16q .. +15 for lane quarter q),
+// so each A load instruction reads 64 contiguous bytes per row.
 // ---------------------------------------------------------------------------
 template <int MT, int CT, int NWAVE, int U>
 __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
     const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
     const int KT = K >> 7;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int nt0 = blockIdx.x * CT;
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
     for (int mt = 0; mt < MT; ++mt) {
         const int m = mt * 16 + col;
         rowok[mt] = m < M;
-        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)(rowok[mt] ? m : 0) * K + kq * 32);
+        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)(rowok[mt] ? m : 0) * K) + kq;
     }
     const u32x4* wtile = reinterpret_cast<const u32x4*>(wq);
 
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     av[u][mt][0] = rowok[mt] ? arow[mt][kt * 8] : u32x4{0u, 0u, 0u, 0u};
-                    av[u][mt][1] = rowok[mt] ? arow[mt][kt * 8 + 1] : u32x4{0u, 0u, 0u, 0u};
+                    av[u][mt][1] = rowok[mt] ? arow[mt][kt * 8 + 4] : u32x4{0u, 0u, 0u, 0u};
                 }
             }
         }
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(256) void w8a8_large_m_kernel(
         for (int mi = 0; mi < 8; ++mi) {
             const int r = wm * 128 + mi * 16 + col;
             const int sw8 = (r >> 1) & 7;
-            const i32x8 af = cat_i32x8(As[buf][r][(kq * 2) ^ sw8], As[buf][r][(kq * 2 + 1) ^ sw8]);
+            const i32x8 af = cat_i32x8(As[buf][r][kq ^ sw8], As[buf][r][(4 + kq) ^ sw8]);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) total[mi][ni] = mfma_fp8_16x16x128(af, bfr[ni], total[mi][ni]);
         }
@@ -334,6 +338,19 @@ __global__ __launch_bounds__(256) void w8a8_large_m_kernel(
             }
         }
     }
+}
+
+const char* w8a8_kernel_for(int M, int N, int K) {
+    (void)K;
+    if (M == 0) return "none";
+    if (M > 64) return "w8a8_large_m_kernel";
+    const int NT = N / 16;
+    const int ct = (NT % 2 == 0 && NT >= 1024) ? 2 : 1;
+    static const char* names[3][2] = {
+        {"w8a8_small_m_kernel<1, 1>", "w8a8_small_m_kernel<1, 2>"},
+        {"w8a8_small_m_kernel<2, 1>", "w8a8_small_m_kernel<2, 2>"},
+        {"w8a8_small_m_kernel<4, 1>", "w8a8_small_m_kernel<4, 2>"}};
+    return names[M <= 16 ? 0 : M <= 32 ? 1 : 2][ct == 1 ? 0 : 1];
 }
 
 size_t w8a8_workspace_bytes(int M, int N, int K) {

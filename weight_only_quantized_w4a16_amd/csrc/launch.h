@@ -14,6 +14,7 @@ void launch_pack_int4_g128(const uint16_t* w, int K, int N, uint32_t* packed,
 void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, int K,
                               int N, uint16_t* w_out, uint8_t* codes_out, hipStream_t s);
 size_t w4a16_workspace_bytes(int M, int N, int K);
+const char* w4a16_kernel_for(int M, int N, int K);
 void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
                         uint16_t* y, int M, int N, int K, void* ws, hipStream_t s);
 
@@ -23,6 +24,7 @@ void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, flo
 void launch_quant_weight_fp8(const uint16_t* w, int K, int N, uint8_t* q, float* s,
                              hipStream_t st);
 size_t w8a8_workspace_bytes(int M, int N, int K);
+const char* w8a8_kernel_for(int M, int N, int K);
 void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w,
                            const float* sw, uint16_t* y, int M, int N, int K, void* ws,
                            hipStream_t st);

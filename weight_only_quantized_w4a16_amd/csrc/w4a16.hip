@@ -22,8 +22,9 @@ namespace qg {
 
 // ---------------------------------------------------------------------------
 // pack_int4_g128: one 64-lane workgroup per (column tile, group) tile.  Lane l
-// owns column 16*nt + l%16 and the 32 rows 32*(l/16) .. +31 of the group, which
-// is exactly the lane's 16-byte slot of the native tile.
+// owns column 16*nt + l%16 and, for each of the four MFMA k-steps t, the 8 rows
+// 32*t + 8*(l/16) .. +7 of the group: exactly the lane's 16-byte slot of the
+// native tile (word t of the slot feeds k-step t).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void pack_int4_g128_kernel(
     const uint16_t* __restrict__ w, int K, int N, uint32_t* __restrict__ packed,
@@ -36,16 +37,16 @@ __global__ __launch_bounds__(64) void pack_int4_g128_kernel(
     const int c = lane & 15;
     const int q = lane >> 4;
     const int n = nt * 16 + c;
-    const int k0 = g * 128 + q * 32;
+    const int k0 = g * 128 + q * 8;
 
-    float v[32];
+    float v[32];                  // v[8t + i] = w[k0 + 32t + i, n]
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        v[i] = bf16_to_f32(w[(size_t)(k0 + i) * N + n]);
+        v[i] = bf16_to_f32(w[(size_t)(k0 + 32 * (i >> 3) + (i & 7)) * N + n]);
         amax = fmaxf(amax, fabsf(v[i]));
     }
-    // the four lanes of one column hold its four 32-row quarters
+    // the four lanes of one column together hold all 128 rows of the group
     amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
 
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(64) void dequant_int4_g128_kernel(
     const int g = tile - nt * G;
     const int lane = threadIdx.x;
     const int n = nt * 16 + (lane & 15);
-    const int kq = g * 128 + (lane >> 4) * 32;
+    const int kq = g * 128 + (lane >> 4) * 8;
     const u32x4 wv = reinterpret_cast<const u32x4*>(packed)[(size_t)tile * 64 + lane];
     const float s = bf16_to_f32(scales[(size_t)tile * 16 + (lane & 15)]);
     const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(64) void dequant_int4_g128_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t pair = int4_pair_biased_bf16x2(words[t], j);   // (128+c_lo, 128+c_hi)
-            const int k = kq + 8 * t + 2 * j;
+            const int k = kq + 32 * t + 2 * j;
             const float lo = (bf16_to_f32(pair & 0xffffu) - 136.0f) * s;  // exact
             const float hi = (bf16_to_f32(pair >> 16) - 136.0f) * s;
             w_out[(size_t)k * N + n] = (uint16_t)f32_to_bf16_rne(lo);
@@ -125,25 +126,49 @@ void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, in
 //
 // A workgroup owns CT column tiles (16 columns each) over the whole K; its
 // NWAVE waves split the groups into contiguous ranges, so each wave streams
-// contiguous 1 KiB tiles.  MT 16-row m-tiles cover M.  Per group a wave loads
-// its A fragments once (64 contiguous bytes per lane and m-tile), computes the
-// offset term -136 * sum(a) with four MFMAs against a constant B, then for each
-// column tile unpacks one 128-bit word load and runs four MFMAs starting from
-// that offset term; the group sum is scaled into the running total.  The
-// waves' totals are reduced in LDS in a fixed order (deterministic).
+// contiguous 1 KiB tiles.  MT 16-row m-tiles cover M (rows >= M read row M-1
+// and their outputs are discarded).  Per group a wave loads its A fragments
+// once (for k-step t the four lane quarters read 64 contiguous bytes of each
+// row, so one load instruction touches one cache line per row), computes the offset term
+// -136 * sum(a) with four MFMAs against a constant B, then for each column
+// tile unpacks one 128-bit weight load and runs four MFMAs starting from that
+// offset term; the group sum is scaled into the running total.  The waves'
+// totals are reduced in LDS in a fixed order (deterministic).
+//
+// The unpack constants live in VGPRs: a VOP3 instruction reads at most one
+// scalar or literal operand here, and keeping both the nibble mask and the
+// bf16 magic in vector registers lets every pair compile to one v_and_or_b32
+// (3 shifts + 4 AND-ORs per 8 weights).
 // ---------------------------------------------------------------------------
+struct Int4Unpacker {
+    uint32_t mask, magic;
+    __device__ __forceinline__ Int4Unpacker() {
+        asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(mask));
+        asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
+    }
+    __device__ __forceinline__ bf16x8 operator()(uint32_t w) const {
+        u32x4 v;
+        v.x = (w & mask) | magic;
+        v.y = ((w >> 4) & mask) | magic;
+        v.z = ((w >> 8) & mask) | magic;
+        v.w = ((w >> 12) & mask) | magic;
+        return as_bf16x8(v);
+    }
+};
+
 template <int MT, int CT, int NWAVE, int U>
 __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K) {
     const int G = K >> 7;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int nt0 = blockIdx.x * CT;
     const int g_begin = (G * wave) / NWAVE;
-    const int g_end = (G * (wave + 1)) / NWAVE;
+    const int ng = (G * (wave + 1)) / NWAVE - g_begin;
+    const Int4Unpacker unpack;
 
     f32x4 total[CT][MT];
 #pragma unroll
@@ -155,57 +180,59 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
     negc_u.x = negc_u.y = negc_u.z = negc_u.w = 0xC308C308u;     // bf16 -136 everywhere
     const bf16x8 negc = as_bf16x8(negc_u);
 
+    // per-wave base pointers; the chunk loop adds immediate offsets
     const u32x4* arow[MT];
-    bool rowok[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + col;
-        rowok[mt] = m < M;
-        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)(rowok[mt] ? m : 0) * K + kq * 32);
+        const int m = min(mt * 16 + col, M - 1);
+        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)m * K) + kq + g_begin * 16;
     }
-    const u32x4* wtile = reinterpret_cast<const u32x4*>(wq);
+    const u32x4* wp[CT];
+    const uint16_t* sp[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const size_t tile = (size_t)(nt0 + ct) * G + g_begin;
+        wp[ct] = reinterpret_cast<const u32x4*>(wq) + tile * 64 + lane;
+        sp[ct] = sc + tile * 16 + col;
+    }
 
-    for (int g0 = g_begin; g0 < g_end; g0 += U) {
+    for (int g0 = 0; g0 < ng; g0 += U) {
         u32x4 wv[U][CT];
         uint32_t sv[U][CT];
         u32x4 av[U][MT][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int g = g0 + u;
-            if (g < g_end) {
+            if (g0 + u < ng) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const size_t tile = (size_t)(nt0 + ct) * G + g;
-                    wv[u][ct] = wtile[tile * 64 + lane];
-                    sv[u][ct] = sc[tile * 16 + col];
+                    wv[u][ct] = __builtin_nontemporal_load(wp[ct] + (g0 + u) * 64);
+                    sv[u][ct] = sp[ct][(g0 + u) * 16];
                 }
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        av[u][mt][t] = rowok[mt] ? arow[mt][g * 16 + t] : u32x4{0u, 0u, 0u, 0u};
-                }
+                    for (int t = 0; t < 4; ++t) av[u][mt][t] = arow[mt][(g0 + u) * 16 + 4 * t];
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (g0 + u < g_end) {
+            if (g0 + u < ng) {
                 f32x4 corr[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    corr[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    corr[mt] = mfma_bf16_16x16x32(as_bf16x8(av[u][mt][0]), negc, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                    for (int t = 1; t < 4; ++t)
                         corr[mt] = mfma_bf16_16x16x32(as_bf16x8(av[u][mt][t]), negc, corr[mt]);
                 }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     const float s = bf16_to_f32(sv[u][ct]);
                     bf16x8 bfr[4];
-                    bfr[0] = int4_word_biased_bf16x8(wv[u][ct].x);
-                    bfr[1] = int4_word_biased_bf16x8(wv[u][ct].y);
-                    bfr[2] = int4_word_biased_bf16x8(wv[u][ct].z);
-                    bfr[3] = int4_word_biased_bf16x8(wv[u][ct].w);
+                    bfr[0] = unpack(wv[u][ct].x);
+                    bfr[1] = unpack(wv[u][ct].y);
+                    bfr[2] = unpack(wv[u][ct].z);
+                    bfr[3] = unpack(wv[u][ct].w);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         f32x4 acc = corr[mt];
@@ -243,6 +270,161 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
         const int n = (nt0 + ct) * 16 + (l & 15);
         y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Small M, many column tiles (decode over wide outputs such as gate_up and the
+// LM head): the whole activation block a[M, K] is staged in LDS once per
+// workgroup with coalesced loads, together with the offset terms
+// -136 * sum_{k in g} a[m, k] for every row and group.  Each wave then owns whole
+// column tiles over the full K and streams their 1 KiB group tiles through a
+// two-stage register pipeline of U groups; the A fragments come from LDS
+// (each row padded by 16 bytes so the 16 rows of a fragment read hit distinct
+// banks).  There is no split-K and no cross-wave reduction: a wave writes its
+// tile's outputs directly.  The grid is sized to the number of compute units
+// and every workgroup gets a contiguous, nearly equal range of column tiles.
+// ---------------------------------------------------------------------------
+constexpr int ST_NWAVE = 8;
+constexpr int ST_U = 8;
+
+__device__ __forceinline__ int st_lds_row_bytes(int K) { return 2 * K + 16; }
+
+template <int TPW>
+__global__ __launch_bounds__(ST_NWAVE * 64) void w4a16_stream_kernel(
+    const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int G = K >> 7;
+    const int NT = N >> 4;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int rowb = st_lds_row_bytes(K);
+    float* corr = reinterpret_cast<float*>(lds + (size_t)M * rowb);   // [G][16]
+
+    // this workgroup's column tiles, then this wave's share of them
+    const int t_begin = (int)(((long long)NT * blockIdx.x) / gridDim.x);
+    const int t_end = (int)(((long long)NT * (blockIdx.x + 1)) / gridDim.x);
+    const int nchunk = G / ST_U;               // host guarantees G % ST_U == 0
+    const int ntiles = (t_end - t_begin - wave + ST_NWAVE - 1) / ST_NWAVE;   // may be <= 0
+    const int nitems = ntiles > 0 ? ntiles * nchunk : 0;
+
+    auto item_tile = [&](int it) { return t_begin + wave + (it / nchunk) * ST_NWAVE; };
+
+    // An item is ST_U consecutive group tiles of one column tile: ST_U KiB of
+    // weights (one 16-byte load per lane and group) and ST_U * 32 contiguous
+    // bytes of scales, fetched as one dword per lane: lane l holds the scales of
+    // group l/8, columns 2*(l%8) and 2*(l%8)+1.
+    u32x4 wb[2][ST_U];
+    uint32_t sb[2];
+    auto load_item = [&](int it, int slot) {
+        const int nt = item_tile(it);
+        const int g0 = (it % nchunk) * ST_U;
+        const size_t tile0 = (size_t)nt * G + g0;          // wave-uniform
+        const u32x4* wp = reinterpret_cast<const u32x4*>(wq) + tile0 * 64;
+#pragma unroll
+        for (int u = 0; u < ST_U; ++u) wb[slot][u] = __builtin_nontemporal_load(wp + u * 64 + lane);
+        sb[slot] = reinterpret_cast<const uint32_t*>(sc + tile0 * 16)[lane];
+    };
+    // weights do not depend on the activations: start streaming before staging A
+    if (nitems > 0) load_item(0, 0);
+
+    // stage a[M, K] (16-byte chunks, row-major, padded rows)
+    {
+        const int cpr = K >> 3;                // chunks per row
+        const int total = M * cpr;
+        const u32x4* src = reinterpret_cast<const u32x4*>(a);
+        for (int c = tid; c < total; c += ST_NWAVE * 64) {
+            const int r = c / cpr;
+            const int cc = c - r * cpr;
+            *reinterpret_cast<u32x4*>(lds + (size_t)r * rowb + cc * 16) = src[c];
+        }
+    }
+    __syncthreads();
+    // offset terms: corr[g][m] = -136 * sum of row m over group g
+    for (int p = tid; p < G * M; p += ST_NWAVE * 64) {
+        const int g = p / M;
+        const int m = p - g * M;
+        const u32x4* row = reinterpret_cast<const u32x4*>(lds + (size_t)m * rowb + g * 256);
+        float s = 0.0f;
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const u32x4 v = row[i];
+            s += bf16_to_f32(v.x & 0xffffu) + bf16_to_f32(v.x >> 16);
+            s += bf16_to_f32(v.y & 0xffffu) + bf16_to_f32(v.y >> 16);
+            s += bf16_to_f32(v.z & 0xffffu) + bf16_to_f32(v.z >> 16);
+            s += bf16_to_f32(v.w & 0xffffu) + bf16_to_f32(v.w >> 16);
+        }
+        corr[g * 16 + m] = -136.0f * s;
+    }
+    __syncthreads();
+
+    const Int4Unpacker unpack;
+    // A fragment row of this lane (rows >= M repeat row M-1; their outputs are dropped)
+    const unsigned char* arow = lds + (size_t)min(col, M - 1) * rowb + kq * 16;
+    const float* crow = corr + 4 * kq;
+    f32x4 total = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // scale of (group u of the item, this lane's column): lane 8u + col/2, half col%2
+    const int sidx = (col >> 1) << 2;                 // byte address of lane col/2 for ds_bpermute
+    const int shalf = (col & 1) << 4;
+    auto compute_item = [&](int it, int slot) {
+        const int g0 = (it % nchunk) * ST_U;
+#pragma unroll
+        for (int u = 0; u < ST_U; ++u) {
+            const int g = g0 + u;
+            f32x4 acc = *reinterpret_cast<const f32x4*>(crow + g * 16);
+            const uint32_t pair = (uint32_t)__builtin_amdgcn_ds_bpermute(sidx + u * 32, (int)sb[slot]);
+            const float s = bf16_to_f32((pair >> shalf) & 0xffffu);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + g * 256 + t * 64));
+                const uint32_t w = t == 0 ? wb[slot][u].x : t == 1 ? wb[slot][u].y
+                                 : t == 2 ? wb[slot][u].z : wb[slot][u].w;
+                acc = mfma_bf16_16x16x32(af, unpack(w), acc);
+            }
+            total[0] = fmaf(s, acc[0], total[0]);
+            total[1] = fmaf(s, acc[1], total[1]);
+            total[2] = fmaf(s, acc[2], total[2]);
+            total[3] = fmaf(s, acc[3], total[3]);
+        }
+        if ((it % nchunk) == nchunk - 1) {       // tile finished: store and reset
+            const int n = item_tile(it) * 16 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * kq + i;
+                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[i]);
+            }
+            total = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    // Steady state: the loop body's prefetches are unconditional, so the loads
+    // stay straight-line code (a load under a branch makes the compiler wait
+    // for every outstanding load before using the current item, which drains
+    // the pipeline); the scheduling barriers keep each prefetch issued ahead of
+    // the wait for the item being computed.  The last one or two items are
+    // peeled off, so nothing is fetched twice.
+    int it = 0;
+    for (; it + 2 < nitems; it += 2) {
+        load_item(it + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_item(it, 0);
+        load_item(it + 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_item(it + 1, 1);
+    }
+    if (it + 1 < nitems) {
+        load_item(it + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_item(it, 0);
+        compute_item(it + 1, 1);
+    } else if (it < nitems) {
+        compute_item(it, 0);
+    }
+    (void)TPW;
 }
 
 // ---------------------------------------------------------------------------
@@ -381,7 +563,7 @@ __global__ __launch_bounds__(256) void w4a16_large_m_kernel(
         for (int mi = 0; mi < 4; ++mi) {
             const int r = wm * 64 + mi * 16 + col;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) af[mi][t] = as_bf16x8(As[buf][r][(kq * 4 + t) ^ col]);
+            for (int t = 0; t < 4; ++t) af[mi][t] = as_bf16x8(As[buf][r][(4 * t + kq) ^ col]);
         }
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
@@ -431,11 +613,25 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
     return (size_t)(K / 128) * (size_t)round_up(M, LM_BM) * sizeof(float);
 }
 
+// Tuning knobs of the small-M dispatch (compile-time; defaults measured on MI355X).
+#ifndef QG_SM_NWAVE
+#define QG_SM_NWAVE 8
+#endif
+#ifndef QG_SM_U
+#define QG_SM_U 2
+#endif
+#ifndef QG_SM_CT2_MIN_TILES   // use 2 column tiles per workgroup from this many tiles
+#define QG_SM_CT2_MIN_TILES 1024
+#endif
+#ifndef QG_SM_CT4_MIN_TILES   // use 4 column tiles per workgroup from this many tiles
+#define QG_SM_CT4_MIN_TILES (1 << 30)
+#endif
+
 template <int MT, int CT>
 static void launch_small(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
                          int M, int N, int K, hipStream_t s) {
-    constexpr int NWAVE = 8;
-    constexpr int U = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
+    constexpr int NWAVE = QG_SM_NWAVE;
+    constexpr int U = MT == 1 ? QG_SM_U : (MT == 2 ? 2 : 1);
     const int NT = N / 16;
     hipLaunchKernelGGL((w4a16_small_m_kernel<MT, CT, NWAVE, U>), dim3(NT / CT), dim3(NWAVE * 64),
                        0, s, a, wq, sc, y, M, N, K);
@@ -445,15 +641,78 @@ template <int MT>
 static void launch_small_ct(const uint16_t* a, const uint32_t* wq, const uint16_t* sc,
                             uint16_t* y, int M, int N, int K, hipStream_t s) {
     const int NT = N / 16;
-    if (NT % 2 == 0 && NT >= 1024)
+    if (NT % 4 == 0 && NT >= QG_SM_CT4_MIN_TILES)
+        launch_small<MT, 4>(a, wq, sc, y, M, N, K, s);
+    else if (NT % 2 == 0 && NT >= QG_SM_CT2_MIN_TILES)
         launch_small<MT, 2>(a, wq, sc, y, M, N, K, s);
     else
         launch_small<MT, 1>(a, wq, sc, y, M, N, K, s);
 }
 
+#ifndef QG_ST_MIN_TILES_PER_CU   // use the LDS-staged streaming kernel from this many tiles per CU
+#define QG_ST_MIN_TILES_PER_CU 2
+#endif
+#ifndef QG_ST_LDS_BUDGET
+#define QG_ST_LDS_BUDGET (144 * 1024)
+#endif
+
+static int device_cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+static size_t stream_lds_bytes(int M, int K) {
+    return (size_t)M * (2 * (size_t)K + 16) + (size_t)(K / 128) * 16 * sizeof(float);
+}
+
+static bool use_stream_kernel(int M, int N, int K, int cus) {
+    const int NT = N / 16;
+    return M <= 16 && (K / 128) % ST_U == 0 && stream_lds_bytes(M, K) <= QG_ST_LDS_BUDGET &&
+           NT >= QG_ST_MIN_TILES_PER_CU * cus;
+}
+
+static void launch_stream(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
+                          int M, int N, int K, int cus, hipStream_t s) {
+    const size_t lds = stream_lds_bytes(M, K);
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_stream_kernel<1>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, QG_ST_LDS_BUDGET);
+        attr_set = true;
+    }
+    const int per_cu = lds * 2 <= 160 * 1024 ? 2 : 1;
+    const int NT = N / 16;
+    const int grid = min(NT, cus * per_cu);
+    hipLaunchKernelGGL(w4a16_stream_kernel<1>, dim3(grid), dim3(ST_NWAVE * 64), lds, s, a, wq, sc,
+                       y, M, N, K);
+}
+
+const char* w4a16_kernel_for(int M, int N, int K) {
+    static const int cus = device_cu_count();
+    if (M == 0) return "none";
+    if (use_stream_kernel(M, N, K, cus)) return "w4a16_stream_kernel";
+    if (M <= 64) {
+        const int NT = N / 16;
+        const int ct = (NT % 4 == 0 && NT >= QG_SM_CT4_MIN_TILES) ? 4
+                     : (NT % 2 == 0 && NT >= QG_SM_CT2_MIN_TILES) ? 2 : 1;
+        static const char* names[3][3] = {
+            {"w4a16_small_m_kernel<1, 1>", "w4a16_small_m_kernel<1, 2>", "w4a16_small_m_kernel<1, 4>"},
+            {"w4a16_small_m_kernel<2, 1>", "w4a16_small_m_kernel<2, 2>", "w4a16_small_m_kernel<2, 4>"},
+            {"w4a16_small_m_kernel<4, 1>", "w4a16_small_m_kernel<4, 2>", "w4a16_small_m_kernel<4, 4>"}};
+        return names[M <= 16 ? 0 : M <= 32 ? 1 : 2][ct == 1 ? 0 : ct == 2 ? 1 : 2];
+    }
+    return "w4a16_large_m_kernel";
+}
+
 void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
                         uint16_t* y, int M, int N, int K, void* ws, hipStream_t s) {
-    if (M <= 16) {
+    static const int cus = device_cu_count();
+    if (use_stream_kernel(M, N, K, cus)) {
+        launch_stream(a, packed, scales, y, M, N, K, cus, s);
+    } else if (M <= 16) {
         launch_small_ct<1>(a, packed, scales, y, M, N, K, s);
     } else if (M <= 32) {
         launch_small_ct<2>(a, packed, scales, y, M, N, K, s);

@@ -14,7 +14,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqgemm.so")
+# QGEMM_LIBRARY selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("QGEMM_LIBRARY") or os.path.join(_PKG, "libqgemm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -33,6 +34,8 @@ _SIGS = {
     "qg_version": (ctypes.c_char_p, []),
     "qg_int4_g128_packed_bytes": (_SZ, [_I64, _I64]),
     "qg_int4_g128_scale_bytes": (_SZ, [_I64, _I64]),
+    "qg_w4a16_kernel_for": (ctypes.c_char_p, [_I64, _I64, _I64]),
+    "qg_w8a8_kernel_for": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "qg_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qg_w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "pack_int4_g128": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -70,6 +73,14 @@ def packed_bytes(K, N):
 
 def scale_bytes(K, N):
     return _lib.qg_int4_g128_scale_bytes(K, N)
+
+
+def w4a16_kernel_for(M, N, K):
+    return _lib.qg_w4a16_kernel_for(M, N, K).decode()
+
+
+def w8a8_kernel_for(M, N, K):
+    return _lib.qg_w8a8_kernel_for(M, N, K).decode()
 
 
 def w4a16_workspace_bytes(M, N, K):

@@ -141,7 +141,11 @@ qg_status dequant_int4_g128(const uint32_t *packed, const uint16_t *scales,
  *   scales     in   native bf16 scales from pack_int4_g128.
  *   y_bf16     out  [M, N].
  *   workspace  scratch of qg_w4a16_workspace_bytes(M, N, K) bytes (may be
- *              NULL when that is 0); its contents are overwritten.
+ *              NULL when that is 0).  It must be zero-filled before its
+ *              first use.  It holds fp32 partial sums (scratch) followed by
+ *              completion counters that every call resets to zero, so one
+ *              workspace stays valid for later calls of any shape.  Calls
+ *              that share a workspace must not overlap in time.
  *
  * Numerics (folded offset): the MFMA multiplies the bf16 activations with the
  * exact bf16 values 128 + code; per group and row the kernel adds

@@ -55,13 +55,28 @@ def test_status_strings_and_version(lib):
     assert "gfx950" in lib.version()
 
 
+def test_kernel_selection_query(lib):
+    assert lib.w4a16_kernel_for(1, 28672, 4096) == "w4a16_decode_kernel"
+    assert lib.w4a16_kernel_for(16, 4096, 14336) == "w4a16_decode_kernel"
+    assert lib.w4a16_kernel_for(4, 4096, 14336).startswith("w4a16_small_m_kernel<1")
+    assert lib.w4a16_kernel_for(32, 4096, 4096).startswith("w4a16_small_m_kernel<2")
+    assert lib.w4a16_kernel_for(512, 4096, 4096) == "w4a16_large_m_kernel"
+    assert lib.w4a16_kernel_for(4, 4096, 4000) == ""                 # invalid shape
+    assert lib.w8a8_kernel_for(512, 4096, 4096) == "w8a8_large_m_kernel"
+
+
 def test_size_queries(lib):
     for K, N in [(4096, 4096), (4096, 6144), (14336, 4096), (4096, 128256), (128, 16)]:
         assert lib.packed_bytes(K, N) == K * N // 2
         assert lib.scale_bytes(K, N) == K // 128 * N * 2
         assert (lib.packed_bytes(K, N) + lib.scale_bytes(K, N)) * 8 == 4.125 * K * N
     assert lib.packed_bytes(100, 16) == 0 and lib.packed_bytes(128, 17) == 0
-    assert lib.w4a16_workspace_bytes(4, 4096, 4096) == 0          # small M: in-workgroup split-K
+    # decode (M <= 16): wide outputs need none, narrow ones fp32 slots + counters
+    assert lib.w4a16_workspace_bytes(4, 28672, 4096) == 0
+    assert lib.w4a16_workspace_bytes(16, 128256, 4096) == 0
+    assert lib.w4a16_workspace_bytes(16, 4096, 14336) > 0           # long K split across workgroups
+    assert lib.w4a16_workspace_bytes(4, 4096, 4096) == 0
+    assert lib.w4a16_workspace_bytes(32, 4096, 4096) == 0          # M <= 64: in-workgroup split-K
     assert lib.w4a16_workspace_bytes(1024, 4096, 4096) == 32 * 1024 * 4
     assert lib.w4a16_workspace_bytes(100, 4096, 4096) == 32 * 128 * 4   # rows padded to 128
     assert lib.w8a8_workspace_bytes(1024, 4096, 4096) == 0

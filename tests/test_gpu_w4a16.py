@@ -256,14 +256,41 @@ def test_gemm_deterministic(ops, M):
     assert np.array_equal(y1, y2)
 
 
-@pytest.mark.parametrize("M", [1, 3, 16])
-@pytest.mark.parametrize("K,N", [(1024, 9600), (2048, 8208), (1280, 8192)])
+@pytest.mark.parametrize("M", [1, 3, 5, 16])
+@pytest.mark.parametrize("K,N", [(1024, 9600), (2048, 8208), (1280, 8192), (8320, 144), (8192, 2064)])
 def test_gemm_wide_small_m(ops, M, K, N):
-    """Wide outputs at small M take the LDS-staged streaming kernel (tile ranges
-    that do not divide evenly over workgroups and waves; K = 1280 falls back)."""
+    """Small M through the decode kernel: wide outputs in one K-slice (tile ranges
+    that do not divide evenly over workgroups and waves), long-K narrow outputs
+    split across workgroups (M > 4), the rest through the split-K kernel."""
     announce(f"qgemm_w4a16 wide M={M} K={K} N={N}")
     w = synth.weights(K, N, seed=31 + K + N)
     a = synth.activations(M, K, seed=37 + M)
     codes, s = q4.quantize(w)
     y = _gemm(ops, _pack(ops, w), a)
     assert_close_rms(y, q4.gemm_ref(a, codes, s), what=f"wide M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 14336, 4096), (16, 14336, 4096), (5, 8320, 144)])
+def test_decode_workspace_counters_reset(ops, M, K, N):
+    """Narrow decode shapes split K across workgroups and count arrivals in the
+    workspace; every call resets its counters, so repeated calls on one
+    workspace keep giving the right answer and the counter region (one 32-bit
+    counter per strip of 8 column tiles, at the end of the workspace) is zero."""
+    announce(f"qgemm_w4a16 workspace counters M={M} K={K} N={N}")
+    nbytes = ops.w4a16_workspace_bytes(M, N, K)
+    assert nbytes > 0
+    n_strips = max(1, (N // 16) // 8)
+    w = synth.weights(K, N, seed=41)
+    a = synth.activations(M, K, seed=43)
+    codes, s = q4.quantize(w)
+    lin = ops.W4A16Linear(_pack(ops, w))
+    ad = dev_bf16(a)
+    first = None
+    for _ in range(3):
+        y = host_bits16(lin(ad))
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(lin._ws[nbytes - 4 * n_strips:nbytes])) == 0
+        assert_close_rms(y, q4.gemm_ref(a, codes, s), what=f"M={M} K={K} N={N}")
+        if first is None:
+            first = y
+        assert np.array_equal(y, first)

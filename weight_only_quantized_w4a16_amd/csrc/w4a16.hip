@@ -273,108 +273,120 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Small M, many column tiles (decode over wide outputs such as gate_up and the
-// LM head): the whole activation block a[M, K] is staged in LDS once per
-// workgroup with coalesced loads, together with the offset terms
-// -136 * sum_{k in g} a[m, k] for every row and group.  Each wave then owns whole
-// column tiles over the full K and streams their 1 KiB group tiles through a
-// two-stage register pipeline of U groups; the A fragments come from LDS
-// (each row padded by 16 bytes so the 16 rows of a fragment read hit distinct
-// banks).  There is no split-K and no cross-wave reduction: a wave writes its
-// tile's outputs directly.  The grid is sized to the number of compute units
-// and every workgroup gets a contiguous, nearly equal range of column tiles.
+// Decode (M <= 16): one kernel for every output width.
+//
+// Workgroup (split s, strip p) owns the column tiles [t0, t1) of strip p and
+// the groups [g0, g1) of K-slice s.  It stages a[:, 128*g0 : 128*g1] and the
+// offset terms -136 * sum_{k in g} a[m, k] in LDS once (coalesced loads; rows
+// padded by 16 bytes so a fragment read hits 16 distinct bank groups), so the
+// activation bytes it reads per weight byte are M / (4 * tiles), not M / 4.
+// Its 8 waves are KW K-sub-ranges x 8/KW tile slots; a wave streams its
+// (tile, chunk of U groups) items through a two-stage register pipeline.
+//   - one slice, KW = 1 (wide outputs: gate_up, LM head): a wave finishes
+//     whole tiles and stores bf16 directly;
+//   - KW > 1: the KW partial sums of a tile are added in LDS in a fixed order;
+//   - S > 1 slices (narrow outputs: qkv, o, down): each workgroup writes its
+//     fp32 partial tile sums to its own workspace slot, then increments the
+//     strip's counter; the workgroup that arrives last adds the S slots in
+//     slice order (deterministic), stores bf16 and resets the counter to 0.
+//     The slots are written and read with agent-scope relaxed atomic accesses
+//     (coherent across the XCDs without cache maintenance); a device-wide
+//     fence would instead write back and invalidate every XCD's whole L2 on
+//     each call, which costs more than the GEMM.
 // ---------------------------------------------------------------------------
-constexpr int ST_NWAVE = 8;
-constexpr int ST_U = 8;
+constexpr int DK_NWAVE = 8;
 
-__device__ __forceinline__ int st_lds_row_bytes(int K) { return 2 * K + 16; }
-
-template <int TPW>
-__global__ __launch_bounds__(ST_NWAVE * 64) void w4a16_stream_kernel(
+template <int KW, int U>
+__global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
-    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K) {
+    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K, int S,
+    int NS, float* __restrict__ part, unsigned* __restrict__ cnt) {
+    constexpr int TW = DK_NWAVE / KW;            // tile slots
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    __shared__ int last_flag;
     const int G = K >> 7;
     const int NT = N >> 4;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int kq = lane >> 4;
-    const int rowb = st_lds_row_bytes(K);
-    float* corr = reinterpret_cast<float*>(lds + (size_t)M * rowb);   // [G][16]
-
-    // this workgroup's column tiles, then this wave's share of them
-    const int t_begin = (int)(((long long)NT * blockIdx.x) / gridDim.x);
-    const int t_end = (int)(((long long)NT * (blockIdx.x + 1)) / gridDim.x);
-    const int nchunk = G / ST_U;               // host guarantees G % ST_U == 0
-    const int ntiles = (t_end - t_begin - wave + ST_NWAVE - 1) / ST_NWAVE;   // may be <= 0
+    const int strip = blockIdx.x % NS;
+    const int split = blockIdx.x / NS;
+    const int t0 = (int)(((long long)NT * strip) / NS);
+    const int t1 = (int)(((long long)NT * (strip + 1)) / NS);
+    const int g0 = (G / S) * split;              // host guarantees G % (S * KW * U) == 0
+    const int Gs = G / S;
+    const int ksub = wave % KW;
+    const int tslot = wave / KW;
+    const int ng = Gs / KW;                      // groups per wave
+    const int gw0 = ksub * ng;                   // first group of the wave, within the slice
+    const int nchunk = ng / U;
+    const int ntiles = (t1 - t0 - tslot + TW - 1) / TW;
     const int nitems = ntiles > 0 ? ntiles * nchunk : 0;
 
-    auto item_tile = [&](int it) { return t_begin + wave + (it / nchunk) * ST_NWAVE; };
+    const int rowb = Gs * 256 + 16;              // bytes per staged activation row
+    float* corr = reinterpret_cast<float*>(lds + (size_t)M * rowb);   // [Gs][16]
+    float* red = corr + Gs * 16;                                        // [T][KW][256]
 
-    // An item is ST_U consecutive group tiles of one column tile: ST_U KiB of
-    // weights (one 16-byte load per lane and group) and ST_U * 32 contiguous
-    // bytes of scales, fetched as one dword per lane: lane l holds the scales of
-    // group l/8, columns 2*(l%8) and 2*(l%8)+1.
-    u32x4 wb[2][ST_U];
+    auto item_tile = [&](int it) { return t0 + tslot + (it / nchunk) * TW; };
+
+    u32x4 wb[2][U];
     uint32_t sb[2];
+    // scales of an item: U * 16 contiguous bf16 = U * 8 dwords; lane l < 8U holds
+    // those of group l/8, columns 2*(l%8), 2*(l%8)+1 (other lanes repeat a dword)
+    const int slane = lane % (8 * U);
     auto load_item = [&](int it, int slot) {
         const int nt = item_tile(it);
-        const int g0 = (it % nchunk) * ST_U;
-        const size_t tile0 = (size_t)nt * G + g0;          // wave-uniform
+        const size_t tile0 = (size_t)nt * G + g0 + gw0 + (it % nchunk) * U;   // wave-uniform
         const u32x4* wp = reinterpret_cast<const u32x4*>(wq) + tile0 * 64;
 #pragma unroll
-        for (int u = 0; u < ST_U; ++u) wb[slot][u] = __builtin_nontemporal_load(wp + u * 64 + lane);
-        sb[slot] = reinterpret_cast<const uint32_t*>(sc + tile0 * 16)[lane];
+        for (int u = 0; u < U; ++u) wb[slot][u] = __builtin_nontemporal_load(wp + u * 64 + lane);
+        sb[slot] = reinterpret_cast<const uint32_t*>(sc + tile0 * 16)[slane];
     };
-    // weights do not depend on the activations: start streaming before staging A
-    if (nitems > 0) load_item(0, 0);
+    if (nitems > 0) load_item(0, 0);             // weights first: they do not depend on a
 
-    // stage a[M, K] (16-byte chunks, row-major, padded rows)
-    {
-        const int cpr = K >> 3;                // chunks per row
+    {   // stage the activation slice, 16-byte chunks
+        const int cpr = Gs * 16;                 // chunks per staged row
         const int total = M * cpr;
-        const u32x4* src = reinterpret_cast<const u32x4*>(a);
-        for (int c = tid; c < total; c += ST_NWAVE * 64) {
+        for (int c = tid; c < total; c += DK_NWAVE * 64) {
             const int r = c / cpr;
             const int cc = c - r * cpr;
-            *reinterpret_cast<u32x4*>(lds + (size_t)r * rowb + cc * 16) = src[c];
+            const u32x4 v = reinterpret_cast<const u32x4*>(a + (size_t)r * K + (size_t)g0 * 128)[cc];
+            *reinterpret_cast<u32x4*>(lds + (size_t)r * rowb + cc * 16) = v;
         }
     }
     __syncthreads();
-    // offset terms: corr[g][m] = -136 * sum of row m over group g
-    for (int p = tid; p < G * M; p += ST_NWAVE * 64) {
+    for (int p = tid; p < Gs * M; p += DK_NWAVE * 64) {   // offset terms
         const int g = p / M;
         const int m = p - g * M;
         const u32x4* row = reinterpret_cast<const u32x4*>(lds + (size_t)m * rowb + g * 256);
-        float s = 0.0f;
+        float sum = 0.0f;
 #pragma unroll 4
         for (int i = 0; i < 16; ++i) {
             const u32x4 v = row[i];
-            s += bf16_to_f32(v.x & 0xffffu) + bf16_to_f32(v.x >> 16);
-            s += bf16_to_f32(v.y & 0xffffu) + bf16_to_f32(v.y >> 16);
-            s += bf16_to_f32(v.z & 0xffffu) + bf16_to_f32(v.z >> 16);
-            s += bf16_to_f32(v.w & 0xffffu) + bf16_to_f32(v.w >> 16);
+            sum += bf16_to_f32(v.x & 0xffffu) + bf16_to_f32(v.x >> 16);
+            sum += bf16_to_f32(v.y & 0xffffu) + bf16_to_f32(v.y >> 16);
+            sum += bf16_to_f32(v.z & 0xffffu) + bf16_to_f32(v.z >> 16);
+            sum += bf16_to_f32(v.w & 0xffffu) + bf16_to_f32(v.w >> 16);
         }
-        corr[g * 16 + m] = -136.0f * s;
+        corr[g * 16 + m] = -136.0f * sum;
     }
     __syncthreads();
 
     const Int4Unpacker unpack;
-    // A fragment row of this lane (rows >= M repeat row M-1; their outputs are dropped)
     const unsigned char* arow = lds + (size_t)min(col, M - 1) * rowb + kq * 16;
     const float* crow = corr + 4 * kq;
+    const int sidx = (col >> 1) << 2;            // ds_bpermute byte address of lane col/2
+    const int shalf = (col & 1) << 4;
+    const bool direct = (KW == 1) && (S == 1);
     f32x4 total = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // scale of (group u of the item, this lane's column): lane 8u + col/2, half col%2
-    const int sidx = (col >> 1) << 2;                 // byte address of lane col/2 for ds_bpermute
-    const int shalf = (col & 1) << 4;
     auto compute_item = [&](int it, int slot) {
-        const int g0 = (it % nchunk) * ST_U;
+        const int gl0 = gw0 + (it % nchunk) * U;            // group within the slice
 #pragma unroll
-        for (int u = 0; u < ST_U; ++u) {
-            const int g = g0 + u;
+        for (int u = 0; u < U; ++u) {
+            const int g = gl0 + u;
             f32x4 acc = *reinterpret_cast<const f32x4*>(crow + g * 16);
             const uint32_t pair = (uint32_t)__builtin_amdgcn_ds_bpermute(sidx + u * 32, (int)sb[slot]);
             const float s = bf16_to_f32((pair >> shalf) & 0xffffu);
@@ -390,23 +402,29 @@ __global__ __launch_bounds__(ST_NWAVE * 64) void w4a16_stream_kernel(
             total[2] = fmaf(s, acc[2], total[2]);
             total[3] = fmaf(s, acc[3], total[3]);
         }
-        if ((it % nchunk) == nchunk - 1) {       // tile finished: store and reset
-            const int n = item_tile(it) * 16 + col;
+        if ((it % nchunk) == nchunk - 1) {       // the wave's share of a tile is done
+            const int tile = item_tile(it);
+            if (direct) {
+                const int n = tile * 16 + col;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * kq + i;
-                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int m = 4 * kq + i;
+                    if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[i]);
+                }
+            } else if (KW == 1) {                // whole tile in this wave: publish the slot
+                float* dst = part + ((size_t)split * NT + tile) * 256 + lane * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __hip_atomic_store(dst + i, total[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                *reinterpret_cast<f32x4*>(red + ((tile - t0) * KW + ksub) * 256 + lane * 4) = total;
             }
             total = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
 
-    // Steady state: the loop body's prefetches are unconditional, so the loads
-    // stay straight-line code (a load under a branch makes the compiler wait
-    // for every outstanding load before using the current item, which drains
-    // the pipeline); the scheduling barriers keep each prefetch issued ahead of
-    // the wait for the item being computed.  The last one or two items are
-    // peeled off, so nothing is fetched twice.
+    // Steady state with straight-line prefetches and pinned issue order; the
+    // last one or two items are peeled so nothing is fetched twice.
     int it = 0;
     for (; it + 2 < nitems; it += 2) {
         load_item(it + 1, 1);
@@ -424,7 +442,56 @@ __global__ __launch_bounds__(ST_NWAVE * 64) void w4a16_stream_kernel(
     } else if (it < nitems) {
         compute_item(it, 0);
     }
-    (void)TPW;
+    if (direct) return;
+
+    // ---- reduction over the KW sub-ranges (LDS), then over the S slices
+    const int T = t1 - t0;
+    if (KW > 1) __syncthreads();
+    for (int e = tid; KW > 1 && e < T * 256; e += DK_NWAVE * 64) {
+        const int tl = e >> 8;
+        const int r = e & 255;                   // lane * 4 + i of the tile's MFMA layout
+        float v = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) v += red[(tl * KW + k) * 256 + r];
+        if (S == 1) {
+            const int m = 4 * ((r >> 2) >> 4) + (r & 3);
+            const int n = (t0 + tl) * 16 + ((r >> 2) & 15);
+            if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+        } else {
+            __hip_atomic_store(&part[((size_t)split * NT + t0 + tl) * 256 + r], v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (S == 1) return;
+    // every thread's slot stores are complete before the counter moves
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0)
+        last_flag = (__hip_atomic_fetch_add(&cnt[strip], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1));
+    __syncthreads();
+    if (!last_flag) return;
+    for (int e = tid; e < T * 256; e += DK_NWAVE * 64) {
+        const int tl = e >> 8;
+        const int r = e & 255;
+        const float* src = part + ((size_t)t0 + tl) * 256 + r;
+        float v = 0.0f;
+        for (int k0 = 0; k0 < S; k0 += 8) {      // 8 independent loads in flight, then add in order
+            float pv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                pv[k] = k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * NT * 256,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v += pv[k];
+        }
+        const int m = 4 * ((r >> 2) >> 4) + (r & 3);
+        const int n = (t0 + tl) * 16 + ((r >> 2) & 15);
+        if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+    }
+    if (tid == 0)                                // leave the counter zero for the next call
+        __hip_atomic_store(&cnt[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -607,11 +674,6 @@ __global__ __launch_bounds__(256) void w4a16_large_m_kernel(
 // ---------------------------------------------------------------------------
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-size_t w4a16_workspace_bytes(int M, int N, int K) {
-    (void)N;
-    if (M <= 64) return 0;
-    return (size_t)(K / 128) * (size_t)round_up(M, LM_BM) * sizeof(float);
-}
 
 // Tuning knobs of the small-M dispatch (compile-time; defaults measured on MI355X).
 #ifndef QG_SM_NWAVE
@@ -649,51 +711,119 @@ static void launch_small_ct(const uint16_t* a, const uint32_t* wq, const uint16_
         launch_small<MT, 1>(a, wq, sc, y, M, N, K, s);
 }
 
-#ifndef QG_ST_MIN_TILES_PER_CU   // use the LDS-staged streaming kernel from this many tiles per CU
-#define QG_ST_MIN_TILES_PER_CU 2
+// ---- decode-kernel configuration (M <= 16), a function of the shape only ----
+#ifndef QG_DK_TARGET_CUS          // workgroups the narrow split aims to fill
+#define QG_DK_TARGET_CUS 256
 #endif
-#ifndef QG_ST_LDS_BUDGET
-#define QG_ST_LDS_BUDGET (144 * 1024)
+#ifndef QG_DK_WIDE_TILES          // one K-slice from this many column tiles
+#define QG_DK_WIDE_TILES 512
 #endif
+#ifndef QG_DK_TILES_PER_STRIP     // column tiles per workgroup for narrow outputs
+#define QG_DK_TILES_PER_STRIP 8
+#endif
+#ifndef QG_DK_LDS_BUDGET
+#define QG_DK_LDS_BUDGET (144 * 1024)
+#endif
+#ifndef QG_DK_SPLIT_MIN_GROUPS   // K splits across workgroups only for K >= 128 * this ...
+#define QG_DK_SPLIT_MIN_GROUPS 64
+#endif
+#ifndef QG_DK_SPLIT_MIN_M        // ... and M above this (measured: below, the in-workgroup
+#define QG_DK_SPLIT_MIN_M 4      // split-K kernel is faster; the slot reduction costs a few us)
+#endif
+
+struct DecodeCfg {
+    int S, NS, KW, U;
+    size_t lds;
+    bool ok;
+};
+
+static int largest_u(int ng) {
+    for (int u : {8, 4, 2, 1})
+        if (ng % u == 0) return u;
+    return 1;
+}
+
+static size_t decode_lds(int M, int Gs, int tmax, int KW, bool direct) {
+    return (size_t)M * (Gs * 256 + 16) + (size_t)Gs * 16 * sizeof(float) +
+           (direct ? 0 : (size_t)tmax * KW * 256 * sizeof(float));
+}
+
+static DecodeCfg decode_cfg(int M, int N, int K) {
+    DecodeCfg c{1, 1, 1, 1, 0, false};
+    if (M > 16) return c;
+    const int NT = N / 16;
+    const int G = K / 128;
+    if (NT >= QG_DK_WIDE_TILES) {                       // wide: whole K per workgroup
+        const size_t lds = decode_lds(M, G, 0, 1, true);
+        if (lds <= QG_DK_LDS_BUDGET) {
+            c.S = 1; c.KW = 1; c.U = largest_u(G); c.lds = lds; c.ok = true;
+            c.NS = 0;                                   // set from the device at launch
+            return c;
+        }
+    }
+    if (G < QG_DK_SPLIT_MIN_GROUPS || M <= QG_DK_SPLIT_MIN_M) return c;
+    const int NS = NT / QG_DK_TILES_PER_STRIP > 0 ? NT / QG_DK_TILES_PER_STRIP : 1;
+    const int tmax = (NT + NS - 1) / NS;
+    for (int S = 1; S <= G; ++S) {                      // smallest K split that fills the GPU
+        if (G % S) continue;
+        const size_t lds = decode_lds(M, G / S, tmax, 1, S == 1);
+        if (lds > QG_DK_LDS_BUDGET) continue;
+        if ((long long)NS * S < QG_DK_TARGET_CUS && S < G) continue;
+        c.S = S; c.NS = NS; c.KW = 1; c.U = largest_u(G / S); c.lds = lds; c.ok = true;
+        return c;
+    }
+    return c;
+}
+
+static size_t decode_ws_bytes(const DecodeCfg& c, int N) {
+    if (!c.ok || c.S == 1) return 0;
+    const size_t part = (size_t)c.S * (N / 16) * 256 * sizeof(float);
+    return part + (size_t)c.NS * sizeof(unsigned);
+}
 
 static int device_cu_count() {
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipGetDevice(&dev) != hipSuccess) return QG_DK_TARGET_CUS;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
+        return QG_DK_TARGET_CUS;
     return cus;
 }
 
-static size_t stream_lds_bytes(int M, int K) {
-    return (size_t)M * (2 * (size_t)K + 16) + (size_t)(K / 128) * 16 * sizeof(float);
-}
-
-static bool use_stream_kernel(int M, int N, int K, int cus) {
-    const int NT = N / 16;
-    return M <= 16 && (K / 128) % ST_U == 0 && stream_lds_bytes(M, K) <= QG_ST_LDS_BUDGET &&
-           NT >= QG_ST_MIN_TILES_PER_CU * cus;
-}
-
-static void launch_stream(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
-                          int M, int N, int K, int cus, hipStream_t s) {
-    const size_t lds = stream_lds_bytes(M, K);
-    static bool attr_set = false;
+template <int KW, int U>
+static void launch_decode_t(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
+                            int M, int N, int K, const DecodeCfg& c, int NS, void* ws,
+                            hipStream_t s) {
+    static bool attr_set = false;   // allow up to the LDS budget (the default limit is 64 KiB)
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_stream_kernel<1>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, QG_ST_LDS_BUDGET);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_decode_kernel<KW, U>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, QG_DK_LDS_BUDGET);
         attr_set = true;
     }
-    const int per_cu = lds * 2 <= 160 * 1024 ? 2 : 1;
-    const int NT = N / 16;
-    const int grid = min(NT, cus * per_cu);
-    hipLaunchKernelGGL(w4a16_stream_kernel<1>, dim3(grid), dim3(ST_NWAVE * 64), lds, s, a, wq, sc,
-                       y, M, N, K);
+    float* part = static_cast<float*>(ws);
+    unsigned* cnt = ws ? reinterpret_cast<unsigned*>(part + (size_t)c.S * (N / 16) * 256) : nullptr;
+    hipLaunchKernelGGL((w4a16_decode_kernel<KW, U>), dim3(c.S * NS), dim3(DK_NWAVE * 64), c.lds, s,
+                       a, wq, sc, y, M, N, K, c.S, NS, part, cnt);
+}
+
+static void launch_decode(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
+                          int M, int N, int K, const DecodeCfg& c, void* ws, hipStream_t s) {
+    int NS = c.NS;
+    if (NS == 0) {                                      // wide: size the grid to the device
+        static const int cus = device_cu_count();
+        const int per_cu = c.lds * 2 <= 160 * 1024 ? 2 : 1;
+        NS = min(N / 16, cus * per_cu);
+    }
+    switch (c.U) {
+        case 8: launch_decode_t<1, 8>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        case 4: launch_decode_t<1, 4>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        case 2: launch_decode_t<1, 2>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        default: launch_decode_t<1, 1>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+    }
 }
 
 const char* w4a16_kernel_for(int M, int N, int K) {
-    static const int cus = device_cu_count();
     if (M == 0) return "none";
-    if (use_stream_kernel(M, N, K, cus)) return "w4a16_stream_kernel";
+    if (decode_cfg(M, N, K).ok) return "w4a16_decode_kernel";
     if (M <= 64) {
         const int NT = N / 16;
         const int ct = (NT % 4 == 0 && NT >= QG_SM_CT4_MIN_TILES) ? 4
@@ -707,11 +837,17 @@ const char* w4a16_kernel_for(int M, int N, int K) {
     return "w4a16_large_m_kernel";
 }
 
+size_t w4a16_workspace_bytes(int M, int N, int K) {
+    if (M <= 16) return decode_ws_bytes(decode_cfg(M, N, K), N);
+    if (M <= 64) return 0;
+    return (size_t)(K / 128) * (size_t)round_up(M, LM_BM) * sizeof(float);
+}
+
 void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
                         uint16_t* y, int M, int N, int K, void* ws, hipStream_t s) {
-    static const int cus = device_cu_count();
-    if (use_stream_kernel(M, N, K, cus)) {
-        launch_stream(a, packed, scales, y, M, N, K, cus, s);
+    const DecodeCfg dc = decode_cfg(M, N, K);
+    if (dc.ok) {
+        launch_decode(a, packed, scales, y, M, N, K, dc, ws, s);
     } else if (M <= 16) {
         launch_small_ct<1>(a, packed, scales, y, M, N, K, s);
     } else if (M <= 32) {

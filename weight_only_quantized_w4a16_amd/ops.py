@@ -193,7 +193,8 @@ class W4A16Linear:
     def workspace(self, M):
         need = w4a16_workspace_bytes(M, self.w.N, self.w.K)
         if need and (self._ws is None or self._ws.numel() < need):
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.w.packed.device)
+            # zero-filled once; every call resets the counters it uses
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.w.packed.device)
         return (self._ws, need) if need else (None, 0)
 
     def __call__(self, a, out=None, stream=None):

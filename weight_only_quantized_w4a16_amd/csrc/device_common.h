@@ -60,6 +60,12 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 128-bit direct-to-LDS load: lane l's 16 bytes from src land at lds_base + 16 * l
+// (lds_base must be the same in every lane of the wave).
+__device__ __forceinline__ void load_lds_b128(const u32x4* src, u32x4* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
 __device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {
     i32x8 r;
     r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;

@@ -524,44 +524,74 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
-// Large M (M > 64): 128 x 128 output tile per workgroup, 4 waves in a 2 x 2
-// grid of 64 x 64.  The activation tile of one group (128 rows x 128 k) is
-// staged in LDS, double buffered, with a 16-byte XOR swizzle (chunk c of row r
-// stored at c ^ (r % 16)) so the fragment reads are conflict free.  Each wave
-// loads its four weight tiles straight into registers (they are already in
-// fragment order), unpacks them once per group and reuses them over its four
-// m-tiles.  Every (m-tile, n-tile) group sum starts at the precomputed offset
-// term and is scaled into the total.
+// Large M (M > 64): BM x 128 output tile per workgroup (BM = 128; 256 is
+// available), four waves in a 2 x 2 grid of (BM/2) x 64.  Per group (128 rows of K):
+//   * the activation tile a[m0 : m0+BM, 128g : 128g+128] is copied straight
+//     into LDS with 128-bit direct-to-LDS loads (no VGPR staging), double
+//     buffered; lane l of a load writes LDS slot l, so each lane fetches the
+//     global chunk that the 16-byte XOR swizzle (chunk c of row r stored at
+//     c ^ (r % 16)) puts in its slot, and fragment reads are conflict free;
+//   * each wave loads its four weight tiles straight into registers (they are
+//     already in fragment order), unpacks them once, and for every m-subtile
+//     reads its A fragment from LDS once and runs the four n-tiles against it;
+//   * every (m-subtile, n-tile) group sum starts from the precomputed offset
+//     term -136 * sum(a) and is scaled into the total by the group scale.
+// The next group's activation, weight, scale and offset loads are in flight
+// while the current group computes.
+//
+// Tile order: the grid is 1-D and workgroups are dealt round-robin to the 8
+// XCDs (each with its own L2).  Workgroup id is remapped so that each XCD
+// receives a contiguous run of tiles, M fastest: the M-tiles that read the same
+// weight tile run on one XCD at about the same time and share it through that
+// XCD's L2 instead of fetching it once per XCD.
 // ---------------------------------------------------------------------------
-constexpr int LM_BM = 128;
-constexpr int LM_BN = 128;
+constexpr int NUM_XCD = 8;
 
+__device__ __forceinline__ int xcd_tile(int id, int total) {
+    const int per = total / NUM_XCD;
+    return id < per * NUM_XCD ? (id % NUM_XCD) * per + id / NUM_XCD : id;
+}
+
+template <int BM>
 __global__ __launch_bounds__(256) void w4a16_large_m_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
     int M, int Mp, int N, int K) {
-    __shared__ u32x4 As[2][LM_BM][16];   // 2 x 32 KiB
+    constexpr int MI = BM / 32;                  // m-subtiles per wave
+    constexpr int ROWS_PER_WAVE_LOAD = BM / 4;   // activation rows each wave copies
+    extern __shared__ __attribute__((aligned(16))) u32x4 As[];   // [2][BM][16]
 
     const int G = K >> 7;
     const int NT = N >> 4;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1;
     const int wn = wave & 1;
     const int col = lane & 15;
     const int kq = lane >> 4;
-    const int m0 = blockIdx.y * LM_BM;
-    const int n0 = blockIdx.x * LM_BN;
+    const int mb = (M + BM - 1) / BM;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int m0 = (tile % mb) * BM;
+    const int n0 = (tile / mb) * 128;
 
-    // activation tile loader: thread -> row lr, chunks 8*lh .. 8*lh+7
-    const int lr = tid >> 1;
-    const int lh = tid & 1;
-    const bool lrow_ok = (m0 + lr) < M;
-    const u32x4* asrc =
-        reinterpret_cast<const u32x4*>(a + (size_t)(lrow_ok ? m0 + lr : 0) * K) + lh * 8;
+    // activation copy: instruction i of wave w fills rows w*BM/4 + 4i + lane/16, slot lane%16
+    const u32x4* aload[BM / 16];
+    int lds_off[BM / 16];
+#pragma unroll
+    for (int i = 0; i < BM / 16; ++i) {
+        const int r = wave * ROWS_PER_WAVE_LOAD + 4 * i + (lane >> 4);
+        const int chunk = (lane & 15) ^ (r & 15);
+        const int grow = min(m0 + r, M - 1);     // rows >= M are never stored
+        aload[i] = reinterpret_cast<const u32x4*>(a + (size_t)grow * K) + chunk;
+        lds_off[i] = (wave * ROWS_PER_WAVE_LOAD + 4 * i) * 16;   // u32x4 units, wave-uniform
+    }
+    auto load_a = [&](int g, int buf) {
+#pragma unroll
+        for (int i = 0; i < BM / 16; ++i)
+            load_lds_b128(aload[i] + (size_t)g * 16, As + buf * BM * 16 + lds_off[i]);
+    };
 
-    // weight tiles of this wave
     const u32x4* wsrc[4];
     const uint16_t* ssrc[4];
     bool tok[4];
@@ -569,100 +599,93 @@ __global__ __launch_bounds__(256) void w4a16_large_m_kernel(
     for (int ni = 0; ni < 4; ++ni) {
         const int nt = (n0 >> 4) + wn * 4 + ni;
         tok[ni] = nt < NT;
-        const size_t ntc = tok[ni] ? nt : 0;
+        const size_t ntc = tok[ni] ? nt : NT - 1;
         wsrc[ni] = reinterpret_cast<const u32x4*>(wq) + ntc * G * 64 + lane;
         ssrc[ni] = sc + ntc * G * 16 + col;
     }
-    // offset-term rows of this wave: m0 + wm*64 + mi*16 + 4*kq + (0..3)
-    const float* csrc = corr + m0 + wm * 64 + 4 * kq;
+    const float* csrc = corr + m0 + wm * (BM / 2) + 4 * kq;
 
-    f32x4 total[4][4];
+    f32x4 total[MI][4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 areg[8];
-    u32x4 wreg[4];
-    uint32_t sreg[4];
-
-    auto load_a = [&](int g) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            areg[i] = lrow_ok ? asrc[(size_t)g * 16 + i] : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) As[buf][lr][(lh * 8 + i) ^ (lr & 15)] = areg[i];
-    };
-    auto load_w = [&](int g) {
+    u32x4 wnext[4];
+    uint32_t snext[4];
+    f32x4 cnext[MI];
+    auto load_rest = [&](int g) {
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-            wreg[ni] = tok[ni] ? wsrc[ni][(size_t)g * 64] : u32x4{0u, 0u, 0u, 0u};
-            sreg[ni] = tok[ni] ? ssrc[ni][(size_t)g * 16] : 0u;
+            wnext[ni] = __builtin_nontemporal_load(wsrc[ni] + (size_t)g * 64);
+            snext[ni] = ssrc[ni][(size_t)g * 16];
         }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            cnext[mi] = *reinterpret_cast<const f32x4*>(csrc + (size_t)g * Mp + mi * 16);
     };
 
-    load_a(0);
-    load_w(0);
-    store_a(0);
+    const Int4Unpacker unpack;
+    load_a(0, 0);
+    load_rest(0);
+    __builtin_amdgcn_s_waitcnt(0);               // vmcnt(0) lgkmcnt(0) expcnt(0)
     __syncthreads();
 
     for (int g = 0; g < G; ++g) {
         const int buf = g & 1;
         u32x4 wcur[4];
         float scur[4];
+        f32x4 ccur[MI];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-            wcur[ni] = wreg[ni];
-            scur[ni] = bf16_to_f32(sreg[ni]);
+            wcur[ni] = wnext[ni];
+            scur[ni] = bf16_to_f32(snext[ni]);
         }
-        f32x4 cr[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-            cr[mi] = *reinterpret_cast<const f32x4*>(csrc + (size_t)g * Mp + mi * 16);
+        for (int mi = 0; mi < MI; ++mi) ccur[mi] = cnext[mi];
         if (g + 1 < G) {
-            load_a(g + 1);
-            load_w(g + 1);
+            load_a(g + 1, buf ^ 1);
+            load_rest(g + 1);
         }
-        bf16x8 af[4][4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int r = wm * 64 + mi * 16 + col;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) af[mi][t] = as_bf16x8(As[buf][r][(4 * t + kq) ^ col]);
-        }
+        bf16x8 bfr[4][4];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-            bf16x8 bfr[4];
-            bfr[0] = int4_word_biased_bf16x8(wcur[ni].x);
-            bfr[1] = int4_word_biased_bf16x8(wcur[ni].y);
-            bfr[2] = int4_word_biased_bf16x8(wcur[ni].z);
-            bfr[3] = int4_word_biased_bf16x8(wcur[ni].w);
+            bfr[ni][0] = unpack(wcur[ni].x);
+            bfr[ni][1] = unpack(wcur[ni].y);
+            bfr[ni][2] = unpack(wcur[ni].z);
+            bfr[ni][3] = unpack(wcur[ni].w);
+        }
+        const u32x4* Ab = As + buf * BM * 16;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                f32x4 acc = cr[mi];
+        for (int mi = 0; mi < MI; ++mi) {
+            const int r = wm * (BM / 2) + mi * 16 + col;
+            bf16x8 af[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc = mfma_bf16_16x16x32(af[mi][t], bfr[t], acc);
+            for (int t = 0; t < 4; ++t) af[t] = as_bf16x8(Ab[r * 16 + ((4 * t + kq) ^ col)]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                f32x4 acc = ccur[mi];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc = mfma_bf16_16x16x32(af[t], bfr[ni][t], acc);
                 total[mi][ni][0] = fmaf(scur[ni], acc[0], total[mi][ni][0]);
                 total[mi][ni][1] = fmaf(scur[ni], acc[1], total[mi][ni][1]);
                 total[mi][ni][2] = fmaf(scur[ni], acc[2], total[mi][ni][2]);
                 total[mi][ni][3] = fmaf(scur[ni], acc[3], total[mi][ni][3]);
             }
         }
-        if (g + 1 < G) store_a(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);           // next group's copies have landed
         __syncthreads();
     }
 
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
             if (!tok[ni]) continue;
             const int n = n0 + wn * 64 + ni * 16 + col;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 64 + mi * 16 + 4 * kq + i;
+                const int m = m0 + wm * (BM / 2) + mi * 16 + 4 * kq + i;
                 if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i]);
             }
         }
@@ -837,10 +860,30 @@ const char* w4a16_kernel_for(int M, int N, int K) {
     return "w4a16_large_m_kernel";
 }
 
+constexpr int LM_MAX_BM = 256;
+#ifndef QG_LM_BM256_MIN_TILES     // 256-row tiles when they give at least this many workgroups;
+#define QG_LM_BM256_MIN_TILES (1 << 30)   // measured slower than 128-row tiles on every
+#endif                                    // stack shape (one workgroup per CU), so off
+
+template <int BM>
+static void launch_large(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, const float* corr,
+                         uint16_t* y, int M, int Mp, int N, int K, hipStream_t s) {
+    static bool attr_set = false;
+    const size_t lds = (size_t)2 * BM * 16 * sizeof(u32x4);
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_large_m_kernel<BM>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        attr_set = true;
+    }
+    const int tiles = ((N + 127) / 128) * ((M + BM - 1) / BM);
+    hipLaunchKernelGGL((w4a16_large_m_kernel<BM>), dim3(tiles), dim3(256), lds, s, a, wq, sc, corr, y,
+                       M, Mp, N, K);
+}
+
 size_t w4a16_workspace_bytes(int M, int N, int K) {
     if (M <= 16) return decode_ws_bytes(decode_cfg(M, N, K), N);
     if (M <= 64) return 0;
-    return (size_t)(K / 128) * (size_t)round_up(M, LM_BM) * sizeof(float);
+    return (size_t)(K / 128) * (size_t)round_up(M, LM_MAX_BM) * sizeof(float);
 }
 
 void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
@@ -855,15 +898,17 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
     } else if (M <= 64) {
         launch_small_ct<4>(a, packed, scales, y, M, N, K, s);
     } else {
-        const int Mp = round_up(M, LM_BM);
+        const int Mp = round_up(M, LM_MAX_BM);
         const int G = K / 128;
         float* corr = static_cast<float*>(ws);
         const size_t n = (size_t)G * Mp;
         hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
                            0, s, a, M, Mp, K, corr);
-        dim3 grid((N + LM_BN - 1) / LM_BN, Mp / LM_BM);
-        hipLaunchKernelGGL(w4a16_large_m_kernel, grid, dim3(256), 0, s, a, packed, scales, corr, y,
-                           M, Mp, N, K);
+        const int nb = (N + 127) / 128;
+        if ((long long)((M + 255) / 256) * nb >= QG_LM_BM256_MIN_TILES)
+            launch_large<256>(a, packed, scales, corr, y, M, Mp, N, K, s);
+        else
+            launch_large<128>(a, packed, scales, corr, y, M, Mp, N, K, s);
     }
 }
 

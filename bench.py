@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--batch", type=int, default=16)
     p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "70b"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-chain", action="store_true",
+                   help="decode workload: skip the chained-launch timing")
     p.add_argument("--only-batch", action="store_true",
                    help="decode workload: time only --batch (short profiled runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -346,29 +348,63 @@ def main():
         run_70b(args, torch, ops, synth)
 
 
+def make_chain(ops, stack, B):
+    """All GEMMs of the step in one chained launch; every GEMM is declared to read
+    the previous GEMM's output (the dependency of a real decode step)."""
+    items = [(r["a"][:B], r["w"], r["y"][:B], True) for r in stack.layers]
+    return ops.W4A16Chain(items, B)
+
+
+def time_launches(torch, fn, steps, warmup):
+    """`warmup` untimed calls, then exactly `steps` calls bracketed by HIP events on
+    the launch stream; returns ms per call."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def run_decode(args, torch, ops, synth):
     batches = [args.batch] if args.only_batch else sorted({1, 2, 4, 8, 16, args.batch})
     stack = Stack(ops, synth, torch, "8b", batches)
     print(f"[bench] packed {len(stack.layers)} GEMMs, {stack.bytes(0) / 1e9:.3f} GB of weights+scales",
           file=sys.stderr, flush=True)
     by_batch = {}
+    chains = {}
     for B in batches:
-        g = graph_of(torch, lambda: stack.step(B))
-        ms = time_graph(torch, g, args.steps, args.warmup)
         nbytes = stack.bytes(B)
-        by_batch[str(B)] = {"ms_per_step": round(ms, 4), "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3),
-                            "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
-        print(f"[bench] B={B}: {ms:.4f} ms/step, {by_batch[str(B)]['TB_s']} TB/s",
-              file=sys.stderr, flush=True)
+        rec = {}
+        if not args.no_chain:
+            chains[B] = make_chain(ops, stack, B)
+            ms_c = time_launches(torch, chains[B], args.steps, args.warmup)
+            assert chains[B].error_word() == 0, "chained launch: a dependency wait timed out"
+            rec["chain_ms"] = round(ms_c, 4)
+        g = graph_of(torch, lambda: stack.step(B))
+        ms_g = time_graph(torch, g, args.steps, args.warmup)
         del g
+        rec["graph_ms"] = round(ms_g, 4)
+        ms = ms_g
+        rec.update({"ms_per_step": ms, "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3),
+                    "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)})
+        by_batch[str(B)] = rec
+        print(f"[bench] B={B}: {rec}", file=sys.stderr, flush=True)
     B = args.batch
     ms = by_batch[str(B)]["ms_per_step"]
     nbytes = stack.bytes(B)
 
-    # dominant kernel: its launches alone, replayed as a graph; HIP events give the
-    # average launch duration on the stream the kernel runs on
+    # dominant kernel and its average launch duration, measured with HIP events
+    # on the stream it runs on
     dom = lambda r: dominant_rule(ops, B, r["K"], r["N"])
     launches = sum(1 for r in stack.layers if dom(r))
+    kernel = f"{DOMINANT_KERNEL} ({launches} launches per step)"
     g = graph_of(torch, lambda: stack.step(B, only=dom))
     dom_ms = time_graph(torch, g, args.steps, args.warmup)
     del g
@@ -392,14 +428,16 @@ def run_decode(args, torch, ops, synth):
         "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)",
         "data": "synthetic: weights N(0, 0.02^2) bf16 RTN-quantized on the GPU, activations N(0,1) bf16",
         "config": {"workload": "Llama-3-8B decode linear stack, W4A16 g128, 129 GEMMs "
-                               "(32 x qkv/o/gate_up/down + LM head), one HIP graph per step",
+                               "(32 x qkv/o/gate_up/down + LM head) in stream order, one HIP graph "
+                               "per step (by_batch.chain_ms: the same step as one chained "
+                               "persistent launch, each GEMM waiting for the previous one)",
                    "batch": B, "streamed_params": synth.stack_params("8b"),
                    "algorithmic_bytes_per_step": nbytes, "parallelism": "single GPU"},
         "by_batch": by_batch,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": f"{DOMINANT_KERNEL} ({launches} launches per step)",
+                     "kernel": kernel,
                      "launches_per_step": launches,
                      "algorithmic_bytes_per_launch": round(dom_bytes_per_launch),
                      "avg_launch_us": round(dom_avg_us, 3)},

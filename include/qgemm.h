@@ -160,6 +160,52 @@ qg_status qgemm_w4a16(const uint16_t *a_bf16, const uint32_t *packed,
                       qg_stream stream);
 
 /*
+ * Chained decode -- the W4A16 GEMMs of one decode step (M <= 16) in a single
+ * persistent, cooperative launch: one workgroup per compute unit, all GEMMs in
+ * order, each GEMM's weight stream starting while the previous GEMM finishes.
+ * Same arithmetic as qgemm_w4a16 (decode path) for every GEMM.
+ * [P1 "The three regimes": at small B the step is the weight stream; P2 3.4
+ *  "Inference with W4A16".]
+ *
+ * Usage: describe the chain (qg_w4a16_chain_gemm, host memory), build a plan
+ * with qg_w4a16_chain_plan (host memory, qg_w4a16_chain_plan_bytes bytes),
+ * copy the plan byte for byte to device memory, then call qgemm_w4a16_chain
+ * with both copies as often as needed.  A plan is valid for the device that is
+ * current when it is made.
+ *
+ * after_previous != 0 declares that the GEMM reads memory the previous GEMM
+ * of the chain writes (e.g. its activations are the previous outputs): it then
+ * starts reading activations only after every workgroup has finished the
+ * previous GEMM.  Outputs are written and activations read with accesses that
+ * are coherent across the GPU, so such chains are exact.
+ *
+ * Plan errors: QG_ERR_SHAPE also when M > 16, count < 1, or a GEMM does not
+ * fit the chained kernel (run it with qgemm_w4a16 instead).
+ * Workspace: qg_w4a16_chain_workspace_bytes(count) bytes, zero-filled before
+ * first use; each call leaves it zero-filled except the error word (32-bit
+ * word 1), which becomes nonzero if a dependency wait exceeded its bound (the
+ * results of that call are then invalid; every wave still exits).  Calls that
+ * share a workspace must not overlap.  A launch that cannot keep every
+ * workgroup resident fails with QG_ERR_HIP instead of running.
+ */
+typedef struct {
+    const uint16_t *a_bf16;     /* [M, K] activations */
+    const uint32_t *packed;     /* native INT4 words (pack_int4_g128) */
+    const uint16_t *scales;     /* native bf16 scales */
+    uint16_t *y_bf16;           /* [M, N] outputs */
+    int32_t N, K;
+    int32_t after_previous;
+    int32_t reserved;           /* must be 0 */
+} qg_w4a16_chain_gemm;
+
+size_t qg_w4a16_chain_plan_bytes(int count);
+size_t qg_w4a16_chain_workspace_bytes(int count);
+qg_status qg_w4a16_chain_plan(const qg_w4a16_chain_gemm *gemms, int count, int M,
+                              void *plan, size_t plan_bytes);
+qg_status qgemm_w4a16_chain(const void *plan_host, const void *plan_device,
+                            void *workspace, size_t workspace_bytes, qg_stream stream);
+
+/*
  * quant_act_per_token -- dynamic per-token e4m3 quantization.
  * [P2 3.4 "W8A8-FP", activation quantization: Q(a_i) = s_i * rnd(a_i / s_i),
  *  s_i = max|a_i| / q_max, computed on the fly per row.]

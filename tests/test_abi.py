@@ -78,7 +78,7 @@ def test_size_queries(lib):
     assert lib.w4a16_workspace_bytes(4, 4096, 4096) == 0
     assert lib.w4a16_workspace_bytes(32, 4096, 4096) == 0          # M <= 64: in-workgroup split-K
     assert lib.w4a16_workspace_bytes(1024, 4096, 4096) == 32 * 1024 * 4
-    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == 32 * 128 * 4   # rows padded to 128
+    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == 32 * 256 * 4   # rows padded to 256
     assert lib.w8a8_workspace_bytes(1024, 4096, 4096) == 0
 
 
@@ -148,3 +148,10 @@ def test_binding_refuses_host_tensors(lib):
     a = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         lib.quantize_activations(a)
+
+
+def test_chain_queries(lib):
+    assert lib._lib.qg_w4a16_chain_plan_bytes(129) == 64 + 129 * 64
+    assert lib._lib.qg_w4a16_chain_workspace_bytes(129) == (129 + 2) * 4
+    assert lib._lib.qg_w4a16_chain_plan_bytes(0) == 0
+    assert ctypes.sizeof(lib.ChainGemm) == 48

@@ -294,3 +294,62 @@ def test_decode_workspace_counters_reset(ops, M, K, N):
         if first is None:
             first = y
         assert np.array_equal(y, first)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+def test_chain_dependent_gemms(ops, M):
+    """A chain whose every GEMM reads the previous GEMM's output: each stage is
+    checked against the oracle applied to the stage's actual input, so a stale
+    or partial read of the previous output fails the comparison."""
+    announce(f"qgemm_w4a16_chain dependent M={M}")
+    dims = [512, 1024, 4096, 2048, 14336, 256, 4096, 9600]
+    a0 = synth.activations(M, dims[0], seed=61 + M)
+    bufs = [dev_bf16(a0)] + [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in dims[1:]]
+    ws, qs = [], []
+    for i in range(len(dims) - 1):
+        w = synth.weights(dims[i], dims[i + 1], seed=71 + i)
+        qs.append(q4.quantize(w))
+        ws.append(_pack(ops, w))
+    chain = ops.W4A16Chain([(bufs[i], ws[i], bufs[i + 1], True) for i in range(len(ws))], M)
+    for rep in range(2):
+        for b in bufs[1:]:
+            b.fill_(float("nan"))
+        chain()
+        torch.cuda.synchronize()
+        assert chain.error_word() == 0
+        assert int(torch.count_nonzero(chain.ws[:4])) == 0 and int(torch.count_nonzero(chain.ws[8:])) == 0
+        for i in range(len(ws)):
+            x = host_bits16(bufs[i])
+            y = host_bits16(bufs[i + 1])
+            codes, s = qs[i]
+            assert_close_rms(y, q4.gemm_ref(x, codes, s), what=f"chain stage {i} M={M} rep={rep}")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_chain_matches_single_calls(ops, M):
+    """Independent GEMMs in one chain give the same bits as qgemm_w4a16 calls
+    through the decode path (same arithmetic, same reduction order) for the
+    wide shapes, and the oracle's result within tolerance for every shape."""
+    announce(f"qgemm_w4a16_chain vs single M={M}")
+    shapes = [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096), (4096, 128256)]
+    items, refs = [], []
+    for j, (K, N) in enumerate(shapes):
+        w = synth.weights(K, N, seed=81 + j)
+        a = synth.activations(M, K, seed=91 + j)
+        wt = _pack(ops, w)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        items.append((dev_bf16(a), wt, y, True))
+        cols = np.arange(N) if N <= 28672 else np.unique(np.random.default_rng(j).integers(0, N, 512))
+        codes, s = q4.quantize(w[:, cols])
+        refs.append((a, codes, s, cols))
+    chain = ops.W4A16Chain(items, M)
+    chain()
+    torch.cuda.synchronize()
+    assert chain.error_word() == 0
+    for (a, wt, y, _), (ah, codes, s, cols) in zip(items, refs):
+        got = host_bits16(y)
+        assert_close_rms(got[:, cols], q4.gemm_ref(ah, codes, s), what=f"chain N={wt.N} M={M}")
+        if wt.N >= 28672:          # wide: same decode kernel arithmetic as the single call
+            single = host_bits16(ops.W4A16Linear(wt)(a))
+            torch.cuda.synchronize()
+            assert np.array_equal(got, single)

@@ -25,6 +25,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
     return u >> 16;
 }
 
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
 // ---- INT4 unpack ------------------------------------------------------------
 // A native word holds eight 4-bit codes; nibble slots j and j+4 hold the rows
 // 2j and 2j+1 of the word's 8-row slice.  Masking both nibbles into the low
@@ -45,6 +47,26 @@ __device__ __forceinline__ bf16x8 int4_word_biased_bf16x8(uint32_t word) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// The unpack constants live in VGPRs: a VOP3 instruction reads at most one
+// scalar or literal operand here, and keeping both the nibble mask and the
+// bf16 magic in vector registers lets every pair compile to one v_and_or_b32
+// (3 shifts + 4 AND-ORs per 8 weights).
+struct Int4Unpacker {
+    uint32_t mask, magic;
+    __device__ __forceinline__ Int4Unpacker() {
+        asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(mask));
+        asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
+    }
+    __device__ __forceinline__ bf16x8 operator()(uint32_t w) const {
+        u32x4 v;
+        v.x = (w & mask) | magic;
+        v.y = ((w >> 4) & mask) | magic;
+        v.z = ((w >> 8) & mask) | magic;
+        v.w = ((w >> 12) & mask) | magic;
+        return as_bf16x8(v);
+    }
+};
+
 // ---- MFMA wrappers ------------------------------------------------------------
 // 16x16x32 bf16, fp32 accumulate.  A: lane l holds row l%16, 8 consecutive k of
 // the 32-wide step; B: lane l holds column l%16, the same 8 k.  D: lane l holds
@@ -58,7 +80,6 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // 128-bit direct-to-LDS load: lane l's 16 bytes from src land at lds_base + 16 * l
 // (lds_base must be the same in every lane of the wave).

@@ -18,6 +18,32 @@ const char* w4a16_kernel_for(int M, int N, int K);
 void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
                         uint16_t* y, int M, int N, int K, void* ws, hipStream_t s);
 
+// Chained decode (chain.hip)
+struct ChainDesc {          // one GEMM of a chain as the kernel reads it (64 bytes)
+    const uint16_t* a;
+    const uint32_t* wq;
+    const uint16_t* sc;
+    uint16_t* y;
+    int N, K;
+    int units;              // column strips (one per workgroup)
+    int kw;                 // waves per column tile (K split inside the workgroup)
+    int u;                  // groups per pipelined item
+    int nchunks;            // K processed in this many LDS-sized chunks
+    int after_prev;         // wait for the previous GEMM to complete
+    int pad;
+};
+struct ChainHeader {        // first 64 bytes of a plan
+    uint32_t magic;
+    int32_t count, M, grid;
+    uint64_t lds;
+    uint64_t reserved[5];
+};
+constexpr uint32_t kChainMagic = 0x51474331u;   // "QGC1"
+int chain_grid();
+bool chain_plan_one(int M, int N, int K, int P, ChainDesc* d, size_t* lds);
+hipError_t launch_chain(const ChainDesc* plan, int count, int M, size_t lds, unsigned* ws,
+                        hipStream_t s);
+
 // W8A8-FP8 path (fp8.hip)
 void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, float* s,
                                 hipStream_t st);

@@ -140,21 +140,6 @@ void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, in
 // bf16 magic in vector registers lets every pair compile to one v_and_or_b32
 // (3 shifts + 4 AND-ORs per 8 weights).
 // ---------------------------------------------------------------------------
-struct Int4Unpacker {
-    uint32_t mask, magic;
-    __device__ __forceinline__ Int4Unpacker() {
-        asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(mask));
-        asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
-    }
-    __device__ __forceinline__ bf16x8 operator()(uint32_t w) const {
-        u32x4 v;
-        v.x = (w & mask) | magic;
-        v.y = ((w >> 4) & mask) | magic;
-        v.z = ((w >> 8) & mask) | magic;
-        v.w = ((w >> 12) & mask) | magic;
-        return as_bf16x8(v);
-    }
-};
 
 template <int MT, int CT, int NWAVE, int U>
 __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(

@@ -58,7 +58,10 @@ def test_status_strings_and_version(lib):
 def test_kernel_selection_query(lib):
     assert lib.w4a16_kernel_for(1, 28672, 4096) == "w4a16_decode_kernel"
     assert lib.w4a16_kernel_for(16, 4096, 14336) == "w4a16_decode_kernel"
+    # narrow outputs whose activation slice fits in LDS: in-workgroup split-K
     assert lib.w4a16_kernel_for(4, 4096, 14336).startswith("w4a16_small_m_kernel<1")
+    assert lib.w4a16_kernel_for(1, 16, 128).startswith("w4a16_small_m_kernel<1")
+    assert lib.w4a16_kernel_for(17, 4096, 4096).startswith("w4a16_small_m_kernel<2")
     assert lib.w4a16_kernel_for(32, 4096, 4096).startswith("w4a16_small_m_kernel<2")
     assert lib.w4a16_kernel_for(512, 4096, 4096) == "w4a16_large_m_kernel"
     assert lib.w4a16_kernel_for(4, 4096, 4000) == ""                 # invalid shape

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace qg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -85,6 +88,64 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
 // (lds_base must be the same in every lane of the wave).
 __device__ __forceinline__ void load_lds_b128(const u32x4* src, u32x4* lds_base) {
     __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+// ---- compile-time loops ----------------------------------------------------------
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(ic<I>{}), ...);
+}
+// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N-1>{}) in order
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---- buffer-resource loads ----------------------------------------------------------
+// A raw buffer resource over [base, base + bytes).  A load whose offset lies at
+// or past `bytes` returns zero and makes no memory access, so `bytes = 0` turns
+// a request into a no-op without a branch (dword 3 is the gfx9-family format
+// word for untyped buffer access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// 16 bytes at byte offset `off`, streaming (non-temporal) hint
+__device__ __forceinline__ u32x4 buffer_load_b128_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+__device__ __forceinline__ uint32_t buffer_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// ---- register ring pipeline ------------------------------------------------------------
+// n items through D register buffers: item i lives in buffer i % D and is
+// requested D - 1 items before it is consumed.  load(slot) requests the next
+// item in order (the caller keeps that cursor and issues an empty request past
+// the last item, see make_rsrc), so every request is unconditional and the
+// compiler's memory-counter waits stay exact; compute(slot) consumes the next
+// item.  The scheduling barriers keep each request ahead of the compute that
+// follows it.
+template <int D, typename Load, typename Compute>
+__device__ __forceinline__ void ring_pipeline(int n, Load&& load, Compute&& compute) {
+    for (int it = 0; it < n; it += D) {
+        static_for<D>([&](auto s) {
+            load(ic<(decltype(s)::value + D - 1) % D>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + decltype(s)::value < n) compute(s);
+        });
+    }
+}
+// the first D - 1 requests of ring_pipeline, issued ahead of other work
+template <int D, typename Load>
+__device__ __forceinline__ void ring_prologue(Load&& load) {
+    static_for<D - 1>([&](auto s) {
+        load(s);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 __device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {

@@ -141,7 +141,7 @@ void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, in
 // (3 shifts + 4 AND-ORs per 8 weights).
 // ---------------------------------------------------------------------------
 
-template <int MT, int CT, int NWAVE, int U>
+template <int MT, int CT, int NWAVE, int U, bool PIPE>
 __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K) {
@@ -153,6 +153,7 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
     const int nt0 = blockIdx.x * CT;
     const int g_begin = (G * wave) / NWAVE;
     const int ng = (G * (wave + 1)) / NWAVE - g_begin;
+    const int nitems = (ng + U - 1) / U;          // the last item may be partial
     const Int4Unpacker unpack;
 
     f32x4 total[CT][MT];
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
     negc_u.x = negc_u.y = negc_u.z = negc_u.w = 0xC308C308u;     // bf16 -136 everywhere
     const bf16x8 negc = as_bf16x8(negc_u);
 
-    // per-wave base pointers; the chunk loop adds immediate offsets
+    // per-wave base pointers; items add immediate offsets
     const u32x4* arow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -181,56 +182,93 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
         sp[ct] = sc + tile * 16 + col;
     }
 
-    for (int g0 = 0; g0 < ng; g0 += U) {
-        u32x4 wv[U][CT];
-        uint32_t sv[U][CT];
-        u32x4 av[U][MT][4];
+    // Item i (U groups) lives in buffer i & 1: no register copies, so a pending
+    // load is never waited for early; the next item is always in flight while
+    // the current one computes.  Groups past the wave's range (a partial last
+    // item) reload the wave's last group and are skipped in the math.
+    struct Buf {
+        u32x4 w[U][CT];
+        uint32_t s[U][CT];
+        u32x4 a[U][MT][4];
+    };
+    Buf b0;
+    [[maybe_unused]] Buf b1;
+    auto load_item = [&](int it, Buf& b) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (g0 + u < ng) {
+            const int g = min(it * U + u, ng - 1);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    wv[u][ct] = __builtin_nontemporal_load(wp[ct] + (g0 + u) * 64);
-                    sv[u][ct] = sp[ct][(g0 + u) * 16];
-                }
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) av[u][mt][t] = arow[mt][(g0 + u) * 16 + 4 * t];
+            for (int ct = 0; ct < CT; ++ct) {
+                b.w[u][ct] = __builtin_nontemporal_load(wp[ct] + g * 64);
+                b.s[u][ct] = sp[ct][g * 16];
             }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) b.a[u][mt][t] = arow[mt][g * 16 + 4 * t];
         }
+    };
+    // nvalid: groups of the item inside the wave's range (U except at the end)
+    auto compute_item = [&](int nvalid, const Buf& b) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (g0 + u < ng) {
-                f32x4 corr[MT];
+            if (u >= nvalid) break;               // uniform
+            f32x4 corr[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                corr[mt] = mfma_bf16_16x16x32(as_bf16x8(b.a[u][mt][0]), negc, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int t = 1; t < 4; ++t)
+                    corr[mt] = mfma_bf16_16x16x32(as_bf16x8(b.a[u][mt][t]), negc, corr[mt]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const float s = bf16_to_f32(b.s[u][ct]);
+                bf16x8 bfr[4];
+                bfr[0] = unpack(b.w[u][ct].x);
+                bfr[1] = unpack(b.w[u][ct].y);
+                bfr[2] = unpack(b.w[u][ct].z);
+                bfr[3] = unpack(b.w[u][ct].w);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    corr[mt] = mfma_bf16_16x16x32(as_bf16x8(av[u][mt][0]), negc, f32x4{0.f, 0.f, 0.f, 0.f});
+                    f32x4 acc = corr[mt];
 #pragma unroll
-                    for (int t = 1; t < 4; ++t)
-                        corr[mt] = mfma_bf16_16x16x32(as_bf16x8(av[u][mt][t]), negc, corr[mt]);
-                }
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    const float s = bf16_to_f32(sv[u][ct]);
-                    bf16x8 bfr[4];
-                    bfr[0] = unpack(wv[u][ct].x);
-                    bfr[1] = unpack(wv[u][ct].y);
-                    bfr[2] = unpack(wv[u][ct].z);
-                    bfr[3] = unpack(wv[u][ct].w);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        f32x4 acc = corr[mt];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            acc = mfma_bf16_16x16x32(as_bf16x8(av[u][mt][t]), bfr[t], acc);
-                        total[ct][mt][0] = fmaf(s, acc[0], total[ct][mt][0]);
-                        total[ct][mt][1] = fmaf(s, acc[1], total[ct][mt][1]);
-                        total[ct][mt][2] = fmaf(s, acc[2], total[ct][mt][2]);
-                        total[ct][mt][3] = fmaf(s, acc[3], total[ct][mt][3]);
-                    }
+                    for (int t = 0; t < 4; ++t)
+                        acc = mfma_bf16_16x16x32(as_bf16x8(b.a[u][mt][t]), bfr[t], acc);
+                    total[ct][mt][0] = fmaf(s, acc[0], total[ct][mt][0]);
+                    total[ct][mt][1] = fmaf(s, acc[1], total[ct][mt][1]);
+                    total[ct][mt][2] = fmaf(s, acc[2], total[ct][mt][2]);
+                    total[ct][mt][3] = fmaf(s, acc[3], total[ct][mt][3]);
                 }
             }
+        }
+    };
+
+    if constexpr (!PIPE) {
+        // register budget too small for two items: load, then compute
+        for (int it = 0; it < nitems; ++it) {
+            load_item(it, b0);
+            compute_item(min(U, ng - it * U), b0);
+        }
+    } else {
+        // unrolled by two so that buffers never change roles inside an iteration
+        if (nitems > 0) load_item(0, b0);
+        int it = 0;
+        for (; it + 2 < nitems; it += 2) {
+            load_item(it + 1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_item(U, b0);
+            load_item(it + 2, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_item(U, b1);
+        }
+        if (it + 1 < nitems) {
+            load_item(it + 1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_item(U, b0);
+            compute_item(ng - (it + 1) * U, b1);
+        } else if (it < nitems) {
+            compute_item(ng - it * U, b0);
         }
     }
 
@@ -262,26 +300,28 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
 //
 // Workgroup (split s, strip p) owns the column tiles [t0, t1) of strip p and
 // the groups [g0, g1) of K-slice s.  It stages a[:, 128*g0 : 128*g1] and the
-// offset terms -136 * sum_{k in g} a[m, k] in LDS once (coalesced loads; rows
-// padded by 16 bytes so a fragment read hits 16 distinct bank groups), so the
-// activation bytes it reads per weight byte are M / (4 * tiles), not M / 4.
-// Its 8 waves are KW K-sub-ranges x 8/KW tile slots; a wave streams its
-// (tile, chunk of U groups) items through a two-stage register pipeline.
+// offset terms -136 * sum_{k in g} a[m, k] in LDS once (direct-to-LDS copies,
+// all in flight together; rows padded by 16 bytes so a fragment read hits 16
+// distinct bank groups), so the activation bytes it reads per weight byte are
+// M / (4 * tiles), not M / 4.  Its 8 waves are KW K-sub-ranges x 8/KW tile
+// slots; a wave streams its (tile, chunk of U groups) items through a D-deep
+// register ring (ring_pipeline), the first D - 1 requests issued before the
+// activations are staged.
 //   - one slice, KW = 1 (wide outputs: gate_up, LM head): a wave finishes
 //     whole tiles and stores bf16 directly;
 //   - KW > 1: the KW partial sums of a tile are added in LDS in a fixed order;
-//   - S > 1 slices (narrow outputs: qkv, o, down): each workgroup writes its
-//     fp32 partial tile sums to its own workspace slot, then increments the
-//     strip's counter; the workgroup that arrives last adds the S slots in
-//     slice order (deterministic), stores bf16 and resets the counter to 0.
-//     The slots are written and read with agent-scope relaxed atomic accesses
-//     (coherent across the XCDs without cache maintenance); a device-wide
-//     fence would instead write back and invalidate every XCD's whole L2 on
-//     each call, which costs more than the GEMM.
+//   - S > 1 slices: each workgroup writes its fp32 partial tile sums to its own
+//     workspace slot, then increments the strip's counter; the workgroup that
+//     arrives last adds the S slots in slice order (deterministic), stores
+//     bf16 and resets the counter to 0.  The slots are written and read with
+//     agent-scope relaxed atomic accesses (coherent across the XCDs without
+//     cache maintenance); a device-wide fence would instead write back and
+//     invalidate every XCD's whole L2 on each call, which costs more than the
+//     GEMM.
 // ---------------------------------------------------------------------------
 constexpr int DK_NWAVE = 8;
 
-template <int KW, int U>
+template <int KW, int U, int D>
 __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K, int S,
@@ -314,25 +354,51 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
     float* corr = reinterpret_cast<float*>(lds + (size_t)M * rowb);   // [Gs][16]
     float* red = corr + Gs * 16;                                        // [T][KW][256]
 
-    auto item_tile = [&](int it) { return t0 + tslot + (it / nchunk) * TW; };
-
-    u32x4 wb[2][U];
-    uint32_t sb[2];
+    // ---- weight requests: a cursor over the wave's items in order
+    u32x4 wb[D][U];
+    uint32_t sb[D];
     // scales of an item: U * 16 contiguous bf16 = U * 8 dwords; lane l < 8U holds
     // those of group l/8, columns 2*(l%8), 2*(l%8)+1 (other lanes repeat a dword)
-    const int slane = lane % (8 * U);
-    auto load_item = [&](int it, int slot) {
-        const int nt = item_tile(it);
-        const size_t tile0 = (size_t)nt * G + g0 + gw0 + (it % nchunk) * U;   // wave-uniform
-        const u32x4* wp = reinterpret_cast<const u32x4*>(wq) + tile0 * 64;
+    const uint32_t soff = (uint32_t)(lane % (8 * U)) * 4;
+    int ld_item = 0, ld_chunk = 0, ld_tile = t0 + tslot;
+    auto load = [&](auto slot) {
+        constexpr int sl = decltype(slot)::value;
+        const bool valid = ld_item < nitems;
+        const size_t tile0 = (size_t)ld_tile * G + g0 + gw0 + (size_t)ld_chunk * U;
+        const auto rw = make_rsrc(valid ? wq + tile0 * 256 : wq, valid ? U * 1024 : 0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) wb[slot][u] = __builtin_nontemporal_load(wp + u * 64 + lane);
-        sb[slot] = reinterpret_cast<const uint32_t*>(sc + tile0 * 16)[slane];
+        for (int u = 0; u < U; ++u) wb[sl][u] = buffer_load_b128_nt(rw, lane * 16 + u * 1024);
+        const auto rs = make_rsrc(valid ? sc + tile0 * 16 : sc, valid ? U * 32 : 0);
+        sb[sl] = buffer_load_b32(rs, soff);
+        ++ld_item;
+        if (++ld_chunk == nchunk) { ld_chunk = 0; ld_tile += TW; }
     };
-    if (nitems > 0) load_item(0, 0);             // weights first: they do not depend on a
-
-    {   // stage the activation slice, 16-byte chunks
-        const int cpr = Gs * 16;                 // chunks per staged row
+    // ---- stage the activation slice, with the first weight requests in flight
+    const int cpr = Gs * 16;                     // 16-byte chunks per staged row
+    if (cpr % 64 == 0) {
+        // direct-to-LDS copies (a wave's 1 KiB stays inside one row), then the
+        // ring's first requests; the wait covers the copies only (the memory
+        // counter retires in issue order and the prologue issues P requests)
+        // The copies' per-lane address offset stays live until the wait: the
+        // compiler treats a pending copy as reading its address register and
+        // would otherwise wait for every load before reusing that register.
+        uint32_t lane16 = (uint32_t)lane * 16;
+        const int nblk = M * cpr / 64;
+        for (int j = wave; j < nblk; j += DK_NWAVE) {
+            const int r = (j * 64) / cpr;
+            const int cc0 = j * 64 - r * cpr;
+            const char* src = reinterpret_cast<const char*>(a + (size_t)r * K + (size_t)g0 * 128 +
+                                                            (size_t)cc0 * 8) + lane16;
+            load_lds_b128(reinterpret_cast<const u32x4*>(src),
+                          reinterpret_cast<u32x4*>(lds + (size_t)r * rowb + cc0 * 16));
+        }
+        ring_prologue<D>(load);
+        constexpr int P = (D - 1) * (U + 1);
+        static_assert(P < 64, "memory counter range");
+        __builtin_amdgcn_s_waitcnt((P & 15) | ((P >> 4) << 14) | (7 << 4) | (15 << 8));
+        asm volatile("" : "+v"(lane16));
+    } else {
+        ring_prologue<D>(load);                  // weights first: they do not depend on a
         const int total = M * cpr;
         for (int c = tid; c < total; c += DK_NWAVE * 64) {
             const int r = c / cpr;
@@ -367,19 +433,22 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
     const bool direct = (KW == 1) && (S == 1);
     f32x4 total = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute_item = [&](int it, int slot) {
-        const int gl0 = gw0 + (it % nchunk) * U;            // group within the slice
+    // ---- consume items in the same order
+    int cp_chunk = 0, cp_tile = t0 + tslot;
+    auto compute = [&](auto slot) {
+        constexpr int sl = decltype(slot)::value;
+        const int gl0 = gw0 + cp_chunk * U;      // group within the slice
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int g = gl0 + u;
             f32x4 acc = *reinterpret_cast<const f32x4*>(crow + g * 16);
-            const uint32_t pair = (uint32_t)__builtin_amdgcn_ds_bpermute(sidx + u * 32, (int)sb[slot]);
+            const uint32_t pair = (uint32_t)__builtin_amdgcn_ds_bpermute(sidx + u * 32, (int)sb[sl]);
             const float s = bf16_to_f32((pair >> shalf) & 0xffffu);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + g * 256 + t * 64));
-                const uint32_t w = t == 0 ? wb[slot][u].x : t == 1 ? wb[slot][u].y
-                                 : t == 2 ? wb[slot][u].z : wb[slot][u].w;
+                const uint32_t w = t == 0 ? wb[sl][u].x : t == 1 ? wb[sl][u].y
+                                 : t == 2 ? wb[sl][u].z : wb[sl][u].w;
                 acc = mfma_bf16_16x16x32(af, unpack(w), acc);
             }
             total[0] = fmaf(s, acc[0], total[0]);
@@ -387,8 +456,8 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
             total[2] = fmaf(s, acc[2], total[2]);
             total[3] = fmaf(s, acc[3], total[3]);
         }
-        if ((it % nchunk) == nchunk - 1) {       // the wave's share of a tile is done
-            const int tile = item_tile(it);
+        if (cp_chunk == nchunk - 1) {            // the wave's share of a tile is done
+            const int tile = cp_tile;
             if (direct) {
                 const int n = tile * 16 + col;
 #pragma unroll
@@ -406,27 +475,10 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
             }
             total = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        if (++cp_chunk == nchunk) { cp_chunk = 0; cp_tile += TW; }
     };
 
-    // Steady state with straight-line prefetches and pinned issue order; the
-    // last one or two items are peeled so nothing is fetched twice.
-    int it = 0;
-    for (; it + 2 < nitems; it += 2) {
-        load_item(it + 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_item(it, 0);
-        load_item(it + 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_item(it + 1, 1);
-    }
-    if (it + 1 < nitems) {
-        load_item(it + 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_item(it, 0);
-        compute_item(it + 1, 1);
-    } else if (it < nitems) {
-        compute_item(it, 0);
-    }
+    ring_pipeline<D>(nitems, load, compute);
     if (direct) return;
 
     // ---- reduction over the KW sub-ranges (LDS), then over the S slices
@@ -701,9 +753,11 @@ template <int MT, int CT>
 static void launch_small(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
                          int M, int N, int K, hipStream_t s) {
     constexpr int NWAVE = QG_SM_NWAVE;
-    constexpr int U = MT == 1 ? QG_SM_U : (MT == 2 ? 2 : 1);
+    constexpr int U = MT == 1 ? QG_SM_U : 1;
+    // two items in flight need 2*U*(5*CT + 16*MT) VGPRs of buffers
+    constexpr bool PIPE = MT <= 2 && CT <= 2;
     const int NT = N / 16;
-    hipLaunchKernelGGL((w4a16_small_m_kernel<MT, CT, NWAVE, U>), dim3(NT / CT), dim3(NWAVE * 64),
+    hipLaunchKernelGGL((w4a16_small_m_kernel<MT, CT, NWAVE, U, PIPE>), dim3(NT / CT), dim3(NWAVE * 64),
                        0, s, a, wq, sc, y, M, N, K);
 }
 
@@ -720,33 +774,58 @@ static void launch_small_ct(const uint16_t* a, const uint32_t* wq, const uint16_
 }
 
 // ---- decode-kernel configuration (M <= 16), a function of the shape only ----
-#ifndef QG_DK_TARGET_CUS          // workgroups the narrow split aims to fill
-#define QG_DK_TARGET_CUS 256
-#endif
-#ifndef QG_DK_WIDE_TILES          // one K-slice from this many column tiles
+#ifndef QG_DK_WIDE_TILES          // one workgroup strip per CU from this many column tiles
 #define QG_DK_WIDE_TILES 512
 #endif
-#ifndef QG_DK_TILES_PER_STRIP     // column tiles per workgroup for narrow outputs
-#define QG_DK_TILES_PER_STRIP 8
+#ifndef QG_DK_WIDE_KW             // waves sharing one tile's K range, wide outputs
+#define QG_DK_WIDE_KW 0       // 0: chosen from the tiles per strip
+#endif
+#ifndef QG_DK_WIDE_PER_CU         // workgroup strips per CU, wide outputs
+#define QG_DK_WIDE_PER_CU 2
+#endif
+#ifndef QG_DK_WIDE_D              // ring depth, wide outputs
+#define QG_DK_WIDE_D 4
+#endif
+#ifndef QG_DK_NARROW_D            // ring depth, narrow outputs
+#define QG_DK_NARROW_D 4
+#endif
+#ifndef QG_DK_NARROW_KW           // waves sharing one tile's K range, narrow outputs
+#define QG_DK_NARROW_KW 8
+#endif
+#ifndef QG_DK_NARROW_TPS          // column tiles per workgroup strip, narrow outputs
+#define QG_DK_NARROW_TPS 1
+#endif
+#ifndef QG_DK_NARROW_SMALLM       // 1: narrow outputs whose slice fits go to the small-M kernel
+#define QG_DK_NARROW_SMALLM 1
+#endif
+#ifndef QG_DK_NARROW_FIT          // 0: narrow outputs always split K across workgroups
+#define QG_DK_NARROW_FIT 1
+#endif
+#ifndef QG_DK_SPLIT_TPS           // column tiles per strip when K is split across workgroups
+#define QG_DK_SPLIT_TPS 4
+#endif
+#ifndef QG_DK_SPLIT_TARGET        // workgroups a K split aims for
+#define QG_DK_SPLIT_TARGET 256
+#endif
+#ifndef QG_DK_SPLIT_LDS           // LDS per workgroup a K split prefers (two per CU)
+#define QG_DK_SPLIT_LDS (80 * 1024)
+#endif
+#ifndef QG_DK_MAX_U               // groups per request (the ring holds D * U KiB per wave)
+#define QG_DK_MAX_U 2
 #endif
 #ifndef QG_DK_LDS_BUDGET
 #define QG_DK_LDS_BUDGET (144 * 1024)
 #endif
-#ifndef QG_DK_SPLIT_MIN_GROUPS   // K splits across workgroups only for K >= 128 * this ...
-#define QG_DK_SPLIT_MIN_GROUPS 64
-#endif
-#ifndef QG_DK_SPLIT_MIN_M        // ... and M above this (measured: below, the in-workgroup
-#define QG_DK_SPLIT_MIN_M 4      // split-K kernel is faster; the slot reduction costs a few us)
-#endif
 
 struct DecodeCfg {
-    int S, NS, KW, U;
+    int S, NS, KW, U, D;
     size_t lds;
     bool ok;
 };
 
-static int largest_u(int ng) {
-    for (int u : {8, 4, 2, 1})
+// largest u <= umax (a power of two) dividing ng
+static int largest_u(int ng, int umax) {
+    for (int u = umax; u > 1; u >>= 1)
         if (ng % u == 0) return u;
     return 1;
 }
@@ -756,29 +835,88 @@ static size_t decode_lds(int M, int Gs, int tmax, int KW, bool direct) {
            (direct ? 0 : (size_t)tmax * KW * 256 * sizeof(float));
 }
 
+static int ring_umax(int D) {
+    const int u = 16 / D;
+    return u < QG_DK_MAX_U ? (u < 1 ? 1 : u) : QG_DK_MAX_U;
+}
+
+// compute units of the current device, read once per process (the grid shapes
+// of a plan must not change between its workspace query and its launch)
+static int device_cu_count() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 256;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        return n;
+    }();
+    return cus;
+}
+
 static DecodeCfg decode_cfg(int M, int N, int K) {
-    DecodeCfg c{1, 1, 1, 1, 0, false};
-    if (M > 16) return c;
+    DecodeCfg c{1, 1, 1, 1, 2, 0, false};
+    if (M < 1 || M > 16) return c;
     const int NT = N / 16;
     const int G = K / 128;
     if (NT >= QG_DK_WIDE_TILES) {                       // wide: whole K per workgroup
-        const size_t lds = decode_lds(M, G, 0, 1, true);
-        if (lds <= QG_DK_LDS_BUDGET) {
-            c.S = 1; c.KW = 1; c.U = largest_u(G); c.lds = lds; c.ok = true;
-            c.NS = 0;                                   // set from the device at launch
+        const int cus = device_cu_count();
+        // waves per tile: enough that every wave streams when a strip has few tiles
+        int kw0 = QG_DK_WIDE_KW;
+        if (kw0 == 0) {
+            const int tpw = (NT + cus * QG_DK_WIDE_PER_CU - 1) / (cus * QG_DK_WIDE_PER_CU);
+            kw0 = tpw >= 3 ? 1 : tpw == 2 ? 4 : 8;
+        }
+        for (int kw = kw0; kw >= 1; kw >>= 1) {
+            if (G % kw) continue;
+            // strips: as many as the LDS allows resident, up to WIDE_PER_CU per CU
+            int per_cu = QG_DK_WIDE_PER_CU;
+            size_t lds = 0;
+            int NS = 0;
+            for (; per_cu >= 1; --per_cu) {
+                NS = min(NT, cus * per_cu);
+                const int tmax = (NT + NS - 1) / NS;
+                lds = decode_lds(M, G, tmax, kw, kw == 1);
+                if (lds <= QG_DK_LDS_BUDGET && lds * per_cu <= 160 * 1024) break;
+            }
+            if (per_cu < 1) continue;
+            c.S = 1; c.KW = kw; c.NS = NS;
+            c.D = kw == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D;
+            c.U = largest_u(G / kw, ring_umax(c.D));
+            c.lds = lds; c.ok = true;
             return c;
         }
     }
-    if (G < QG_DK_SPLIT_MIN_GROUPS || M <= QG_DK_SPLIT_MIN_M) return c;
-    const int NS = NT / QG_DK_TILES_PER_STRIP > 0 ? NT / QG_DK_TILES_PER_STRIP : 1;
-    const int tmax = (NT + NS - 1) / NS;
-    for (int S = 1; S <= G; ++S) {                      // smallest K split that fills the GPU
-        if (G % S) continue;
-        const size_t lds = decode_lds(M, G / S, tmax, 1, S == 1);
+    // narrow, slice fits: strips of TPS tiles, KW waves share each tile's K range
+    const int tps = QG_DK_NARROW_TPS < NT ? QG_DK_NARROW_TPS : NT;
+    for (int kw = QG_DK_NARROW_KW; QG_DK_NARROW_FIT && kw >= 1; kw >>= 1) {
+        const int NS = NT / tps;
+        const int tmax = (NT + NS - 1) / NS;
+        if (G % kw || kw * tmax > DK_NWAVE * 4) continue;
+        const bool direct = kw == 1;
+        const size_t lds = decode_lds(M, G, tmax, kw, direct);
         if (lds > QG_DK_LDS_BUDGET) continue;
-        if ((long long)NS * S < QG_DK_TARGET_CUS && S < G) continue;
-        c.S = S; c.NS = NS; c.KW = 1; c.U = largest_u(G / S); c.lds = lds; c.ok = true;
+        if (QG_DK_NARROW_SMALLM) return c;              // leave it to the small-M kernel
+        c.S = 1; c.NS = NS; c.KW = kw; c.D = kw == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D;
+        c.U = largest_u(G / kw, ring_umax(c.D));
+        c.lds = lds; c.ok = true;
         return c;
+    }
+    // narrow, slice too large for LDS: strips of SPLIT_TPS tiles, one wave per
+    // tile, the smallest K split that fits and gives enough workgroups
+    const int NS = NT / QG_DK_SPLIT_TPS > 0 ? NT / QG_DK_SPLIT_TPS : 1;
+    const int tmax = (NT + NS - 1) / NS;
+    // first pass: two workgroups fit per CU; second pass: one
+    for (const size_t budget : {(size_t)QG_DK_SPLIT_LDS, (size_t)QG_DK_LDS_BUDGET}) {
+        for (int S = 2; S <= G; ++S) {
+            if (G % S) continue;
+            const size_t lds = decode_lds(M, G / S, tmax, 1, false);
+            if (lds > budget) continue;
+            if ((long long)NS * S < QG_DK_SPLIT_TARGET && S < G) continue;
+            c.S = S; c.NS = NS; c.KW = 1; c.D = QG_DK_WIDE_D;
+            c.U = largest_u(G / S, ring_umax(c.D));
+            c.lds = lds; c.ok = true;
+            return c;
+        }
     }
     return c;
 }
@@ -789,43 +927,42 @@ static size_t decode_ws_bytes(const DecodeCfg& c, int N) {
     return part + (size_t)c.NS * sizeof(unsigned);
 }
 
-static int device_cu_count() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return QG_DK_TARGET_CUS;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return QG_DK_TARGET_CUS;
-    return cus;
-}
-
-template <int KW, int U>
+template <int KW, int U, int D>
 static void launch_decode_t(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
                             int M, int N, int K, const DecodeCfg& c, int NS, void* ws,
                             hipStream_t s) {
     static bool attr_set = false;   // allow up to the LDS budget (the default limit is 64 KiB)
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_decode_kernel<KW, U>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_decode_kernel<KW, U, D>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, QG_DK_LDS_BUDGET);
         attr_set = true;
     }
     float* part = static_cast<float*>(ws);
     unsigned* cnt = ws ? reinterpret_cast<unsigned*>(part + (size_t)c.S * (N / 16) * 256) : nullptr;
-    hipLaunchKernelGGL((w4a16_decode_kernel<KW, U>), dim3(c.S * NS), dim3(DK_NWAVE * 64), c.lds, s,
+    hipLaunchKernelGGL((w4a16_decode_kernel<KW, U, D>), dim3(c.S * NS), dim3(DK_NWAVE * 64), c.lds, s,
                        a, wq, sc, y, M, N, K, c.S, NS, part, cnt);
+}
+
+template <int KW, int D>
+static void launch_decode_u(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
+                            int M, int N, int K, const DecodeCfg& c, int NS, void* ws,
+                            hipStream_t s) {
+    switch (c.U) {
+        case 8: launch_decode_t<KW, (16 / D >= 8 ? 8 : 1), D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        case 4: launch_decode_t<KW, (16 / D >= 4 ? 4 : 1), D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        case 2: launch_decode_t<KW, 2, D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        default: launch_decode_t<KW, 1, D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+    }
 }
 
 static void launch_decode(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
                           int M, int N, int K, const DecodeCfg& c, void* ws, hipStream_t s) {
-    int NS = c.NS;
-    if (NS == 0) {                                      // wide: size the grid to the device
-        static const int cus = device_cu_count();
-        const int per_cu = c.lds * 2 <= 160 * 1024 ? 2 : 1;
-        NS = min(N / 16, cus * per_cu);
-    }
-    switch (c.U) {
-        case 8: launch_decode_t<1, 8>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
-        case 4: launch_decode_t<1, 4>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
-        case 2: launch_decode_t<1, 2>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
-        default: launch_decode_t<1, 1>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+    const int NS = c.NS;
+    switch (c.KW) {
+        case 8: launch_decode_u<8, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        case 4: launch_decode_u<4, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        case 2: launch_decode_u<2, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        default: launch_decode_u<1, QG_DK_WIDE_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
     }
 }
 

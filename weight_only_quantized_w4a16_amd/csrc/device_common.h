@@ -78,6 +78,15 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16, fp32 accumulate.  A: lane l holds row l%32, k = 8*(l/32) .. +7;
+// B: lane l holds column l%32, the same 8 k; D: register i of lane l holds
+// row 8*(i/4) + 4*(l/32) + i%4, column l%32.  On gfx950 this form sustains about
+// twice the bf16 rate of the 16x16x32 form.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // 16x16x128 OCP e4m3 x e4m3, fp32 accumulate (block scales fixed at 2^0).
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -146,6 +155,18 @@ __device__ __forceinline__ void ring_prologue(Load&& load) {
         load(s);
         __builtin_amdgcn_sched_barrier(0);
     });
+}
+
+// The same copy issued as inline assembly: the compiler does not track it, so
+// it adds no waits of its own between copies and later LDS accesses (it cannot
+// tell LDS stages apart and would wait for every copy).  The caller waits for
+// the copy with s_waitcnt vmcnt and publishes it with a barrier.
+__device__ __forceinline__ void lds_copy_b128(const void* src, const void* lds_dst) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {

@@ -561,20 +561,26 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
-// Large M (M > 64): BM x 128 output tile per workgroup (BM = 128; 256 is
-// available), four waves in a 2 x 2 grid of (BM/2) x 64.  Per group (128 rows of K):
-//   * the activation tile a[m0 : m0+BM, 128g : 128g+128] is copied straight
-//     into LDS with 128-bit direct-to-LDS loads (no VGPR staging), double
-//     buffered; lane l of a load writes LDS slot l, so each lane fetches the
-//     global chunk that the 16-byte XOR swizzle (chunk c of row r stored at
-//     c ^ (r % 16)) puts in its slot, and fragment reads are conflict free;
-//   * each wave loads its four weight tiles straight into registers (they are
-//     already in fragment order), unpacks them once, and for every m-subtile
-//     reads its A fragment from LDS once and runs the four n-tiles against it;
-//   * every (m-subtile, n-tile) group sum starts from the precomputed offset
-//     term -136 * sum(a) and is scaled into the total by the group scale.
-// The next group's activation, weight, scale and offset loads are in flight
-// while the current group computes.
+// Large M (M > 64): 128 x 256 output tile per workgroup, eight waves in a
+// 2 x 4 grid of 64 x 64, K walked one group (128 rows) at a time through an
+// NS-stage pipeline in LDS.  Stage g % NS holds, for group g:
+//   * the activation tile a[m0 : m0+128, 128g : 128g+128] (32 KiB), stored with
+//     a 16-byte XOR swizzle (chunk c of row r at c ^ (r % 16)) so fragment
+//     reads are conflict free;
+//   * the 16 weight tiles of the 256 columns (16 KiB) in their native fragment
+//     order (a wave reads its fragment of a tile with one 128-bit LDS read);
+//   * their bf16 scales (512 B) and the offset terms corr[g][m0 : m0+128].
+// Everything is copied with 128-bit direct-to-LDS loads, eight per thread per
+// stage, issued NS - 1 groups ahead.  A group step waits until at most
+// (NS - 2) stages of copies are outstanding, so this stage has landed, then a
+// barrier publishes it (and frees the stage read one step earlier, which the
+// next copies refill).  A wave's 64 x 64 tile is 2 x 2 blocks of 32 x 32 on
+// v_mfma_f32_32x32x16_bf16 (on gfx950 the 16x16x32 form sustains only about
+// half the bf16 rate); per group and 16-k step it unpacks one weight word per
+// 32-column block and reads one A fragment per 32-row block.  Every block's
+// group sum starts from the offset terms and is scaled into the total by the
+// group scale (one per lane: a lane owns one column).  Two waves per SIMD let
+// one wave's unpack and scaling overlap the other's MFMAs.
 //
 // Tile order: the grid is 1-D and workgroups are dealt round-robin to the 8
 // XCDs (each with its own L2).  Workgroup id is remapped so that each XCD
@@ -583,147 +589,187 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 // XCD's L2 instead of fetching it once per XCD.
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
+constexpr int LM_BM = 128;
+constexpr int LM_BN = 256;
 
 __device__ __forceinline__ int xcd_tile(int id, int total) {
     const int per = total / NUM_XCD;
     return id < per * NUM_XCD ? (id % NUM_XCD) * per + id / NUM_XCD : id;
 }
 
-template <int BM>
-__global__ __launch_bounds__(256) void w4a16_large_m_kernel(
+template <int NS>
+__global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
     int M, int Mp, int N, int K) {
-    constexpr int MI = BM / 32;                  // m-subtiles per wave
-    constexpr int ROWS_PER_WAVE_LOAD = BM / 4;   // activation rows each wave copies
-    extern __shared__ __attribute__((aligned(16))) u32x4 As[];   // [2][BM][16]
+    constexpr int BM = LM_BM;
+    constexpr int NTB = LM_BN / 16;              // column tiles per workgroup
+    static_assert(NS >= 2 && NS <= 3, "stages");
+    // one LDS object per stage: activation tile, weight tiles, scales, offset terms
+    struct Stage {
+        u32x4 a[BM * 16];
+        u32x4 w[NTB * 64];
+        uint16_t s[NTB * 16];
+        float c[BM];
+    };
+    __shared__ __attribute__((aligned(16))) Stage S0, S1, S2x[NS > 2 ? 1 : 0 + 1];
+    auto stage = [&](auto st) -> Stage& {
+        constexpr int v = decltype(st)::value;
+        if constexpr (v == 0) return S0;
+        else if constexpr (v == 1) return S1;
+        else return S2x[0];
+    };
 
     const int G = K >> 7;
     const int NT = N >> 4;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wm = wave >> 2;                    // 0..1: 64-row half
+    const int wn = wave & 3;                     // 0..3: 64-column quarter
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int mb = (M + BM - 1) / BM;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     const int m0 = (tile % mb) * BM;
-    const int n0 = (tile / mb) * 128;
+    const int nt0 = (tile / mb) * NTB;           // first column tile
 
-    // activation copy: instruction i of wave w fills rows w*BM/4 + 4i + lane/16, slot lane%16
-    const u32x4* aload[BM / 16];
-    int lds_off[BM / 16];
+    // copies per thread per stage: 4 activation, 2 weight, 1 scale, 1 offset
+    // activation: copy i of wave w fills rows 16w + 4i + lane/16 .. (4 rows), slot lane%16
+    const u32x4* aload[4];
+    int a_off[4];
 #pragma unroll
-    for (int i = 0; i < BM / 16; ++i) {
-        const int r = wave * ROWS_PER_WAVE_LOAD + 4 * i + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+        const int r = wave * 16 + 4 * i + (lane >> 4);
         const int chunk = (lane & 15) ^ (r & 15);
         const int grow = min(m0 + r, M - 1);     // rows >= M are never stored
         aload[i] = reinterpret_cast<const u32x4*>(a + (size_t)grow * K) + chunk;
-        lds_off[i] = (wave * ROWS_PER_WAVE_LOAD + 4 * i) * 16;   // u32x4 units, wave-uniform
+        a_off[i] = (wave * 16 + 4 * i) * 16;     // u32x4 units, wave-uniform
     }
-    auto load_a = [&](int g, int buf) {
+    // weights: wave w copies column tiles 2w, 2w+1 (clamped past N: never stored)
+    const u32x4* wload[2];
 #pragma unroll
-        for (int i = 0; i < BM / 16; ++i)
-            load_lds_b128(aload[i] + (size_t)g * 16, As + buf * BM * 16 + lds_off[i]);
-    };
-
-    const u32x4* wsrc[4];
-    const uint16_t* ssrc[4];
-    bool tok[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        const int nt = (n0 >> 4) + wn * 4 + ni;
-        tok[ni] = nt < NT;
-        const size_t ntc = tok[ni] ? nt : NT - 1;
-        wsrc[ni] = reinterpret_cast<const u32x4*>(wq) + ntc * G * 64 + lane;
-        ssrc[ni] = sc + ntc * G * 16 + col;
+    for (int j = 0; j < 2; ++j) {
+        const int nt = min(nt0 + 2 * wave + j, NT - 1);
+        wload[j] = reinterpret_cast<const u32x4*>(wq) + (size_t)nt * G * 64 + lane;
     }
-    const float* csrc = corr + m0 + wm * (BM / 2) + 4 * kq;
+    // scales: 16 tiles x 32 B = 32 chunks; wave w copies chunks 4w .. 4w+3 (lanes 0..3)
+    const bool sl = lane < 4;
+    const int sc_chunk = wave * 4 + (sl ? lane : 0);
+    const uint16_t* sload = sc + (size_t)min(nt0 + (sc_chunk >> 1), NT - 1) * G * 16 + (sc_chunk & 1) * 8;
+    // offset terms: 128 floats = 32 chunks; wave w copies rows 16w .. 16w+15 (lanes 0..3)
+    const float* cload = corr + m0 + wave * 16 + (sl ? lane : 0) * 4;
 
-    f32x4 total[MI][4];
+    int ld_g = 0;
+    auto load = [&](auto slot) {
+        Stage& S = stage(slot);
+        const int gc = ld_g < G ? ld_g : G - 1;  // past the last group: a stage never read
+        // (copies as inline assembly: the compiler does not order them against
+        // LDS reads itself -- it would drain every copy at the loop head -- so
+        // the step's counted wait and barrier are what publish a stage)
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+        for (int i = 0; i < 4; ++i) lds_copy_b128(aload[i] + (size_t)gc * 16, S.a + a_off[i]);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 wnext[4];
-    uint32_t snext[4];
-    f32x4 cnext[MI];
-    auto load_rest = [&](int g) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            wnext[ni] = __builtin_nontemporal_load(wsrc[ni] + (size_t)g * 64);
-            snext[ni] = ssrc[ni][(size_t)g * 16];
+        for (int j = 0; j < 2; ++j) lds_copy_b128(wload[j] + (size_t)gc * 64, S.w + (2 * wave + j) * 64);
+        if (sl) {
+            lds_copy_b128(sload + (size_t)gc * 16, reinterpret_cast<u32x4*>(S.s) + wave * 4);
+            lds_copy_b128(cload + (size_t)gc * Mp, reinterpret_cast<u32x4*>(S.c) + wave * 4);
         }
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            cnext[mi] = *reinterpret_cast<const f32x4*>(csrc + (size_t)g * Mp + mi * 16);
+        ++ld_g;
     };
+
+    f32x16 total[2][2];                          // [m-block][32-column block]
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) total[mi][bb][i] = 0.f;
 
     const Int4Unpacker unpack;
-    load_a(0, 0);
-    load_rest(0);
-    __builtin_amdgcn_s_waitcnt(0);               // vmcnt(0) lgkmcnt(0) expcnt(0)
-    __syncthreads();
-
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        u32x4 wcur[4];
-        float scur[4];
-        f32x4 ccur[MI];
+    auto step = [&](auto slot, bool live) {
+        // every step issues 8 copies per thread: once at most (NS - 2) * 8 are
+        // outstanding this stage has landed; the barrier publishes it to all
+        // waves and frees the stage read one step earlier
+        constexpr int P = (NS - 2) * 8;
+        __builtin_amdgcn_s_waitcnt((P & 15) | ((P >> 4) << 14) | (7 << 4) | (15 << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        load(ic<(decltype(slot)::value + NS - 1) % NS>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if (!live) return;
+        const Stage& S = stage(slot);
+        // 32-column block b of the wave = native tiles 4wn+2b, 4wn+2b+1; lane l
+        // (column l%32, k-half h = l/32) reads two 16-byte fragment slots of its
+        // tile: slot (l%16) + 16h holds rows 32t + 8h + 0..7 (k-step 2t), slot
+        // (l%16) + 16(2+h) rows 32t + 16 + 8h + 0..7 (k-step 2t+1), word t each
+        const int h = lane >> 5;
+        u32x4 wlo[2], whi[2];
+        float scur[2];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            wcur[ni] = wnext[ni];
-            scur[ni] = bf16_to_f32(snext[ni]);
+        for (int bb = 0; bb < 2; ++bb) {
+            const int tl = wn * 4 + 2 * bb + ((lane & 31) >> 4);
+            wlo[bb] = S.w[tl * 64 + (lane & 15) + 16 * h];
+            whi[bb] = S.w[tl * 64 + (lane & 15) + 16 * h + 32];
+            scur[bb] = bf16_to_f32(S.s[tl * 16 + (lane & 15)]);
         }
+        f32x16 acc[2][2];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) ccur[mi] = cnext[mi];
-        if (g + 1 < G) {
-            load_a(g + 1, buf ^ 1);
-            load_rest(g + 1);
-        }
-        bf16x8 bfr[4][4];
+        for (int mi = 0; mi < 2; ++mi) {         // the group sums start from the offset terms
+            const float* cb = S.c + wm * 64 + mi * 32 + 4 * h;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            bfr[ni][0] = unpack(wcur[ni].x);
-            bfr[ni][1] = unpack(wcur[ni].y);
-            bfr[ni][2] = unpack(wcur[ni].z);
-            bfr[ni][3] = unpack(wcur[ni].w);
-        }
-        const u32x4* Ab = As + buf * BM * 16;
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(cb + 8 * q);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            const int r = wm * (BM / 2) + mi * 16 + col;
-            bf16x8 af[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) af[t] = as_bf16x8(Ab[r * 16 + ((4 * t + kq) ^ col)]);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                f32x4 acc = ccur[mi];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) acc = mfma_bf16_16x16x32(af[t], bfr[ni][t], acc);
-                total[mi][ni][0] = fmaf(scur[ni], acc[0], total[mi][ni][0]);
-                total[mi][ni][1] = fmaf(scur[ni], acc[1], total[mi][ni][1]);
-                total[mi][ni][2] = fmaf(scur[ni], acc[2], total[mi][ni][2]);
-                total[mi][ni][3] = fmaf(scur[ni], acc[3], total[mi][ni][3]);
+                for (int e = 0; e < 4; ++e) acc[mi][0][4 * q + e] = acc[mi][1][4 * q + e] = c4[e];
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);           // next group's copies have landed
-        __syncthreads();
-    }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {            // 16-k steps of the group
+            bf16x8 bfr[2], af[2];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const u32x4 wv = (j & 1) ? whi[bb] : wlo[bb];
+                const int t = j >> 1;
+                bfr[bb] = unpack(t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w);
+            }
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                const int r = wm * 64 + mi * 32 + (lane & 31);
+                af[mi] = as_bf16x8(S.a[r * 16 + ((2 * j + h) ^ (r & 15))]);
+            }
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) acc[mi][bb] = mfma_bf16_32x32x16(af[mi], bfr[bb], acc[mi][bb]);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) total[mi][bb][i] = fmaf(scur[bb], acc[mi][bb][i], total[mi][bb][i]);
+    };
+
+    static_for<NS - 1>([&](auto s) {
+        load(s);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    for (int g = 0; g < G; g += NS)
+        static_for<NS>([&](auto s) { step(s, g + decltype(s)::value < G); });
 
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    for (int bb = 0; bb < 2; ++bb) {
+        const int nt = nt0 + wn * 4 + 2 * bb + ((lane & 31) >> 4);
+        if (nt >= NT) continue;
+        const int n = nt * 16 + (lane & 15);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            if (!tok[ni]) continue;
-            const int n = n0 + wn * 64 + ni * 16 + col;
+        for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * (BM / 2) + mi * 16 + 4 * kq + i;
-                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i]);
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][bb][i]);
             }
         }
     }
@@ -982,24 +1028,16 @@ const char* w4a16_kernel_for(int M, int N, int K) {
     return "w4a16_large_m_kernel";
 }
 
-constexpr int LM_MAX_BM = 256;
-#ifndef QG_LM_BM256_MIN_TILES     // 256-row tiles when they give at least this many workgroups;
-#define QG_LM_BM256_MIN_TILES (1 << 30)   // measured slower than 128-row tiles on every
-#endif                                    // stack shape (one workgroup per CU), so off
+constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple of this
+#ifndef QG_LM_NS                   // pipeline stages of the large-M kernel
+#define QG_LM_NS 3
+#endif
 
-template <int BM>
 static void launch_large(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, const float* corr,
                          uint16_t* y, int M, int Mp, int N, int K, hipStream_t s) {
-    static bool attr_set = false;
-    const size_t lds = (size_t)2 * BM * 16 * sizeof(u32x4);
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_large_m_kernel<BM>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        attr_set = true;
-    }
-    const int tiles = ((N + 127) / 128) * ((M + BM - 1) / BM);
-    hipLaunchKernelGGL((w4a16_large_m_kernel<BM>), dim3(tiles), dim3(256), lds, s, a, wq, sc, corr, y,
-                       M, Mp, N, K);
+    const int tiles = ((N + LM_BN - 1) / LM_BN) * ((M + LM_BM - 1) / LM_BM);
+    hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS>), dim3(tiles), dim3(512), 0, s, a, wq, sc,
+                       corr, y, M, Mp, N, K);
 }
 
 size_t w4a16_workspace_bytes(int M, int N, int K) {
@@ -1026,11 +1064,7 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
         const size_t n = (size_t)G * Mp;
         hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
                            0, s, a, M, Mp, K, corr);
-        const int nb = (N + 127) / 128;
-        if ((long long)((M + 255) / 256) * nb >= QG_LM_BM256_MIN_TILES)
-            launch_large<256>(a, packed, scales, corr, y, M, Mp, N, K, s);
-        else
-            launch_large<128>(a, packed, scales, corr, y, M, Mp, N, K, s);
+        launch_large(a, packed, scales, corr, y, M, Mp, N, K, s);
     }
 }
 

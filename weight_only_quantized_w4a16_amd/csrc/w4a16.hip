@@ -570,8 +570,11 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 //   * the 16 weight tiles of the 256 columns (16 KiB) in their native fragment
 //     order (a wave reads its fragment of a tile with one 128-bit LDS read);
 //   * their bf16 scales (512 B) and the offset terms corr[g][m0 : m0+128].
-// Everything is copied with 128-bit direct-to-LDS loads, eight per thread per
-// stage, issued NS - 1 groups ahead.  A group step waits until at most
+// Everything is copied with 128-bit direct-to-LDS loads, six per thread per
+// stage (scales and offset terms share one more copy by wave 0), issued NS - 1
+// groups ahead and spread over the previous group's math: a direct-to-LDS copy
+// occupies the CU's address unit for about 40 cycles whatever its size, so the
+// copies pace the loop unless they overlap the MFMAs.  A group step waits until at most
 // (NS - 2) stages of copies are outstanding, so this stage has landed, then a
 // barrier publishes it (and frees the stage read one step earlier, which the
 // next copies refill).  A wave's 64 x 64 tile is 2 x 2 blocks of 32 x 32 on
@@ -653,28 +656,32 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
         const int nt = min(nt0 + 2 * wave + j, NT - 1);
         wload[j] = reinterpret_cast<const u32x4*>(wq) + (size_t)nt * G * 64 + lane;
     }
-    // scales: 16 tiles x 32 B = 32 chunks; wave w copies chunks 4w .. 4w+3 (lanes 0..3)
-    const bool sl = lane < 4;
-    const int sc_chunk = wave * 4 + (sl ? lane : 0);
-    const uint16_t* sload = sc + (size_t)min(nt0 + (sc_chunk >> 1), NT - 1) * G * 16 + (sc_chunk & 1) * 8;
-    // offset terms: 128 floats = 32 chunks; wave w copies rows 16w .. 16w+15 (lanes 0..3)
-    const float* cload = corr + m0 + wave * 16 + (sl ? lane : 0) * 4;
+    // scales (16 tiles x 32 B) and offset terms (128 floats) are adjacent in a
+    // stage: one 1 KiB copy by wave 0, lanes 0..31 the scale chunks (tile l/2,
+    // half l%2), lanes 32..63 the offset-term chunks (rows 4(l-32) .. +3)
+    const bool sc_lane = lane < 32;
+    const uint16_t* sload = sc + (size_t)min(nt0 + ((lane & 31) >> 1), NT - 1) * G * 16 + (lane & 1) * 8;
+    const float* cload = corr + m0 + (lane & 31) * 4;
+    const char* scload = sc_lane ? reinterpret_cast<const char*>(sload) : reinterpret_cast<const char*>(cload);
+    const size_t sc_step = sc_lane ? (size_t)16 * sizeof(uint16_t) : (size_t)Mp * sizeof(float);
 
     int ld_g = 0;
-    auto load = [&](auto slot) {
+    // copy i (0..5 in every wave, 6 in wave 0 only) of group gc into stage S
+    auto copy = [&](Stage& S, int gc, int i) {
+        if (i < 4) {
+            lds_copy_b128(aload[i] + (size_t)gc * 16, S.a + a_off[i]);
+        } else if (i < 6) {
+            const int j = i - 4;
+            lds_copy_b128(wload[j] + (size_t)gc * 64, S.w + (2 * wave + j) * 64);
+        } else if (wave == 0) {
+            lds_copy_b128(scload + (size_t)gc * sc_step, S.s);
+        }
+    };
+    auto load_all = [&](auto slot) {
         Stage& S = stage(slot);
         const int gc = ld_g < G ? ld_g : G - 1;  // past the last group: a stage never read
-        // (copies as inline assembly: the compiler does not order them against
-        // LDS reads itself -- it would drain every copy at the loop head -- so
-        // the step's counted wait and barrier are what publish a stage)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_copy_b128(aload[i] + (size_t)gc * 16, S.a + a_off[i]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) lds_copy_b128(wload[j] + (size_t)gc * 64, S.w + (2 * wave + j) * 64);
-        if (sl) {
-            lds_copy_b128(sload + (size_t)gc * 16, reinterpret_cast<u32x4*>(S.s) + wave * 4);
-            lds_copy_b128(cload + (size_t)gc * Mp, reinterpret_cast<u32x4*>(S.c) + wave * 4);
-        }
+        for (int i = 0; i < 7; ++i) copy(S, gc, i);
         ++ld_g;
     };
 
@@ -688,17 +695,27 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
 
     const Int4Unpacker unpack;
     auto step = [&](auto slot, bool live) {
-        // every step issues 8 copies per thread: once at most (NS - 2) * 8 are
-        // outstanding this stage has landed; the barrier publishes it to all
-        // waves and frees the stage read one step earlier
-        constexpr int P = (NS - 2) * 8;
-        __builtin_amdgcn_s_waitcnt((P & 15) | ((P >> 4) << 14) | (7 << 4) | (15 << 8));
+        // every step issues 6 copies per thread (7 in wave 0): once at most
+        // (NS - 2) steps' copies are outstanding this stage has landed; the
+        // barrier publishes it to all waves and frees the stage read one step
+        // earlier
+        constexpr int P1 = (NS - 2) * 6, P0 = (NS - 2) * 7;
+        if (wave == 0)
+            __builtin_amdgcn_s_waitcnt((P0 & 15) | ((P0 >> 4) << 14) | (7 << 4) | (15 << 8));
+        else
+            __builtin_amdgcn_s_waitcnt((P1 & 15) | ((P1 >> 4) << 14) | (7 << 4) | (15 << 8));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        load(ic<(decltype(slot)::value + NS - 1) % NS>{});
-        __builtin_amdgcn_sched_barrier(0);
-        if (!live) return;
+        constexpr int nst = (decltype(slot)::value + NS - 1) % NS;   // stage refilled this step
+        Stage& Dst = stage(ic<nst>{});
+        const int gnext = ld_g < G ? ld_g : G - 1;
+        ++ld_g;
+        if (!live) {
+#pragma unroll
+            for (int i = 0; i < 7; ++i) copy(Dst, gnext, i);
+            return;
+        }
         const Stage& S = stage(slot);
         // 32-column block b of the wave = native tiles 4wn+2b, 4wn+2b+1; lane l
         // (column l%32, k-half h = l/32) reads two 16-byte fragment slots of its
@@ -714,19 +731,26 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
             whi[bb] = S.w[tl * 64 + (lane & 15) + 16 * h + 32];
             scur[bb] = bf16_to_f32(S.s[tl * 16 + (lane & 15)]);
         }
-        f32x16 acc[2][2];
+        // the group sums start from the offset terms: they are the first k-step's
+        // accumulator input (an MFMA may write a register other than the one it
+        // reads, so neither block copies them)
+        f32x16 cinit[2];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {         // the group sums start from the offset terms
+        for (int mi = 0; mi < 2; ++mi) {
             const float* cb = S.c + wm * 64 + mi * 32 + 4 * h;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 c4 = *reinterpret_cast<const f32x4*>(cb + 8 * q);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[mi][0][4 * q + e] = acc[mi][1][4 * q + e] = c4[e];
+                for (int e = 0; e < 4; ++e) cinit[mi][4 * q + e] = c4[e];
             }
         }
+        f32x16 acc[2][2];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {            // 16-k steps of the group
+            // the next stage's copies go out one per k-step, between the MFMAs,
+            // so a wave does not stall on the copy queue before its math
+            if (j < 7) copy(Dst, gnext, j);
             bf16x8 bfr[2], af[2];
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
@@ -742,7 +766,8 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-                for (int bb = 0; bb < 2; ++bb) acc[mi][bb] = mfma_bf16_32x32x16(af[mi], bfr[bb], acc[mi][bb]);
+                for (int bb = 0; bb < 2; ++bb)
+                    acc[mi][bb] = mfma_bf16_32x32x16(af[mi], bfr[bb], j == 0 ? cinit[mi] : acc[mi][bb]);
         }
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
@@ -753,7 +778,7 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     };
 
     static_for<NS - 1>([&](auto s) {
-        load(s);
+        load_all(s);
         __builtin_amdgcn_sched_barrier(0);
     });
     for (int g = 0; g < G; g += NS)

@@ -176,6 +176,15 @@ __device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {
     return r;
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  This
+// remaps workgroup id so that each XCD receives a contiguous run of tile ids,
+// so tiles that are neighbours in the caller's order share that XCD's L2.
+constexpr int NUM_XCD = 8;
+__device__ __forceinline__ int xcd_tile(int id, int total) {
+    const int per = total / NUM_XCD;
+    return id < per * NUM_XCD ? (id % NUM_XCD) * per + id / NUM_XCD : id;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

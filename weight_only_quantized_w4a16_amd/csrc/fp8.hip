@@ -232,109 +232,154 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large M (M > 64): 256 x 128 output tile per workgroup, 4 waves in a 2 x 2
-// grid of 128 x 64.  The fp8 activation tile of one 128-row k-tile (256 rows
-// x 128 bytes) is staged in LDS, double buffered, with the 16-byte chunk
-// swizzle c ^ ((r / 2) % 8) (two 128-byte rows share one pass over the 64
-// banks); weight tiles go straight to registers.
+// Large M (M > 64): 128 x 256 output tile per workgroup, eight waves in a
+// 2 x 4 grid of 64 x 64 (4 x 4 MFMA tiles of 16x16x128 e4m3), K walked one
+// 128-row k-tile at a time through an NS-stage pipeline in LDS.  Stage
+// kt % NS holds, for k-tile kt, the activation tile (128 rows x 128 bytes,
+// 16-byte chunk c of row r at c ^ ((r / 2) % 8): two 128-byte rows share one
+// pass over the 64 banks) and the 16 weight tiles of the 256 columns in their
+// native fragment order (2 KiB each).  Everything is copied with 128-bit
+// direct-to-LDS loads, six per thread per stage, issued NS - 1 k-tiles ahead
+// and spread over the previous k-tile's MFMAs; a k-tile step waits until at
+// most (NS - 2) steps of copies are outstanding (so its stage has landed),
+// then a barrier publishes the stage and frees the one read a step earlier.
+// The fp32 totals are scaled by s_a[m] * s_w[n] once, in the epilogue.
 // ---------------------------------------------------------------------------
-constexpr int F8_BM = 256;
-constexpr int F8_BN = 128;
+constexpr int F8_BM = 128;
+constexpr int F8_BN = 256;
+#ifndef QG_F8_NS
+#define QG_F8_NS 3
+#endif
 
-__global__ __launch_bounds__(256) void w8a8_large_m_kernel(
+template <int NS>
+__global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
     const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
-    __shared__ u32x4 As[2][F8_BM][8];   // 2 x 32 KiB
+    constexpr int NTB = F8_BN / 16;              // column tiles per workgroup
+    static_assert(NS >= 2 && NS <= 3, "stages");
+    struct Stage {
+        u32x4 a[F8_BM * 8];                      // 16 KiB
+        u32x4 w[NTB * 128];                      // 32 KiB
+    };
+    __shared__ __attribute__((aligned(16))) Stage S0, S1, S2x[1];
+    auto stage = [&](auto st) -> Stage& {
+        constexpr int v = decltype(st)::value;
+        if constexpr (v == 0) return S0;
+        else if constexpr (v == 1) return S1;
+        else return S2x[0];
+    };
 
     const int KT = K >> 7;
     const int NT = N >> 4;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2;                    // 0..1: 64-row half
+    const int wn = wave & 3;                     // 0..3: 64-column quarter
     const int col = lane & 15;
     const int kq = lane >> 4;
-    const int m0 = blockIdx.y * F8_BM;
-    const int n0 = blockIdx.x * F8_BN;
+    const int mb = (M + F8_BM - 1) / F8_BM;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int m0 = (tile % mb) * F8_BM;
+    const int nt0 = (tile / mb) * NTB;
 
-    // loader: thread -> row tid (256 rows), 8 chunks of 16 bytes
-    const bool lrow_ok = (m0 + tid) < M;
-    const u32x4* asrc = reinterpret_cast<const u32x4*>(a + (size_t)(lrow_ok ? m0 + tid : 0) * K);
-
-    const u32x4* wsrc[4];
-    bool tok[4];
+    // activation copy i (0, 1) of wave w: rows 16w + 8i + lane/8, slot lane%8
+    const uint8_t* aload[2];
+    int a_off[2];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        const int nt = (n0 >> 4) + wn * 4 + ni;
-        tok[ni] = nt < NT;
-        wsrc[ni] = reinterpret_cast<const u32x4*>(wq) + (size_t)(tok[ni] ? nt : 0) * KT * 128 +
-                   lane * 2;
+    for (int i = 0; i < 2; ++i) {
+        const int r = wave * 16 + 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        const int grow = min(m0 + r, M - 1);     // rows >= M are never stored
+        aload[i] = a + (size_t)grow * K + chunk * 16;
+        a_off[i] = (wave * 16 + 8 * i) * 8;      // u32x4 units, wave-uniform
     }
-
-    f32x4 total[8][4];
+    // weight copies 2..5 of wave w: tiles 2w, 2w+1, two 1 KiB halves each
+    const uint8_t* wload[2];
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int j = 0; j < 2; ++j) {
+        const int nt = min(nt0 + 2 * wave + j, NT - 1);   // past N: never stored
+        wload[j] = wq + (size_t)nt * KT * 2048 + lane * 16;
+    }
+    auto copy = [&](Stage& S, int kt, int i) {
+        if (i < 2) {
+            lds_copy_b128(aload[i] + (size_t)kt * 128, S.a + a_off[i]);
+        } else {
+            const int j = (i - 2) >> 1, half = (i - 2) & 1;
+            lds_copy_b128(wload[j] + (size_t)kt * 2048 + half * 1024,
+                          S.w + (2 * wave + j) * 128 + half * 64);
+        }
+    };
+
+    f32x4 total[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 areg[8];
-    u32x4 wreg[4][2];
-    auto load_a = [&](int kt) {
+    int ld_kt = 0;
+    auto step = [&](auto slot, bool live) {
+        constexpr int P = (NS - 2) * 6;
+        __builtin_amdgcn_s_waitcnt((P & 15) | ((P >> 4) << 14) | (7 << 4) | (15 << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        constexpr int nst = (decltype(slot)::value + NS - 1) % NS;   // stage refilled this step
+        Stage& Dst = stage(ic<nst>{});
+        const int knext = ld_kt < KT ? ld_kt : KT - 1;   // past the end: a stage never read
+        ++ld_kt;
+        if (!live) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            areg[i] = lrow_ok ? asrc[(size_t)kt * 8 + i] : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) As[buf][tid][i ^ ((tid >> 1) & 7)] = areg[i];
-    };
-    auto load_w = [&](int kt) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            wreg[ni][0] = tok[ni] ? wsrc[ni][(size_t)kt * 128] : u32x4{0u, 0u, 0u, 0u};
-            wreg[ni][1] = tok[ni] ? wsrc[ni][(size_t)kt * 128 + 1] : u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < 6; ++i) copy(Dst, knext, i);
+            return;
         }
-    };
-
-    load_a(0);
-    load_w(0);
-    store_a(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
+        const Stage& S = stage(slot);
         i32x8 bfr[4];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) bfr[ni] = cat_i32x8(wreg[ni][0], wreg[ni][1]);
-        if (kt + 1 < KT) {
-            load_a(kt + 1);
-            load_w(kt + 1);
+        for (int ni = 0; ni < 4; ++ni) {
+            const int tl = wn * 4 + ni;
+            bfr[ni] = cat_i32x8(S.w[tl * 128 + lane * 2], S.w[tl * 128 + lane * 2 + 1]);
         }
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
-            const int r = wm * 128 + mi * 16 + col;
+        for (int mi = 0; mi < 4; ++mi) {
+            // the next stage's copies go out between the MFMAs
+            if (mi < 2) {
+                copy(Dst, knext, 2 * mi);
+                copy(Dst, knext, 2 * mi + 1);
+            } else {
+                copy(Dst, knext, mi + 2);
+            }
+            const int r = wm * 64 + mi * 16 + col;
             const int sw8 = (r >> 1) & 7;
-            const i32x8 af = cat_i32x8(As[buf][r][kq ^ sw8], As[buf][r][(4 + kq) ^ sw8]);
+            const i32x8 af = cat_i32x8(S.a[r * 8 + (kq ^ sw8)], S.a[r * 8 + ((4 + kq) ^ sw8)]);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) total[mi][ni] = mfma_fp8_16x16x128(af, bfr[ni], total[mi][ni]);
         }
-        if (kt + 1 < KT) store_a(buf ^ 1);
-        __syncthreads();
-    }
+    };
+
+    static_for<NS - 1>([&](auto s) {
+        Stage& S = stage(s);
+        const int kc = ld_kt < KT ? ld_kt : KT - 1;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) copy(S, kc, i);
+        ++ld_kt;
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    for (int kt = 0; kt < KT; kt += NS)
+        static_for<NS>([&](auto s) { step(s, kt + decltype(s)::value < KT); });
 
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-        if (!tok[ni]) continue;
-        const int n = n0 + wn * 64 + ni * 16 + col;
+        const int nt = nt0 + wn * 4 + ni;
+        if (nt >= NT) continue;
+        const int n = nt * 16 + col;
         const float swn = sw[n];
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
+        for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 128 + mi * 16 + 4 * kq + i;
-                if (m < M)
-                    y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i] * sa[m] * swn);
+                const int m = m0 + wm * 64 + mi * 16 + 4 * kq + i;
+                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i] * sa[m] * swn);
             }
         }
     }
@@ -387,8 +432,9 @@ void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w, 
     } else if (M <= 64) {
         launch_small_ct<4>(a, sa, w, sw, y, M, N, K, st);
     } else {
-        dim3 grid((N + F8_BN - 1) / F8_BN, (M + F8_BM - 1) / F8_BM);
-        hipLaunchKernelGGL(w8a8_large_m_kernel, grid, dim3(256), 0, st, a, sa, w, sw, y, M, N, K);
+        const int tiles = ((N + F8_BN - 1) / F8_BN) * ((M + F8_BM - 1) / F8_BM);
+        hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS>), dim3(tiles), dim3(512), 0, st, a, sa, w, sw,
+                           y, M, N, K);
     }
 }
 

@@ -591,14 +591,8 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 // weight tile run on one XCD at about the same time and share it through that
 // XCD's L2 instead of fetching it once per XCD.
 // ---------------------------------------------------------------------------
-constexpr int NUM_XCD = 8;
 constexpr int LM_BM = 128;
 constexpr int LM_BN = 256;
-
-__device__ __forceinline__ int xcd_tile(int id, int total) {
-    const int per = total / NUM_XCD;
-    return id < per * NUM_XCD ? (id % NUM_XCD) * per + id / NUM_XCD : id;
-}
 
 template <int NS>
 __global__ __launch_bounds__(512) void w4a16_large_m_kernel(

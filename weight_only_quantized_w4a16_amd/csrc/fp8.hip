@@ -232,31 +232,45 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large M (M > 64): 128 x 256 output tile per workgroup, eight waves in a
-// 2 x 4 grid of 64 x 64 (4 x 4 MFMA tiles of 16x16x128 e4m3), K walked one
+// Large M (M > 64): 128 x 128·NB output tile per workgroup (NB = 2, or 1 when
+// 256-column tiles would leave CUs idle), eight waves in a 2 x 4 grid of
+// 64 x 32·NB (4 x 2NB MFMA tiles of 16x16x128 e4m3), K walked one
 // 128-row k-tile at a time through an NS-stage pipeline in LDS.  Stage
 // kt % NS holds, for k-tile kt, the activation tile (128 rows x 128 bytes,
 // 16-byte chunk c of row r at c ^ ((r / 2) % 8): two 128-byte rows share one
-// pass over the 64 banks) and the 16 weight tiles of the 256 columns in their
+// pass over the 64 banks) and the 8·NB weight tiles of the columns in their
 // native fragment order (2 KiB each).  Everything is copied with 128-bit
-// direct-to-LDS loads, six per thread per stage, issued NS - 1 k-tiles ahead
+// direct-to-LDS loads, 2 + 2·NB per thread per stage, issued NS - 1 k-tiles ahead
 // and spread over the previous k-tile's MFMAs; a k-tile step waits until at
 // most (NS - 2) steps of copies are outstanding (so its stage has landed),
 // then a barrier publishes the stage and frees the one read a step earlier.
 // The fp32 totals are scaled by s_a[m] * s_w[n] once, in the epilogue.
 // ---------------------------------------------------------------------------
 constexpr int F8_BM = 128;
-constexpr int F8_BN = 256;
+
+static int f8_cu_count() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 256;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        return n;
+    }();
+    return cus;
+}
 #ifndef QG_F8_NS
 #define QG_F8_NS 3
 #endif
 
-template <int NS>
+template <int NS, int NB>
 __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
     const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
-    constexpr int NTB = F8_BN / 16;              // column tiles per workgroup
+    constexpr int NTB = 8 * NB;                  // column tiles per workgroup
+    constexpr int NI = 2 * NB;                   // column tiles per wave
+    constexpr int NCOPY = 2 + 2 * NB;            // copies per thread per stage
     static_assert(NS >= 2 && NS <= 3, "stages");
+    static_assert(NB == 1 || NB == 2, "column blocks");
     struct Stage {
         u32x4 a[F8_BM * 8];                      // 16 KiB
         u32x4 w[NTB * 128];                      // 32 KiB
@@ -275,7 +289,7 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2;                    // 0..1: 64-row half
-    const int wn = wave & 3;                     // 0..3: 64-column quarter
+    const int wn = wave & 3;                     // 0..3: column quarter (32 * NB columns)
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int mb = (M + F8_BM - 1) / F8_BM;
@@ -294,11 +308,11 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         aload[i] = a + (size_t)grow * K + chunk * 16;
         a_off[i] = (wave * 16 + 8 * i) * 8;      // u32x4 units, wave-uniform
     }
-    // weight copies 2..5 of wave w: tiles 2w, 2w+1, two 1 KiB halves each
-    const uint8_t* wload[2];
+    // weight copies 2 .. NCOPY-1 of wave w: tiles NB*w + j, two 1 KiB halves each
+    const uint8_t* wload[NB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int nt = min(nt0 + 2 * wave + j, NT - 1);   // past N: never stored
+    for (int j = 0; j < NB; ++j) {
+        const int nt = min(nt0 + NB * wave + j, NT - 1);  // past N: never stored
         wload[j] = wq + (size_t)nt * KT * 2048 + lane * 16;
     }
     auto copy = [&](Stage& S, int kt, int i) {
@@ -307,19 +321,19 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         } else {
             const int j = (i - 2) >> 1, half = (i - 2) & 1;
             lds_copy_b128(wload[j] + (size_t)kt * 2048 + half * 1024,
-                          S.w + (2 * wave + j) * 128 + half * 64);
+                          S.w + (NB * wave + j) * 128 + half * 64);
         }
     };
 
-    f32x4 total[4][4];
+    f32x4 total[4][NI];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ni = 0; ni < NI; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int ld_kt = 0;
     auto step = [&](auto slot, bool live) {
-        constexpr int P = (NS - 2) * 6;
+        constexpr int P = (NS - 2) * NCOPY;
         __builtin_amdgcn_s_waitcnt((P & 15) | ((P >> 4) << 14) | (7 << 4) | (15 << 8));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -330,30 +344,34 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         ++ld_kt;
         if (!live) {
 #pragma unroll
-            for (int i = 0; i < 6; ++i) copy(Dst, knext, i);
+            for (int i = 0; i < NCOPY; ++i) copy(Dst, knext, i);
             return;
         }
         const Stage& S = stage(slot);
-        i32x8 bfr[4];
+        i32x8 bfr[NI];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int tl = wn * 4 + ni;
+        for (int ni = 0; ni < NI; ++ni) {
+            const int tl = wn * NI + ni;
             bfr[ni] = cat_i32x8(S.w[tl * 128 + lane * 2], S.w[tl * 128 + lane * 2 + 1]);
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             // the next stage's copies go out between the MFMAs
-            if (mi < 2) {
-                copy(Dst, knext, 2 * mi);
-                copy(Dst, knext, 2 * mi + 1);
+            if (NCOPY == 6) {
+                if (mi < 2) {
+                    copy(Dst, knext, 2 * mi);
+                    copy(Dst, knext, 2 * mi + 1);
+                } else {
+                    copy(Dst, knext, mi + 2);
+                }
             } else {
-                copy(Dst, knext, mi + 2);
+                copy(Dst, knext, mi);
             }
             const int r = wm * 64 + mi * 16 + col;
             const int sw8 = (r >> 1) & 7;
             const i32x8 af = cat_i32x8(S.a[r * 8 + (kq ^ sw8)], S.a[r * 8 + ((4 + kq) ^ sw8)]);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) total[mi][ni] = mfma_fp8_16x16x128(af, bfr[ni], total[mi][ni]);
+            for (int ni = 0; ni < NI; ++ni) total[mi][ni] = mfma_fp8_16x16x128(af, bfr[ni], total[mi][ni]);
         }
     };
 
@@ -361,7 +379,7 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         Stage& S = stage(s);
         const int kc = ld_kt < KT ? ld_kt : KT - 1;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) copy(S, kc, i);
+        for (int i = 0; i < NCOPY; ++i) copy(S, kc, i);
         ++ld_kt;
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -369,8 +387,8 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         static_for<NS>([&](auto s) { step(s, kt + decltype(s)::value < KT); });
 
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        const int nt = nt0 + wn * 4 + ni;
+    for (int ni = 0; ni < NI; ++ni) {
+        const int nt = nt0 + wn * NI + ni;
         if (nt >= NT) continue;
         const int n = nt * 16 + col;
         const float swn = sw[n];
@@ -432,9 +450,17 @@ void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w, 
     } else if (M <= 64) {
         launch_small_ct<4>(a, sa, w, sw, y, M, N, K, st);
     } else {
-        const int tiles = ((N + F8_BN - 1) / F8_BN) * ((M + F8_BM - 1) / F8_BM);
-        hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS>), dim3(tiles), dim3(512), 0, st, a, sa, w, sw,
-                           y, M, N, K);
+        // 128-column tiles when 256-column tiles would take fewer, emptier rounds
+        const int mb = (M + F8_BM - 1) / F8_BM;
+        const int cus = f8_cu_count();
+        const int rounds256 = ((N + 255) / 256 * mb + cus - 1) / cus;
+        const int rounds128 = ((N + 127) / 128 * mb + cus - 1) / cus;
+        if (8 * rounds128 < 14 * rounds256)
+            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS, 1>), dim3((N + 127) / 128 * mb), dim3(512), 0,
+                               st, a, sa, w, sw, y, M, N, K);
+        else
+            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS, 2>), dim3((N + 255) / 256 * mb), dim3(512), 0,
+                               st, a, sa, w, sw, y, M, N, K);
     }
 }
 

@@ -561,15 +561,16 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
-// Large M (M > 64): 128 x 256 output tile per workgroup, eight waves in a
-// 2 x 4 grid of 64 x 64, K walked one group (128 rows) at a time through an
-// NS-stage pipeline in LDS.  Stage g % NS holds, for group g:
+// Large M (M > 64): 128 x 128·NB output tile per workgroup (NB = 2, or 1 when
+// 256-column tiles would leave CUs idle), eight waves in a 2 x 4 grid of
+// 64 x 32·NB, K walked one group (128 rows) at a time through an NS-stage
+// pipeline in LDS.  Stage g % NS holds, for group g:
 //   * the activation tile a[m0 : m0+128, 128g : 128g+128] (32 KiB), stored with
 //     a 16-byte XOR swizzle (chunk c of row r at c ^ (r % 16)) so fragment
 //     reads are conflict free;
-//   * the 16 weight tiles of the 256 columns (16 KiB) in their native fragment
-//     order (a wave reads its fragment of a tile with one 128-bit LDS read);
-//   * their bf16 scales (512 B) and the offset terms corr[g][m0 : m0+128].
+//   * the 8·NB weight tiles of the columns in their native fragment order (a
+//     wave reads its fragment of a tile with one 128-bit LDS read);
+//   * their bf16 scales and the offset terms corr[g][m0 : m0+128].
 // Everything is copied with 128-bit direct-to-LDS loads, six per thread per
 // stage (scales and offset terms share one more copy by wave 0), issued NS - 1
 // groups ahead and spread over the previous group's math: a direct-to-LDS copy
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 // copies pace the loop unless they overlap the MFMAs.  A group step waits until at most
 // (NS - 2) stages of copies are outstanding, so this stage has landed, then a
 // barrier publishes it (and frees the stage read one step earlier, which the
-// next copies refill).  A wave's 64 x 64 tile is 2 x 2 blocks of 32 x 32 on
+// next copies refill).  A wave's tile is 2 x NB blocks of 32 x 32 on
 // v_mfma_f32_32x32x16_bf16 (on gfx950 the 16x16x32 form sustains only about
 // half the bf16 rate); per group and 16-k step it unpacks one weight word per
 // 32-column block and reads one A fragment per 32-row block.  Every block's
@@ -592,16 +593,17 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 // XCD's L2 instead of fetching it once per XCD.
 // ---------------------------------------------------------------------------
 constexpr int LM_BM = 128;
-constexpr int LM_BN = 256;
 
-template <int NS>
+template <int NS, int NB>
 __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
     int M, int Mp, int N, int K) {
     constexpr int BM = LM_BM;
-    constexpr int NTB = LM_BN / 16;              // column tiles per workgroup
+    constexpr int NTB = 8 * NB;                  // column tiles per workgroup (NB 32-column blocks per wave)
+    constexpr int NCOPY = 4 + NB;                // copies per thread per stage (wave 0: one more)
     static_assert(NS >= 2 && NS <= 3, "stages");
+    static_assert(NB == 1 || NB == 2, "column blocks per wave");
     // one LDS object per stage: activation tile, weight tiles, scales, offset terms
     struct Stage {
         u32x4 a[BM * 16];
@@ -623,7 +625,7 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2;                    // 0..1: 64-row half
-    const int wn = wave & 3;                     // 0..3: 64-column quarter
+    const int wn = wave & 3;                     // 0..3: column quarter (32 * NB columns)
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int mb = (M + BM - 1) / BM;
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const int m0 = (tile % mb) * BM;
     const int nt0 = (tile / mb) * NTB;           // first column tile
 
-    // copies per thread per stage: 4 activation, 2 weight, 1 scale, 1 offset
+    // copies per thread per stage: 4 activation, NB weight (+1 scale/offset in wave 0)
     // activation: copy i of wave w fills rows 16w + 4i + lane/16 .. (4 rows), slot lane%16
     const u32x4* aload[4];
     int a_off[4];
@@ -643,57 +645,58 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
         aload[i] = reinterpret_cast<const u32x4*>(a + (size_t)grow * K) + chunk;
         a_off[i] = (wave * 16 + 4 * i) * 16;     // u32x4 units, wave-uniform
     }
-    // weights: wave w copies column tiles 2w, 2w+1 (clamped past N: never stored)
-    const u32x4* wload[2];
+    // weights: wave w copies column tiles NB*w .. NB*w + NB-1 (clamped past N: never stored)
+    const u32x4* wload[NB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int nt = min(nt0 + 2 * wave + j, NT - 1);
+    for (int j = 0; j < NB; ++j) {
+        const int nt = min(nt0 + NB * wave + j, NT - 1);
         wload[j] = reinterpret_cast<const u32x4*>(wq) + (size_t)nt * G * 64 + lane;
     }
-    // scales (16 tiles x 32 B) and offset terms (128 floats) are adjacent in a
-    // stage: one 1 KiB copy by wave 0, lanes 0..31 the scale chunks (tile l/2,
-    // half l%2), lanes 32..63 the offset-term chunks (rows 4(l-32) .. +3)
-    const bool sc_lane = lane < 32;
-    const uint16_t* sload = sc + (size_t)min(nt0 + ((lane & 31) >> 1), NT - 1) * G * 16 + (lane & 1) * 8;
-    const float* cload = corr + m0 + (lane & 31) * 4;
+    // scales (NTB tiles x 32 B) and offset terms (128 floats) are adjacent in a
+    // stage: one copy by wave 0, lanes 0 .. 2NTB-1 the scale chunks (tile l/2,
+    // half l%2), the next 32 lanes the offset-term chunks (rows 4i .. 4i+3)
+    const bool sc_lane = lane < 2 * NTB;
+    const bool co_lane = lane < 2 * NTB + 32;
+    const uint16_t* sload = sc + (size_t)min(nt0 + (lane >> 1), NT - 1) * G * 16 + (lane & 1) * 8;
+    const float* cload = corr + m0 + (co_lane && !sc_lane ? lane - 2 * NTB : 0) * 4;
     const char* scload = sc_lane ? reinterpret_cast<const char*>(sload) : reinterpret_cast<const char*>(cload);
     const size_t sc_step = sc_lane ? (size_t)16 * sizeof(uint16_t) : (size_t)Mp * sizeof(float);
 
     int ld_g = 0;
-    // copy i (0..5 in every wave, 6 in wave 0 only) of group gc into stage S
+    // copy i (0 .. NCOPY-1 in every wave, NCOPY in wave 0 only) of group gc into stage S
     auto copy = [&](Stage& S, int gc, int i) {
         if (i < 4) {
             lds_copy_b128(aload[i] + (size_t)gc * 16, S.a + a_off[i]);
-        } else if (i < 6) {
+        } else if (i < NCOPY) {
             const int j = i - 4;
-            lds_copy_b128(wload[j] + (size_t)gc * 64, S.w + (2 * wave + j) * 64);
+            lds_copy_b128(wload[j] + (size_t)gc * 64, S.w + (NB * wave + j) * 64);
         } else if (wave == 0) {
-            lds_copy_b128(scload + (size_t)gc * sc_step, S.s);
+            if (co_lane) lds_copy_b128(scload + (size_t)gc * sc_step, S.s);
         }
     };
     auto load_all = [&](auto slot) {
         Stage& S = stage(slot);
         const int gc = ld_g < G ? ld_g : G - 1;  // past the last group: a stage never read
 #pragma unroll
-        for (int i = 0; i < 7; ++i) copy(S, gc, i);
+        for (int i = 0; i <= NCOPY; ++i) copy(S, gc, i);
         ++ld_g;
     };
 
-    f32x16 total[2][2];                          // [m-block][32-column block]
+    f32x16 total[2][NB];                         // [m-block][32-column block]
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+        for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) total[mi][bb][i] = 0.f;
 
     const Int4Unpacker unpack;
     auto step = [&](auto slot, bool live) {
-        // every step issues 6 copies per thread (7 in wave 0): once at most
-        // (NS - 2) steps' copies are outstanding this stage has landed; the
-        // barrier publishes it to all waves and frees the stage read one step
-        // earlier
-        constexpr int P1 = (NS - 2) * 6, P0 = (NS - 2) * 7;
+        // every step issues NCOPY copies per thread (one more in wave 0): once
+        // at most (NS - 2) steps' copies are outstanding this stage has landed;
+        // the barrier publishes it to all waves and frees the stage read one
+        // step earlier
+        constexpr int P1 = (NS - 2) * NCOPY, P0 = (NS - 2) * (NCOPY + 1);
         if (wave == 0)
             __builtin_amdgcn_s_waitcnt((P0 & 15) | ((P0 >> 4) << 14) | (7 << 4) | (15 << 8));
         else
@@ -707,7 +710,7 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
         ++ld_g;
         if (!live) {
 #pragma unroll
-            for (int i = 0; i < 7; ++i) copy(Dst, gnext, i);
+            for (int i = 0; i <= NCOPY; ++i) copy(Dst, gnext, i);
             return;
         }
         const Stage& S = stage(slot);
@@ -716,11 +719,11 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
         // tile: slot (l%16) + 16h holds rows 32t + 8h + 0..7 (k-step 2t), slot
         // (l%16) + 16(2+h) rows 32t + 16 + 8h + 0..7 (k-step 2t+1), word t each
         const int h = lane >> 5;
-        u32x4 wlo[2], whi[2];
-        float scur[2];
+        u32x4 wlo[NB], whi[NB];
+        float scur[NB];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int tl = wn * 4 + 2 * bb + ((lane & 31) >> 4);
+        for (int bb = 0; bb < NB; ++bb) {
+            const int tl = wn * 2 * NB + 2 * bb + ((lane & 31) >> 4);
             wlo[bb] = S.w[tl * 64 + (lane & 15) + 16 * h];
             whi[bb] = S.w[tl * 64 + (lane & 15) + 16 * h + 32];
             scur[bb] = bf16_to_f32(S.s[tl * 16 + (lane & 15)]);
@@ -739,15 +742,15 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
                 for (int e = 0; e < 4; ++e) cinit[mi][4 * q + e] = c4[e];
             }
         }
-        f32x16 acc[2][2];
+        f32x16 acc[2][NB];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {            // 16-k steps of the group
             // the next stage's copies go out one per k-step, between the MFMAs,
             // so a wave does not stall on the copy queue before its math
-            if (j < 7) copy(Dst, gnext, j);
-            bf16x8 bfr[2], af[2];
+            if (j <= NCOPY) copy(Dst, gnext, j);
+            bf16x8 bfr[NB], af[2];
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
+            for (int bb = 0; bb < NB; ++bb) {
                 const u32x4 wv = (j & 1) ? whi[bb] : wlo[bb];
                 const int t = j >> 1;
                 bfr[bb] = unpack(t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w);
@@ -760,13 +763,13 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-                for (int bb = 0; bb < 2; ++bb)
+                for (int bb = 0; bb < NB; ++bb)
                     acc[mi][bb] = mfma_bf16_32x32x16(af[mi], bfr[bb], j == 0 ? cinit[mi] : acc[mi][bb]);
         }
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
+            for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) total[mi][bb][i] = fmaf(scur[bb], acc[mi][bb][i], total[mi][bb][i]);
     };
@@ -779,8 +782,8 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
         static_for<NS>([&](auto s) { step(s, g + decltype(s)::value < G); });
 
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        const int nt = nt0 + wn * 4 + 2 * bb + ((lane & 31) >> 4);
+    for (int bb = 0; bb < NB; ++bb) {
+        const int nt = nt0 + wn * 2 * NB + 2 * bb + ((lane & 31) >> 4);
         if (nt >= NT) continue;
         const int n = nt * 16 + (lane & 15);
 #pragma unroll
@@ -1052,11 +1055,28 @@ constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple 
 #define QG_LM_NS 3
 #endif
 
+static int large_m_nb(int M, int N) {
+    // One workgroup per CU at a time: a launch takes about ceil(tiles / CUs)
+    // rounds.  A 256-column round takes about 1.75 times a 128-column round
+    // (measured: the wider tile reuses each activation fragment twice), so
+    // 128-column tiles only when 1.75 * rounds256 exceeds rounds128.
+    const int mb = (M + LM_BM - 1) / LM_BM;
+    const int cus = device_cu_count();
+    const int rounds256 = ((N + 255) / 256 * mb + cus - 1) / cus;
+    const int rounds128 = ((N + 127) / 128 * mb + cus - 1) / cus;
+    return 8 * rounds128 < 14 * rounds256 ? 1 : 2;
+}
+
 static void launch_large(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, const float* corr,
                          uint16_t* y, int M, int Mp, int N, int K, hipStream_t s) {
-    const int tiles = ((N + LM_BN - 1) / LM_BN) * ((M + LM_BM - 1) / LM_BM);
-    hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS>), dim3(tiles), dim3(512), 0, s, a, wq, sc,
-                       corr, y, M, Mp, N, K);
+    const int nb = large_m_nb(M, N);
+    const int tiles = ((N + 128 * nb - 1) / (128 * nb)) * ((M + LM_BM - 1) / LM_BM);
+    if (nb == 1)
+        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, 1>), dim3(tiles), dim3(512), 0, s, a, wq, sc,
+                           corr, y, M, Mp, N, K);
+    else
+        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, 2>), dim3(tiles), dim3(512), 0, s, a, wq, sc,
+                           corr, y, M, Mp, N, K);
 }
 
 size_t w4a16_workspace_bytes(int M, int N, int K) {

@@ -811,7 +811,7 @@ static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #define QG_SM_U 2
 #endif
 #ifndef QG_SM_CT2_MIN_TILES   // use 2 column tiles per workgroup from this many tiles
-#define QG_SM_CT2_MIN_TILES 1024
+#define QG_SM_CT2_MIN_TILES 384
 #endif
 #ifndef QG_SM_CT4_MIN_TILES   // use 4 column tiles per workgroup from this many tiles
 #define QG_SM_CT4_MIN_TILES (1 << 30)
@@ -829,13 +829,22 @@ static void launch_small(const uint16_t* a, const uint32_t* wq, const uint16_t* 
                        0, s, a, wq, sc, y, M, N, K);
 }
 
+// column tiles per workgroup of the small-M kernel: more tiles share each
+// wave's activation fragments (their L2 traffic is M/4 times the weights' per
+// tile), fewer tiles give more workgroups
+static int small_ct(int NT) {
+    if (NT % 4 == 0 && NT >= QG_SM_CT4_MIN_TILES) return 4;
+    if (NT % 2 == 0 && NT >= QG_SM_CT2_MIN_TILES) return 2;
+    return 1;
+}
+
 template <int MT>
 static void launch_small_ct(const uint16_t* a, const uint32_t* wq, const uint16_t* sc,
                             uint16_t* y, int M, int N, int K, hipStream_t s) {
-    const int NT = N / 16;
-    if (NT % 4 == 0 && NT >= QG_SM_CT4_MIN_TILES)
+    const int ct = small_ct(N / 16);
+    if (ct == 4)
         launch_small<MT, 4>(a, wq, sc, y, M, N, K, s);
-    else if (NT % 2 == 0 && NT >= QG_SM_CT2_MIN_TILES)
+    else if (ct == 2)
         launch_small<MT, 2>(a, wq, sc, y, M, N, K, s);
     else
         launch_small<MT, 1>(a, wq, sc, y, M, N, K, s);
@@ -1039,8 +1048,7 @@ const char* w4a16_kernel_for(int M, int N, int K) {
     if (decode_cfg(M, N, K).ok) return "w4a16_decode_kernel";
     if (M <= 64) {
         const int NT = N / 16;
-        const int ct = (NT % 4 == 0 && NT >= QG_SM_CT4_MIN_TILES) ? 4
-                     : (NT % 2 == 0 && NT >= QG_SM_CT2_MIN_TILES) ? 2 : 1;
+        const int ct = small_ct(NT);
         static const char* names[3][3] = {
             {"w4a16_small_m_kernel<1, 1>", "w4a16_small_m_kernel<1, 2>", "w4a16_small_m_kernel<1, 4>"},
             {"w4a16_small_m_kernel<2, 1>", "w4a16_small_m_kernel<2, 2>", "w4a16_small_m_kernel<2, 4>"},

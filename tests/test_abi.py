@@ -81,7 +81,12 @@ def test_size_queries(lib):
     assert lib.w4a16_workspace_bytes(4, 4096, 4096) == 0
     assert lib.w4a16_workspace_bytes(32, 4096, 4096) == 0          # M <= 64: in-workgroup split-K
     assert lib.w4a16_workspace_bytes(1024, 4096, 4096) == 32 * 1024 * 4
-    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == 32 * 256 * 4   # rows padded to 256
+    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == 32 * 256 * 4   # offset terms, rows padded to 256
+    # long K: offset terms, then K split 8 ways (32 column tiles of 128 on 256
+    # CUs): 8 fp32 slots of [M, N], then one counter per tile
+    corr = 112 * 256 * 4
+    slots = 8 * 100 * 4096 * 4
+    assert lib.w4a16_workspace_bytes(100, 4096, 14336) == (corr + slots + 255) // 256 * 256 + 32 * 4
     assert lib.w8a8_workspace_bytes(1024, 4096, 4096) == 0
 
 
@@ -112,7 +117,8 @@ def test_w4a16_validation(lib):
     # large M needs the workspace
     assert _gemm(raw, 256, 4096, 4096) == QG_ERR_NULL
     assert _gemm(raw, 256, 4096, 4096, ws=FAKE, wsb=100) == QG_ERR_WORKSPACE
-    assert _gemm(raw, 256, 4096, 4096, ws=FAKE + 4, wsb=1 << 20) == QG_ERR_ALIGN
+    need = lib.w4a16_workspace_bytes(256, 4096, 4096)
+    assert _gemm(raw, 256, 4096, 4096, ws=FAKE + 4, wsb=need) == QG_ERR_ALIGN
 
 
 def test_other_entry_points_validate(lib):

@@ -202,8 +202,9 @@ def test_gemm_llama3_70b_layer_shapes_sampled(ops, B, j, name, K, N):
     assert_close_rms(y[:, cols], q4.gemm_ref(a, codes, s), what=f"70B {name} B={B}")
 
 
-@pytest.mark.parametrize("B", [32, 128, 512, 1024])
-@pytest.mark.parametrize("j,name,K,N", [(0, "qkv", 4096, 6144), (3, "down", 14336, 4096)])
+@pytest.mark.parametrize("B", [32, 48, 64, 128, 512, 1024])
+@pytest.mark.parametrize("j,name,K,N", [(0, "qkv", 4096, 6144), (2, "gate_up", 4096, 28672),
+                                        (3, "down", 14336, 4096)])
 def test_gemm_large_batch_sampled_rows(ops, B, j, name, K, N):
     announce(f"qgemm_w4a16 8B {name} B={B}")
     w = synth.weights(K, N, seed=synth.weight_seed(0, j))
@@ -321,6 +322,34 @@ def test_decode_workspace_counters_reset(ops, M, K, N):
         torch.cuda.synchronize()
         assert int(torch.count_nonzero(lin._ws[nbytes - 4 * n_strips:nbytes])) == 0
         assert_close_rms(y, q4.gemm_ref(a, codes, s), what=f"M={M} K={K} N={N}")
+        if first is None:
+            first = y
+        assert np.array_equal(y, first)
+
+
+# tiles: 128-row x 128-column tiles these shapes use (too few for 256 CUs, so K is split)
+@pytest.mark.parametrize("M,K,N,tiles", [(200, 14336, 4096, 64), (48, 14336, 4096, 32),
+                                          (256, 28672, 8192, 128)])
+def test_large_m_split_counters_reset(ops, M, K, N, tiles):
+    """Large-M shapes whose tiles cannot fill the GPU split K across workgroups
+    and count arrivals per tile (one 32-bit counter each, at the end of the
+    workspace); every call leaves those counters at zero, and repeated calls on
+    one workspace are bit-identical and match the oracle."""
+    announce(f"qgemm_w4a16 large-M split M={M} K={K} N={N}")
+    nbytes = ops.w4a16_workspace_bytes(M, N, K)
+    w = synth.weights(K, N, seed=47)
+    a = synth.activations(M, K, seed=53)
+    codes, s = q4.quantize(w)
+    lin = ops.W4A16Linear(_pack(ops, w))
+    ad = dev_bf16(a)
+    ref = q4.gemm_ref(a, codes, s)
+    first = None
+    for _ in range(3):
+        y = host_bits16(lin(ad))
+        torch.cuda.synchronize()
+        tail = lin._ws[nbytes - 4 * tiles:nbytes]    # the tile counters
+        assert int(torch.count_nonzero(tail)) == 0
+        assert_close_rms(y, ref, what=f"M={M} K={K} N={N}")
         if first is None:
             first = y
         assert np.array_equal(y, first)

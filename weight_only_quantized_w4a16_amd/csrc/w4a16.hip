@@ -598,7 +598,7 @@ template <int NS, int NB>
 __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
-    int M, int Mp, int N, int K) {
+    int M, int Mp, int N, int K, int S, float* __restrict__ part, unsigned* __restrict__ cnt) {
     constexpr int BM = LM_BM;
     constexpr int NTB = 8 * NB;                  // column tiles per workgroup (NB 32-column blocks per wave)
     constexpr int NCOPY = 4 + NB;                // copies per thread per stage (wave 0: one more)
@@ -619,7 +619,6 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
         else return S2x[0];
     };
 
-    const int G = K >> 7;
     const int NT = N >> 4;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -629,7 +628,13 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int mb = (M + BM - 1) / BM;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    // grid = tiles x S K-slices; slice s holds groups [s*G/S, (s+1)*G/S)
+    const int tiles = gridDim.x / S;
+    const int split = blockIdx.x / tiles;
+    const int tile = xcd_tile(blockIdx.x - split * tiles, tiles);
+    const int G = (K >> 7) / S;                  // groups of this slice (host: S divides K/128)
+    const int gb = split * G;                    // first group of the slice
+    const int Gall = K >> 7;
     const int m0 = (tile % mb) * BM;
     const int nt0 = (tile / mb) * NTB;           // first column tile
 
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
         const int r = wave * 16 + 4 * i + (lane >> 4);
         const int chunk = (lane & 15) ^ (r & 15);
         const int grow = min(m0 + r, M - 1);     // rows >= M are never stored
-        aload[i] = reinterpret_cast<const u32x4*>(a + (size_t)grow * K) + chunk;
+        aload[i] = reinterpret_cast<const u32x4*>(a + (size_t)grow * K + (size_t)gb * 128) + chunk;
         a_off[i] = (wave * 16 + 4 * i) * 16;     // u32x4 units, wave-uniform
     }
     // weights: wave w copies column tiles NB*w .. NB*w + NB-1 (clamped past N: never stored)
@@ -650,15 +655,15 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int nt = min(nt0 + NB * wave + j, NT - 1);
-        wload[j] = reinterpret_cast<const u32x4*>(wq) + (size_t)nt * G * 64 + lane;
+        wload[j] = reinterpret_cast<const u32x4*>(wq) + ((size_t)nt * Gall + gb) * 64 + lane;
     }
     // scales (NTB tiles x 32 B) and offset terms (128 floats) are adjacent in a
     // stage: one copy by wave 0, lanes 0 .. 2NTB-1 the scale chunks (tile l/2,
     // half l%2), the next 32 lanes the offset-term chunks (rows 4i .. 4i+3)
     const bool sc_lane = lane < 2 * NTB;
     const bool co_lane = lane < 2 * NTB + 32;
-    const uint16_t* sload = sc + (size_t)min(nt0 + (lane >> 1), NT - 1) * G * 16 + (lane & 1) * 8;
-    const float* cload = corr + m0 + (co_lane && !sc_lane ? lane - 2 * NTB : 0) * 4;
+    const uint16_t* sload = sc + ((size_t)min(nt0 + (lane >> 1), NT - 1) * Gall + gb) * 16 + (lane & 1) * 8;
+    const float* cload = corr + (size_t)gb * Mp + m0 + (co_lane && !sc_lane ? lane - 2 * NTB : 0) * 4;
     const char* scload = sc_lane ? reinterpret_cast<const char*>(sload) : reinterpret_cast<const char*>(cload);
     const size_t sc_step = sc_lane ? (size_t)16 * sizeof(uint16_t) : (size_t)Mp * sizeof(float);
 
@@ -781,6 +786,28 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     for (int g = 0; g < G; g += NS)
         static_for<NS>([&](auto s) { step(s, g + decltype(s)::value < G); });
 
+    if (S == 1) {
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            const int nt = nt0 + wn * 2 * NB + 2 * bb + ((lane & 31) >> 4);
+            if (nt >= NT) continue;
+            const int n = nt * 16 + (lane & 15);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][bb][i]);
+                }
+            }
+        }
+        return;
+    }
+    // K split: this slice's fp32 sums go to its own slot (agent-scope stores:
+    // coherent across the XCDs' L2s without cache maintenance); the workgroup
+    // that completes a tile's count adds the S slots in slice order
+    // (deterministic), stores bf16 and leaves the counter at zero
+    __shared__ int last_flag;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
         const int nt = nt0 + wn * 2 * NB + 2 * bb + ((lane & 31) >> 4);
@@ -791,10 +818,40 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int m = m0 + wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][bb][i]);
+                if (m < M)
+                    __hip_atomic_store(part + ((size_t)split * M + m) * N + n, total[mi][bb][i],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0)
+        last_flag = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (unsigned)(S - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    constexpr int BN = 128 * NB;
+    const int n0 = nt0 * 16;
+    for (int e = tid; e < BM * BN; e += 512) {
+        const int m = m0 + e / BN;
+        const int n = n0 + e % BN;
+        if (m >= M || n >= N) continue;
+        const float* src = part + (size_t)m * N + n;
+        float v = 0.0f;
+        for (int k0 = 0; k0 < S; k0 += 4) {      // four loads in flight, then add in slice order
+            float pv[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                pv[k] = k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * M * N, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v += pv[k];
+        }
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+    }
+    if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -804,6 +861,18 @@ static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 
 // Tuning knobs of the small-M dispatch (compile-time; defaults measured on MI355X).
+#ifndef QG_LM_MIN_M                // rows from which the large-M kernel may run
+#define QG_LM_MIN_M 33
+#endif
+#ifndef QG_LM_MAX_SPLIT            // largest K split of the large-M kernel
+#define QG_LM_MAX_SPLIT 8
+#endif
+#ifndef QG_LM_SPLIT_MIN_G          // split K only from this many groups ...
+#define QG_LM_SPLIT_MIN_G 64
+#endif
+#ifndef QG_LM_SPLIT_MIN_GPS        // ... keeping at least this many per slice
+#define QG_LM_SPLIT_MIN_GPS 14
+#endif
 #ifndef QG_SM_NWAVE
 #define QG_SM_NWAVE 8
 #endif
@@ -1043,20 +1112,6 @@ static void launch_decode(const uint16_t* a, const uint32_t* wq, const uint16_t*
     }
 }
 
-const char* w4a16_kernel_for(int M, int N, int K) {
-    if (M == 0) return "none";
-    if (decode_cfg(M, N, K).ok) return "w4a16_decode_kernel";
-    if (M <= 64) {
-        const int NT = N / 16;
-        const int ct = small_ct(NT);
-        static const char* names[3][3] = {
-            {"w4a16_small_m_kernel<1, 1>", "w4a16_small_m_kernel<1, 2>", "w4a16_small_m_kernel<1, 4>"},
-            {"w4a16_small_m_kernel<2, 1>", "w4a16_small_m_kernel<2, 2>", "w4a16_small_m_kernel<2, 4>"},
-            {"w4a16_small_m_kernel<4, 1>", "w4a16_small_m_kernel<4, 2>", "w4a16_small_m_kernel<4, 4>"}};
-        return names[M <= 16 ? 0 : M <= 32 ? 1 : 2][ct == 1 ? 0 : ct == 2 ? 1 : 2];
-    }
-    return "w4a16_large_m_kernel";
-}
 
 constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple of this
 #ifndef QG_LM_NS                   // pipeline stages of the large-M kernel
@@ -1075,22 +1130,86 @@ static int large_m_nb(int M, int N) {
     return 8 * rounds128 < 14 * rounds256 ? 1 : 2;
 }
 
-static void launch_large(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, const float* corr,
-                         uint16_t* y, int M, int Mp, int N, int K, hipStream_t s) {
-    const int nb = large_m_nb(M, N);
-    const int tiles = ((N + 128 * nb - 1) / (128 * nb)) * ((M + LM_BM - 1) / LM_BM);
-    if (nb == 1)
-        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, 1>), dim3(tiles), dim3(512), 0, s, a, wq, sc,
-                           corr, y, M, Mp, N, K);
+// Large-M plan: tile width, K split and workspace layout (corr | slots | counters),
+// a function of the shape and the device's CU count only.
+struct LargePlan {
+    int nb, S, tiles, Mp;
+    size_t corr_off, part_off, cnt_off, bytes;
+};
+
+static LargePlan large_plan(int M, int N, int K) {
+    LargePlan p{};
+    const int G = K / 128;
+    p.nb = large_m_nb(M, N);
+    p.tiles = ((N + 128 * p.nb - 1) / (128 * p.nb)) * ((M + LM_BM - 1) / LM_BM);
+    p.Mp = round_up(M, LM_MAX_BM);
+    p.S = 1;
+    const int cus = device_cu_count();
+    // split long K (measured: with 32 groups the shorter slices and the partial
+    // sums cost more than the idle CUs) until the grid fills the CUs, keeping
+    // at least QG_LM_SPLIT_MIN_GPS groups per slice
+    if (p.tiles < cus && G >= QG_LM_SPLIT_MIN_G) {
+        int best = 1;
+        for (int d = 2; d <= QG_LM_MAX_SPLIT && G / d >= QG_LM_SPLIT_MIN_GPS; ++d) {
+            if (G % d) continue;
+            best = d;
+            if ((long long)p.tiles * d >= cus) break;
+        }
+        p.S = best;
+    }
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    p.corr_off = 0;
+    p.part_off = al((size_t)G * p.Mp * sizeof(float));
+    p.cnt_off = al(p.part_off + (p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0));
+    p.bytes = p.cnt_off + (p.S > 1 ? (size_t)p.tiles * sizeof(unsigned) : 0);
+    return p;
+}
+
+// 33..64 rows: the large-M kernel when its grid (with the K split) covers most
+// CUs, else the in-workgroup split-K kernel (measured: wide gate_up and long-K
+// down gain, narrow short-K qkv and o lose)
+static bool use_large_m(int M, int N, int K) {
+    if (M > 64) return true;
+    if (M < QG_LM_MIN_M) return false;
+    const LargePlan p = large_plan(M, N, K);
+    return 4LL * p.tiles * p.S >= 3LL * device_cu_count();
+}
+
+static void launch_large(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, void* ws,
+                         uint16_t* y, int M, int N, int K, hipStream_t s) {
+    const LargePlan p = large_plan(M, N, K);
+    char* w = static_cast<char*>(ws);
+    const float* corr = reinterpret_cast<const float*>(w + p.corr_off);
+    float* part = p.S > 1 ? reinterpret_cast<float*>(w + p.part_off) : nullptr;
+    unsigned* cnt = p.S > 1 ? reinterpret_cast<unsigned*>(w + p.cnt_off) : nullptr;
+    const dim3 grid((unsigned)(p.tiles * p.S));
+    if (p.nb == 1)
+        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, 1>), grid, dim3(512), 0, s, a, wq, sc, corr, y,
+                           M, p.Mp, N, K, p.S, part, cnt);
     else
-        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, 2>), dim3(tiles), dim3(512), 0, s, a, wq, sc,
-                           corr, y, M, Mp, N, K);
+        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, 2>), grid, dim3(512), 0, s, a, wq, sc, corr, y,
+                           M, p.Mp, N, K, p.S, part, cnt);
+}
+
+const char* w4a16_kernel_for(int M, int N, int K) {
+    if (M == 0) return "none";
+    if (decode_cfg(M, N, K).ok) return "w4a16_decode_kernel";
+    if (M <= 64 && !use_large_m(M, N, K)) {
+        const int NT = N / 16;
+        const int ct = small_ct(NT);
+        static const char* names[3][3] = {
+            {"w4a16_small_m_kernel<1, 1>", "w4a16_small_m_kernel<1, 2>", "w4a16_small_m_kernel<1, 4>"},
+            {"w4a16_small_m_kernel<2, 1>", "w4a16_small_m_kernel<2, 2>", "w4a16_small_m_kernel<2, 4>"},
+            {"w4a16_small_m_kernel<4, 1>", "w4a16_small_m_kernel<4, 2>", "w4a16_small_m_kernel<4, 4>"}};
+        return names[M <= 16 ? 0 : M <= 32 ? 1 : 2][ct == 1 ? 0 : ct == 2 ? 1 : 2];
+    }
+    return "w4a16_large_m_kernel";
 }
 
 size_t w4a16_workspace_bytes(int M, int N, int K) {
     if (M <= 16) return decode_ws_bytes(decode_cfg(M, N, K), N);
-    if (M <= 64) return 0;
-    return (size_t)(K / 128) * (size_t)round_up(M, LM_MAX_BM) * sizeof(float);
+    if (!use_large_m(M, N, K)) return 0;
+    return large_plan(M, N, K).bytes;
 }
 
 void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
@@ -1100,9 +1219,9 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
         launch_decode(a, packed, scales, y, M, N, K, dc, ws, s);
     } else if (M <= 16) {
         launch_small_ct<1>(a, packed, scales, y, M, N, K, s);
-    } else if (M <= 32) {
+    } else if (!use_large_m(M, N, K) && M <= 32) {
         launch_small_ct<2>(a, packed, scales, y, M, N, K, s);
-    } else if (M <= 64) {
+    } else if (!use_large_m(M, N, K)) {
         launch_small_ct<4>(a, packed, scales, y, M, N, K, s);
     } else {
         const int Mp = round_up(M, LM_MAX_BM);
@@ -1111,7 +1230,7 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
         const size_t n = (size_t)G * Mp;
         hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
                            0, s, a, M, Mp, K, corr);
-        launch_large(a, packed, scales, corr, y, M, Mp, N, K, s);
+        launch_large(a, packed, scales, ws, y, M, N, K, s);
     }
 }
 

@@ -101,8 +101,9 @@ class Stack:
             if fp8:
                 rec["qa"] = torch.empty((maxb, K), dtype=torch.uint8, device=dev)
                 rec["sa"] = torch.empty(maxb, dtype=torch.float32, device=dev)
-            else:
-                ws, _ = lin.workspace(maxb)      # allocate the largest workspace up front
+            # allocate the largest workspace up front
+            for b in batches:
+                lin.workspace(b)
             self.layers.append(rec)
         torch.cuda.synchronize()
 
@@ -115,8 +116,9 @@ class Stack:
             y = r["y"][:B]
             if self.fp8:
                 ops.quant_act_per_token(a, B, r["K"], r["qa"][:B], r["sa"][:B])
+                ws, nb = r["lin"].workspace(B)
                 ops.qgemm_w8a8_fp8(r["qa"][:B], r["sa"][:B], r["w"].codes, r["w"].scales, y,
-                                   B, r["N"], r["K"])
+                                   B, r["N"], r["K"], ws, nb)
             else:
                 ws, nb = r["lin"].workspace(B)
                 ops.qgemm_w4a16(a, r["w"].packed, r["w"].scales, y, B, r["N"], r["K"], ws, nb)

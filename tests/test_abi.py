@@ -88,6 +88,11 @@ def test_size_queries(lib):
     slots = 8 * 100 * 4096 * 4
     assert lib.w4a16_workspace_bytes(100, 4096, 14336) == (corr + slots + 255) // 256 * 256 + 32 * 4
     assert lib.w8a8_workspace_bytes(1024, 4096, 4096) == 0
+    assert lib.w8a8_workspace_bytes(64, 4096, 14336) == 0             # small M: no split
+    assert lib.w8a8_workspace_bytes(1024, 4096, 14336) == 0           # 256 tiles fill the CUs
+    # 64 tiles of 128 x 128, 112 k-tiles split 4 ways: 4 fp32 slots of [M, N],
+    # then one counter per tile
+    assert lib.w8a8_workspace_bytes(200, 4096, 14336) == (4 * 200 * 4096 * 4 + 255) // 256 * 256 + 64 * 4
 
 
 FAKE = 0x100000          # 16-byte aligned, never dereferenced (validation fails first)

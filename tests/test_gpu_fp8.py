@@ -140,3 +140,34 @@ def test_fp8_deterministic(ops, M):
     y1 = host_bits16(lin(a))
     y2 = host_bits16(lin(a))
     assert np.array_equal(y1, y2)
+
+
+# (M, K, N, tiles, S): shapes whose 128 x 128 tiles cannot fill 256 CUs, so K
+# is split S ways; N = 1040 leaves a ragged last column tile, S = 5 a partial
+# group of four slots in the final reduction
+@pytest.mark.parametrize("M,K,N,tiles,S", [(200, 14336, 4096, 64, 4), (100, 14336, 1040, 9, 8),
+                                            (100, 10240, 1040, 9, 5), (300, 14336, 4096, 96, 4)])
+def test_fp8_large_m_split_counters_reset(ops, M, K, N, tiles, S):
+    """The K split writes unscaled fp32 slots and counts arrivals per tile (one
+    32-bit counter each, after the slots); the last arriver applies the scales.
+    Every call leaves the counters at zero; repeated calls on one workspace are
+    bit-identical and match the oracle."""
+    announce(f"qgemm_w8a8_fp8 large-M split M={M} K={K} N={N}")
+    nbytes = ops.w8a8_workspace_bytes(M, N, K)
+    assert nbytes == (S * M * N * 4 + 255) // 256 * 256 + 4 * tiles
+    w = synth.weights(K, N, seed=83)
+    a = synth.activations(M, K, seed=89)
+    qa, sa = f8.quant_act_per_token(a)
+    qw, sw = f8.quant_weight_per_channel(w)
+    ref = f8.gemm_ref(qa, sa, qw, sw)
+    lin = ops.W8A8Fp8Linear(ops.Fp8Weight.from_bf16(dev_bf16(w)))
+    ad = dev_bf16(a)
+    first = None
+    for _ in range(3):
+        y = host_bits16(lin(ad))
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(lin._ws[nbytes - 4 * tiles:nbytes])) == 0
+        assert_close_rms(y, ref, what=f"fp8 split M={M} K={K} N={N}")
+        if first is None:
+            first = y
+        assert np.array_equal(y, first)

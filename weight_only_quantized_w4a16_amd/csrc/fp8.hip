@@ -235,7 +235,8 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 // Large M (M > 64): 128 x 128·NB output tile per workgroup (NB = 2, or 1 when
 // 256-column tiles would leave CUs idle), eight waves in a 2 x 4 grid of
 // 64 x 32·NB (4 x 2NB MFMA tiles of 16x16x128 e4m3), K walked one
-// 128-row k-tile at a time through an NS-stage pipeline in LDS.  Stage
+// 128-row k-tile at a time through an NS-stage pipeline in LDS (three stages
+// of 48 KiB with 256-column tiles, four of 32 KiB with 128-column tiles).  Stage
 // kt % NS holds, for k-tile kt, the activation tile (128 rows x 128 bytes,
 // 16-byte chunk c of row r at c ^ ((r / 2) % 8): two 128-byte rows share one
 // pass over the 64 banks) and the 8·NB weight tiles of the columns in their
@@ -245,6 +246,12 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 // most (NS - 2) steps of copies are outstanding (so its stage has landed),
 // then a barrier publishes the stage and frees the one read a step earlier.
 // The fp32 totals are scaled by s_a[m] * s_w[n] once, in the epilogue.
+//
+// When the tiles alone cannot fill the CUs and K is long, the grid holds S
+// copies of the tiles and copy s walks the s-th of S equal runs of k-tiles.
+// Each writes its unscaled fp32 totals to its own slot of `part`; the
+// workgroup that completes a tile's counter adds the S slots in slice order
+// (deterministic), applies the scales, stores bf16 and resets the counter.
 // ---------------------------------------------------------------------------
 constexpr int F8_BM = 128;
 
@@ -258,32 +265,38 @@ static int f8_cu_count() {
     }();
     return cus;
 }
-#ifndef QG_F8_NS
+#ifndef QG_F8_NS                   // stages with 256-column tiles (48 KiB each)
 #define QG_F8_NS 3
+#endif
+#ifndef QG_F8_NS1                  // stages with 128-column tiles (32 KiB each)
+#define QG_F8_NS1 4
 #endif
 
 template <int NS, int NB>
 __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
-    const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
+    const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K, int S,
+    float* __restrict__ part, unsigned* __restrict__ cnt) {
     constexpr int NTB = 8 * NB;                  // column tiles per workgroup
     constexpr int NI = 2 * NB;                   // column tiles per wave
     constexpr int NCOPY = 2 + 2 * NB;            // copies per thread per stage
-    static_assert(NS >= 2 && NS <= 3, "stages");
+    static_assert(NS >= 2 && NS <= 4, "stages");
     static_assert(NB == 1 || NB == 2, "column blocks");
     struct Stage {
         u32x4 a[F8_BM * 8];                      // 16 KiB
         u32x4 w[NTB * 128];                      // 32 KiB
     };
-    __shared__ __attribute__((aligned(16))) Stage S0, S1, S2x[1];
+    __shared__ __attribute__((aligned(16))) Stage S0, S1, S2x[1], S3x[1];   // unused stages are dropped
     auto stage = [&](auto st) -> Stage& {
         constexpr int v = decltype(st)::value;
         if constexpr (v == 0) return S0;
         else if constexpr (v == 1) return S1;
-        else return S2x[0];
+        else if constexpr (v == 2) return S2x[0];
+        else return S3x[0];
     };
 
-    const int KT = K >> 7;
+    const int KT_all = K >> 7;
+    const int KT = KT_all / S;                   // k-tiles of this slice (host: S divides KT_all)
     const int NT = N >> 4;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -293,7 +306,10 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int mb = (M + F8_BM - 1) / F8_BM;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int tiles = gridDim.x / S;
+    const int split = blockIdx.x / tiles;
+    const int tile = xcd_tile(blockIdx.x - split * tiles, tiles);
+    const int kb = split * KT;                   // first k-tile of the slice
     const int m0 = (tile % mb) * F8_BM;
     const int nt0 = (tile / mb) * NTB;
 
@@ -305,7 +321,7 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         const int r = wave * 16 + 8 * i + (lane >> 3);
         const int chunk = (lane & 7) ^ ((r >> 1) & 7);
         const int grow = min(m0 + r, M - 1);     // rows >= M are never stored
-        aload[i] = a + (size_t)grow * K + chunk * 16;
+        aload[i] = a + (size_t)grow * K + (size_t)kb * 128 + chunk * 16;
         a_off[i] = (wave * 16 + 8 * i) * 8;      // u32x4 units, wave-uniform
     }
     // weight copies 2 .. NCOPY-1 of wave w: tiles NB*w + j, two 1 KiB halves each
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int nt = min(nt0 + NB * wave + j, NT - 1);  // past N: never stored
-        wload[j] = wq + (size_t)nt * KT * 2048 + lane * 16;
+        wload[j] = wq + ((size_t)nt * KT_all + kb) * 2048 + lane * 16;
     }
     auto copy = [&](Stage& S, int kt, int i) {
         if (i < 2) {
@@ -386,21 +402,72 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     for (int kt = 0; kt < KT; kt += NS)
         static_for<NS>([&](auto s) { step(s, kt + decltype(s)::value < KT); });
 
+    if (S == 1) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            const int nt = nt0 + wn * NI + ni;
+            if (nt >= NT) continue;
+            const int n = nt * 16 + col;
+            const float swn = sw[n];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + wm * 64 + mi * 16 + 4 * kq + i;
+                    if (m < M)
+                        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i] * sa[m] * swn);
+                }
+            }
+        }
+        return;
+    }
+    // K split: unscaled fp32 totals to this slice's slot with agent-scope
+    // stores (coherent across the XCDs' L2s without cache maintenance)
+    __shared__ int last_flag;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
         const int nt = nt0 + wn * NI + ni;
         if (nt >= NT) continue;
         const int n = nt * 16 + col;
-        const float swn = sw[n];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = m0 + wm * 64 + mi * 16 + 4 * kq + i;
-                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i] * sa[m] * swn);
+                if (m < M)
+                    __hip_atomic_store(part + ((size_t)split * M + m) * N + n, total[mi][ni][i],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0)
+        last_flag = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (unsigned)(S - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    constexpr int BN = 128 * NB;
+    const int n0 = nt0 * 16;
+    for (int e = tid; e < F8_BM * BN; e += 512) {
+        const int m = m0 + e / BN;
+        const int n = n0 + e % BN;
+        if (m >= M || n >= N) continue;
+        const float* src = part + (size_t)m * N + n;
+        float v = 0.0f;
+        for (int k0 = 0; k0 < S; k0 += 4) {      // four loads in flight, then add in slice order
+            float pv[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                pv[k] = k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * M * N, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v += pv[k];
+        }
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v * sa[m] * sw[n]);
+    }
+    if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 const char* w8a8_kernel_for(int M, int N, int K) {
@@ -416,9 +483,51 @@ const char* w8a8_kernel_for(int M, int N, int K) {
     return names[M <= 16 ? 0 : M <= 32 ? 1 : 2][ct == 1 ? 0 : 1];
 }
 
+// Large-M plan: tile width, K split and workspace layout (slots | counters).
+#ifndef QG_F8_MAX_SPLIT            // largest K split of the large-M kernel
+#define QG_F8_MAX_SPLIT 8
+#endif
+#ifndef QG_F8_SPLIT_MIN_KT         // split K only from this many k-tiles ...
+#define QG_F8_SPLIT_MIN_KT 64
+#endif
+#ifndef QG_F8_SPLIT_MIN_KPS        // ... keeping at least this many per slice
+#define QG_F8_SPLIT_MIN_KPS 14
+#endif
+struct F8Plan {
+    int nb, S, tiles;
+    size_t cnt_off, bytes;
+};
+
+static F8Plan f8_plan(int M, int N, int K) {
+    F8Plan p{};
+    const int KT = K / 128;
+    const int mb = (M + F8_BM - 1) / F8_BM;
+    const int cus = f8_cu_count();
+    // 128-column tiles when 256-column tiles would take fewer, emptier rounds
+    const int rounds256 = ((N + 255) / 256 * mb + cus - 1) / cus;
+    const int rounds128 = ((N + 127) / 128 * mb + cus - 1) / cus;
+    p.nb = 8 * rounds128 < 14 * rounds256 ? 1 : 2;
+    p.tiles = (N + 128 * p.nb - 1) / (128 * p.nb) * mb;
+    p.S = 1;
+    if (p.tiles < cus && KT >= QG_F8_SPLIT_MIN_KT) {
+        int best = 1;
+        for (int d = 2; d <= QG_F8_MAX_SPLIT && KT / d >= QG_F8_SPLIT_MIN_KPS; ++d) {
+            if (KT % d) continue;
+            best = d;
+            if ((long long)p.tiles * d >= cus) break;
+        }
+        p.S = best;
+    }
+    if (p.S > 1) {
+        p.cnt_off = ((size_t)p.S * M * N * sizeof(float) + 255) / 256 * 256;
+        p.bytes = p.cnt_off + (size_t)p.tiles * sizeof(unsigned);
+    }
+    return p;
+}
+
 size_t w8a8_workspace_bytes(int M, int N, int K) {
-    (void)M; (void)N; (void)K;
-    return 0;
+    if (M <= 64) return 0;
+    return f8_plan(M, N, K).bytes;
 }
 
 template <int MT, int CT>
@@ -442,7 +551,6 @@ static void launch_small_ct(const uint8_t* a, const float* sa, const uint8_t* w,
 
 void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                            uint16_t* y, int M, int N, int K, void* ws, hipStream_t st) {
-    (void)ws;
     if (M <= 16) {
         launch_small_ct<1>(a, sa, w, sw, y, M, N, K, st);
     } else if (M <= 32) {
@@ -450,17 +558,17 @@ void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w, 
     } else if (M <= 64) {
         launch_small_ct<4>(a, sa, w, sw, y, M, N, K, st);
     } else {
-        // 128-column tiles when 256-column tiles would take fewer, emptier rounds
-        const int mb = (M + F8_BM - 1) / F8_BM;
-        const int cus = f8_cu_count();
-        const int rounds256 = ((N + 255) / 256 * mb + cus - 1) / cus;
-        const int rounds128 = ((N + 127) / 128 * mb + cus - 1) / cus;
-        if (8 * rounds128 < 14 * rounds256)
-            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS, 1>), dim3((N + 127) / 128 * mb), dim3(512), 0,
-                               st, a, sa, w, sw, y, M, N, K);
+        const F8Plan p = f8_plan(M, N, K);
+        char* wsb = static_cast<char*>(ws);
+        float* part = p.S > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+        unsigned* cnt = p.S > 1 ? reinterpret_cast<unsigned*>(wsb + p.cnt_off) : nullptr;
+        const dim3 grid((unsigned)(p.tiles * p.S));
+        if (p.nb == 1)
+            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS1, 1>), grid, dim3(512), 0, st, a, sa, w, sw, y,
+                               M, N, K, p.S, part, cnt);
         else
-            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS, 2>), dim3((N + 255) / 256 * mb), dim3(512), 0,
-                               st, a, sa, w, sw, y, M, N, K);
+            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS, 2>), grid, dim3(512), 0, st, a, sa, w, sw, y,
+                               M, N, K, p.S, part, cnt);
     }
 }
 

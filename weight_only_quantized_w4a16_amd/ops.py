@@ -242,18 +242,22 @@ class W8A8Fp8Linear:
         self.w = weight
         self._ws = None
 
+    def workspace(self, M):
+        need = w8a8_workspace_bytes(M, self.w.N, self.w.K)
+        if need and (self._ws is None or self._ws.numel() < need):
+            # zero-filled once; every call resets the counters it uses
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.w.codes.device)
+        return (self._ws, need) if need else (None, 0)
+
     def __call__(self, a, out=None, stream=None, qa=None, sa=None):
         M, K = a.shape
+        if K != self.w.K:
+            raise ValueError(f"activation K={K} != weight K={self.w.K}")
         if qa is None:
             qa, sa = quantize_activations(a, stream)
         y = out if out is not None else torch.empty((M, self.w.N), dtype=torch.bfloat16,
                                                     device=a.device)
-        need = w8a8_workspace_bytes(M, self.w.N, K)
-        ws = None
-        if need:
-            if self._ws is None or self._ws.numel() < need:
-                self._ws = torch.empty(need, dtype=torch.uint8, device=a.device)
-            ws = self._ws
+        ws, need = self.workspace(M)
         qgemm_w8a8_fp8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
         return y
 

@@ -90,6 +90,81 @@ def quantize(w_bits):
     return codes, s_bits
 
 
+def quantize_mse(w_bits, n_alpha=100):
+    """INT4 g128 quantization with MSE-optimal clipping, searched on a grid.
+
+    "Give Me BF16 or Give Me Death", section 3.4, "W4A16-INT", paragraphs on
+    MSE-optimal clipping: per group of 128 weights, instead of the abs-max
+    range the clipping threshold is alpha * max|x| with alpha in (0, 1], the
+    scale is that threshold over 7, weights beyond the threshold saturate at
+    the largest code, and alpha minimizes the group's summed squared error
+    sum_i (x_i - Q_alpha(x_i))^2, found by a grid search over the scalar.
+
+    Readings where the page is silent (listed with the design notes):
+    M1  The grid is alpha_i = i / n_alpha, i = 1 .. n_alpha (default 100
+        uniform steps); among equal errors the larger alpha wins.
+    M2  The candidate scale is bf16_rne(float32(amax * i) / float32(7 * n_alpha)):
+        amax * i is exact in fp32 (an 8-bit bf16 mantissa times an integer
+        below 2^16) and the division is one IEEE fp32 quotient, so i = n_alpha
+        reproduces the abs-max scale of quantize() exactly.
+    M3  Codes are clamp(rne(x / s), -7, 7) with the IEEE fp32 quotient (the
+        page's symmetric range; saturation is the clipping), scale 0 gives
+        code 0; stored code = code + 8.
+    M4  The error is evaluated in fp64: d = x - q * s (exact), then the 128
+        squares d * d are each rounded to fp64 and added in row order, one
+        rounding per addition.
+
+    w_bits: uint16 bf16 patterns [K, N].  Returns (codes uint8 [K, N],
+    scale_bits uint16 [K/128, N]) like quantize().
+    """
+    if not 1 <= n_alpha <= 65535:
+        raise ValueError(f"n_alpha={n_alpha} outside [1, 65535]")
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    K, N = w_bits.shape
+    _check_shape(K, N, need_tile=False)
+    G = K // GROUP
+    w = bf16_bits_to_f32(w_bits).reshape(G, GROUP, N)
+    w64 = w.astype(np.float64)
+    amax = np.max(np.abs(w), axis=1)                            # [G, N] fp32, exact
+
+    def codes_for(s):
+        zero = s == 0
+        s_safe = np.where(zero, np.float32(1.0), s)
+        with np.errstate(over="ignore", invalid="ignore"):
+            q = np.rint(w / s_safe[:, None, :])                 # fp32 quotient, then half-even
+        q = np.clip(q, -7, 7)                                   # saturate beyond the threshold
+        return np.where(zero[:, None, :], 0.0, q)
+
+    best_err = np.full((G, N), np.inf)
+    best_bits = np.zeros((G, N), dtype=np.uint16)
+    for i in range(1, n_alpha + 1):
+        with np.errstate(over="ignore"):
+            t = amax * np.float32(i)                             # exact (reading M2)
+            s_bits = f32_to_bf16_bits(t / np.float32(7 * n_alpha))
+        s = bf16_bits_to_f32(s_bits)
+        q = codes_for(s).astype(np.float64)
+        s64 = s.astype(np.float64)
+        err = np.zeros((G, N))
+        with np.errstate(invalid="ignore", over="ignore"):
+            for j in range(GROUP):                              # row order (reading M4)
+                d = w64[:, j, :] - q[:, j, :] * s64
+                err = err + d * d
+        take = err <= best_err                                  # ties: the larger alpha
+        best_err = np.where(take, err, best_err)
+        best_bits = np.where(take, s_bits, best_bits)
+    q = codes_for(bf16_bits_to_f32(best_bits))
+    codes = (q.astype(np.int16) + OFFSET).astype(np.uint8).reshape(K, N)
+    return codes, best_bits
+
+
+def group_sq_error(w_bits, codes, scale_bits):
+    """sum over each group of (x - (code - 8) * s)^2 in fp64, [K/128, N]."""
+    K, N = codes.shape
+    x = bf16_bits_to_f32(w_bits).astype(np.float64)
+    d = x - dequant_f32(codes, scale_bits).astype(np.float64)
+    return (d * d).reshape(K // GROUP, GROUP, N).sum(axis=1)
+
+
 def dequant_f32(codes, scale_bits):
     """w_hat = (code - 8) * s in fp32.  Exact: at most 4 + 8 significant bits."""
     codes = np.asarray(codes, dtype=np.uint8)

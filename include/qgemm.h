@@ -118,6 +118,29 @@ qg_status pack_int4_g128(const uint16_t *w_bf16, int K, int N,
                          uint32_t *packed, uint16_t *scales, qg_stream stream);
 
 /*
+ * pack_int4_g128_mse -- offline INT4 g128 quantization with MSE-optimal
+ * clipping, written in the same native order as pack_int4_g128.
+ * [P2 3.4 "W4A16-INT", MSE-optimal clipping: per group the threshold
+ *  alpha * max|x|, alpha in (0, 1], that minimizes the summed squared error,
+ *  found by grid search; weights beyond it saturate; s = threshold / 7.]
+ *
+ *   w_bf16   in   [K, N] bf16 weights.
+ *   n_alpha  in   grid size: alpha = i / n_alpha, i = 1 .. n_alpha
+ *                 (1 <= n_alpha <= 65535; 1 gives the abs-max result).
+ *   packed   out  as pack_int4_g128.
+ *   scales   out  as pack_int4_g128.
+ *
+ * Per group g and column n, candidate i has s_i = bf16_rne(float(amax * i) /
+ * float(7 * n_alpha)), codes q = clamp(rne(w / s_i), -7, 7) (IEEE fp32
+ * quotient; s_i == 0 gives q = 0) and error E_i = sum over the group's rows,
+ * in row order, of the fp64 square of w - q * s_i, each square and each
+ * partial sum rounded to fp64.  The smallest E_i wins, ties to the larger i;
+ * stored code = q + 8.  Cost: n_alpha * 128 fp32 divisions per group.
+ */
+qg_status pack_int4_g128_mse(const uint16_t *w_bf16, int K, int N, int n_alpha,
+                             uint32_t *packed, uint16_t *scales, qg_stream stream);
+
+/*
  * dequant_int4_g128 -- reconstruct the bf16 weights from the native buffers
  * with the same device unpack code the GEMM uses (test / debug export).
  * [P2 3.4 "Inference with W4A16": w_hat = s_g * w_int4; P1 "Counting c": the

@@ -135,6 +135,13 @@ def test_other_entry_points_validate(lib):
     assert pack(FAKE, 100, 16, FAKE, FAKE, None) == QG_ERR_SHAPE
     assert pack(FAKE, 128, 8, FAKE, FAKE, None) == QG_ERR_SHAPE
     assert pack(FAKE + 4, 128, 16, FAKE, FAKE, None) == QG_ERR_ALIGN
+    pm = raw.pack_int4_g128_mse
+    pm.restype, pm.argtypes = I, [V, I, I, I, V, V, V]
+    assert pm(FAKE, 128, 16, 0, FAKE, FAKE, None) == QG_ERR_SHAPE      # empty grid
+    assert pm(FAKE, 128, 16, 65536, FAKE, FAKE, None) == QG_ERR_SHAPE  # grid beyond 2^16 - 1
+    assert pm(FAKE, 100, 16, 100, FAKE, FAKE, None) == QG_ERR_SHAPE
+    assert pm(None, 128, 16, 100, FAKE, FAKE, None) == QG_ERR_NULL
+    assert pm(FAKE, 128, 16, 100, FAKE + 4, FAKE, None) == QG_ERR_ALIGN
     deq = raw.dequant_int4_g128
     deq.restype, deq.argtypes = I, [V, V, I, I, V, V, V]
     assert deq(FAKE, FAKE, 128, 16, None, None, None) == QG_ERR_NULL

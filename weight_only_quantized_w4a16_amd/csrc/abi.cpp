@@ -88,6 +88,15 @@ qg_status pack_int4_g128(const uint16_t* w_bf16, int K, int N, uint32_t* packed,
     return launched();
 }
 
+qg_status pack_int4_g128_mse(const uint16_t* w_bf16, int K, int N, int n_alpha, uint32_t* packed,
+                             uint16_t* scales, qg_stream stream) {
+    if (!w_bf16 || !packed || !scales) return QG_ERR_NULL;
+    if (!shape_ok(0, N, K) || n_alpha < 1 || n_alpha > 65535) return QG_ERR_SHAPE;
+    if (!aligned(w_bf16, 16) || !aligned(packed, 16) || !aligned(scales, 4)) return QG_ERR_ALIGN;
+    qg::launch_pack_int4_g128_mse(w_bf16, K, N, n_alpha, packed, scales, as_stream(stream));
+    return launched();
+}
+
 qg_status dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, int K, int N,
                             uint16_t* w_bf16_out, uint8_t* codes_out, qg_stream stream) {
     if (!packed || !scales || !w_bf16_out) return QG_ERR_NULL;

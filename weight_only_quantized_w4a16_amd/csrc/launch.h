@@ -11,6 +11,8 @@ namespace qg {
 // W4A16 path (w4a16.hip)
 void launch_pack_int4_g128(const uint16_t* w, int K, int N, uint32_t* packed,
                            uint16_t* scales, hipStream_t s);
+void launch_pack_int4_g128_mse(const uint16_t* w, int K, int N, int n_alpha, uint32_t* packed,
+                               uint16_t* scales, hipStream_t s);
 void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, int K,
                               int N, uint16_t* w_out, uint8_t* codes_out, hipStream_t s);
 size_t w4a16_workspace_bytes(int M, int N, int K);

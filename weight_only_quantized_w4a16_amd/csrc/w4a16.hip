@@ -25,7 +25,12 @@ namespace qg {
 // owns column 16*nt + l%16 and, for each of the four MFMA k-steps t, the 8 rows
 // 32*t + 8*(l/16) .. +7 of the group: exactly the lane's 16-byte slot of the
 // native tile (word t of the slot feeds k-step t).
+//
+// GIVEN: the scales are already in `scales` (native order, from the clipping
+// search below); codes saturate at +-7, the largest symmetric code.  Without
+// it the scale is the abs-max one, for which |w / s| never exceeds 7.02.
 // ---------------------------------------------------------------------------
+template <bool GIVEN>
 __global__ __launch_bounds__(64) void pack_int4_g128_kernel(
     const uint16_t* __restrict__ w, int K, int N, uint32_t* __restrict__ packed,
     uint16_t* __restrict__ scales) {
@@ -50,7 +55,8 @@ __global__ __launch_bounds__(64) void pack_int4_g128_kernel(
     amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
 
-    const uint32_t sbits = f32_to_bf16_rne(amax / 7.0f);   // IEEE fp32 quotient
+    const uint32_t sbits = GIVEN ? (uint32_t)scales[(size_t)tile * 16 + c]
+                                 : f32_to_bf16_rne(amax / 7.0f);   // IEEE fp32 quotient
     const float s = bf16_to_f32(sbits);
 
     uint32_t words[4] = {0u, 0u, 0u, 0u};
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(64) void pack_int4_g128_kernel(
         int code = 8;
         if (s != 0.0f) {
             float r = rintf(v[i] / s);                       // half-even of the IEEE quotient
-            r = fminf(fmaxf(r, -8.0f), 7.0f);
+            r = fminf(fmaxf(r, GIVEN ? -7.0f : -8.0f), 7.0f);
             code = (int)r + 8;
         }
         const int t = i >> 3;
@@ -70,13 +76,79 @@ __global__ __launch_bounds__(64) void pack_int4_g128_kernel(
     u32x4 out;
     out.x = words[0]; out.y = words[1]; out.z = words[2]; out.w = words[3];
     reinterpret_cast<u32x4*>(packed)[(size_t)tile * 64 + lane] = out;
-    if (q == 0) scales[(size_t)tile * 16 + c] = (uint16_t)sbits;
+    if (!GIVEN && q == 0) scales[(size_t)tile * 16 + c] = (uint16_t)sbits;
 }
 
 void launch_pack_int4_g128(const uint16_t* w, int K, int N, uint32_t* packed,
                            uint16_t* scales, hipStream_t s) {
     const int tiles = (N / 16) * (K / 128);
-    hipLaunchKernelGGL(pack_int4_g128_kernel, dim3(tiles), dim3(64), 0, s, w, K, N, packed,
+    hipLaunchKernelGGL(pack_int4_g128_kernel<false>, dim3(tiles), dim3(64), 0, s, w, K, N, packed,
+                       scales);
+}
+
+// ---------------------------------------------------------------------------
+// MSE-optimal clipping ("Give Me BF16 or Give Me Death", section 3.4,
+// "W4A16-INT"): per group of 128 weights the clipping threshold alpha * amax,
+// alpha = i / n_alpha, i = 1 .. n_alpha, that minimizes the group's summed
+// squared quantization error; equal errors keep the larger alpha.  One thread
+// per (group, column): the candidate scale is
+// bf16_rne(float(amax * i) / float(7 * n_alpha)) (amax * i is exact), the codes
+// clamp(rne(x / s), -7, 7) of the IEEE fp32 quotient, and the error the fp64
+// sum, in row order, of the fp64-rounded squares of the exact differences
+// x - q * s.  The chosen scale goes to `scales` in native order; the packer
+// then writes the codes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void int4_mse_scale_kernel(const uint16_t* __restrict__ w, int K,
+                                                            int N, int n_alpha,
+                                                            uint16_t* __restrict__ scales) {
+    const int G = K >> 7;
+    const int g = blockIdx.y;
+    const int n = blockIdx.x * 64 + threadIdx.x;
+    if (n >= N) return;
+    uint32_t xb[64];                        // bf16 rows 2j (low half) and 2j + 1 (high half)
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+        const uint32_t lo = w[(size_t)(g * 128 + 2 * j) * N + n];
+        const uint32_t hi = w[(size_t)(g * 128 + 2 * j + 1) * N + n];
+        xb[j] = lo | (hi << 16);
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(lo)), fabsf(bf16_to_f32(hi))));
+    }
+    const float denom = (float)(7 * n_alpha);
+    double best = __builtin_inf();
+    uint32_t best_bits = 0u;
+    for (int i = 1; i <= n_alpha; ++i) {
+        const uint32_t sb = f32_to_bf16_rne((amax * (float)i) / denom);
+        const float s = bf16_to_f32(sb);
+        const double s64 = (double)s;
+        double err = 0.0;
+        {
+#pragma clang fp contract(off)              // one rounding for the square, one for the sum
+#pragma unroll
+            for (int j = 0; j < 128; ++j) {
+                const uint32_t bits = (j & 1) ? (xb[j >> 1] >> 16) : (xb[j >> 1] & 0xffffu);
+                const float x = bf16_to_f32(bits);
+                const float q = s != 0.0f ? fminf(fmaxf(rintf(x / s), -7.0f), 7.0f) : 0.0f;
+                const double d = (double)x - (double)q * s64;     // exact
+                const double d2 = d * d;
+                err = err + d2;
+            }
+        }
+        if (err <= best) {
+            best = err;
+            best_bits = sb;
+        }
+    }
+    scales[((size_t)(n >> 4) * G + g) * 16 + (n & 15)] = (uint16_t)best_bits;
+}
+
+void launch_pack_int4_g128_mse(const uint16_t* w, int K, int N, int n_alpha, uint32_t* packed,
+                               uint16_t* scales, hipStream_t s) {
+    const int G = K / 128;
+    hipLaunchKernelGGL(int4_mse_scale_kernel, dim3((N + 63) / 64, G), dim3(64), 0, s, w, K, N,
+                       n_alpha, scales);
+    const int tiles = (N / 16) * G;
+    hipLaunchKernelGGL(pack_int4_g128_kernel<true>, dim3(tiles), dim3(64), 0, s, w, K, N, packed,
                        scales);
 }
 

@@ -39,6 +39,7 @@ _SIGS = {
     "qg_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qg_w8a8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "pack_int4_g128": (_I, [_P, _I, _I, _P, _P, _P]),
+    "pack_int4_g128_mse": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "dequant_int4_g128": (_I, [_P, _P, _I, _I, _P, _P, _P]),
     "qgemm_w4a16": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "qg_w4a16_chain_plan_bytes": (_SZ, [_I]),
@@ -123,6 +124,11 @@ def pack_int4_g128(w_bf16, K, N, packed, scales, stream=None):
                                                  _stream(stream)))
 
 
+def pack_int4_g128_mse(w_bf16, K, N, n_alpha, packed, scales, stream=None):
+    _check("pack_int4_g128_mse", _lib.pack_int4_g128_mse(_ptr(w_bf16), K, N, n_alpha, _ptr(packed),
+                                                         _ptr(scales), _stream(stream)))
+
+
 def dequant_int4_g128(packed, scales, K, N, w_bf16_out, codes_out=None, stream=None):
     _check("dequant_int4_g128", _lib.dequant_int4_g128(_ptr(packed), _ptr(scales), K, N,
                                                        _ptr(w_bf16_out), _ptr(codes_out),
@@ -172,11 +178,16 @@ class Int4G128Weight:
         self.packed, self.scales, self.K, self.N = packed, scales, K, N
 
     @classmethod
-    def from_bf16(cls, w, stream=None):
+    def from_bf16(cls, w, stream=None, mse_grid=0):
+        """Abs-max scales, or with mse_grid > 0 the MSE-optimal clipping
+        threshold searched over alpha = i / mse_grid, i = 1 .. mse_grid."""
         K, N = w.shape
         packed = torch.empty(max(packed_bytes(K, N) // 4, 1), dtype=torch.int32, device=w.device)
         scales = torch.empty(max(scale_bytes(K, N) // 2, 1), dtype=torch.int16, device=w.device)
-        pack_int4_g128(_bf16(w.contiguous()), K, N, packed, scales, stream)
+        if mse_grid:
+            pack_int4_g128_mse(_bf16(w.contiguous()), K, N, mse_grid, packed, scales, stream)
+        else:
+            pack_int4_g128(_bf16(w.contiguous()), K, N, packed, scales, stream)
         return cls(packed, scales, K, N)
 
     def dequant(self, with_codes=False, stream=None):

@@ -1,7 +1,7 @@
 """Benchmark: Llama-3-8B W4A16 decode step (129 quantized linears) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
-                    [--workload decode|large-batch|fp8|70b]
+                    [--workload decode|large-batch|fp8|70b|pack-mse]
 
 One step is one pass of the whole hot path over one batch: the 129 W4A16
 GEMMs of a Llama-3-8B decode step (32 layers of qkv 4096->6144, o 4096->4096,
@@ -18,6 +18,8 @@ listed under "by_batch".  Other workloads (one line each):
                (hipBLASLt through torch.matmul), MFMA utilisation and crossover
   fp8          the W8A8-FP8 stack (per-token activation quantization + fp8 GEMM)
   70b          the Llama-3-70B W4A16 stack on one GPU
+  pack-mse     offline INT4 g128 packing of the Llama-3-8B weights with
+               MSE-optimal clipping (100-point grid), against abs-max packing
 
 Algorithmic bytes of one W4A16 GEMM: K*N/2 (codes) + 2*N*K/128 (scales) +
 2*M*K (activations) + 2*M*N (outputs); flops: 2*M*N*K.
@@ -37,6 +39,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+# Vector ALU rates per lane and clock from the published peaks: fp32 157.3 TFLOP/s
+# = 256 CUs x 64 lanes x 2.4 GHz x 2 FMA x 2 flops, fp64 78.6 = the same x 1 FMA
+VALU_LANE_CLOCKS = 256 * 64 * 2.4e9
+VALU_FP32_PER_CLK, VALU_FP64_PER_CLK = 2.0, 1.0
+# Instructions per (weight, grid point) in the clipping search's inner loop,
+# counted in the AMD assembly of this build: 32-bit ones (the IEEE fp32 division
+# sequence, rint, clamp, select) and 64-bit ones (convert, product, difference,
+# square, sum)
+MSE_FP32_OPS_PER_POINT = 14.05
+MSE_FP64_OPS_PER_POINT = 5.58
+MSE_GRID = 100
 DOMINANT_SRC = os.path.join(ROOT, "weight_only_quantized_w4a16_amd", "csrc", "w4a16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_decode_kernel_llama3_8b_decode_B16_traffic.txt")
 
@@ -56,7 +69,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--batch", type=int, default=16)
-    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "70b"])
+    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "70b", "pack-mse"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-chain", action="store_true",
                    help="decode workload: skip the chained-launch timing")
@@ -346,6 +359,8 @@ def main():
         run_large_batch(args, torch, ops, synth)
     elif args.workload == "fp8":
         run_fp8(args, torch, ops, synth)
+    elif args.workload == "pack-mse":
+        run_pack_mse(args, torch, ops, synth)
     else:
         run_70b(args, torch, ops, synth)
 
@@ -513,6 +528,94 @@ def run_fp8(args, torch, ops, synth):
            "vs_baseline": None, "dtype": "e4m3 x e4m3 -> fp32 acc (fp8 MFMA)", "data": "synthetic",
            "config": {"workload": "Llama-3-8B W8A8-FP8 stack incl. per-token activation quantization",
                       "batch": 16}, "by_batch": res}
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_pack_mse():
+    """The oracle's MSE-clipping quantizer on gate_up columns [0, 1536) of layer 0
+    (4096 x 1536 weights), one run.  Its work is numpy element-wise arithmetic,
+    which runs on one thread."""
+    from oracle import int4_g128 as q4
+    from weight_only_quantized_w4a16_amd import synth
+    threads = 1
+    K, cols = 4096, 1536
+    w = synth.weights(K, 28672, seed=synth.weight_seed(0, 2))[:, :cols]
+    t = time.perf_counter()
+    q4.quantize_mse(w, n_alpha=MSE_GRID)
+    sec = time.perf_counter() - t
+    return K * cols / sec, threads, f"layer-0 gate_up columns [0, {cols}) ({K * cols} weights), one run"
+
+
+def run_pack_mse(args, torch, ops, synth):
+    dev = torch.device("cuda:0")
+    reps = max(3, min(args.steps, 10))
+    stream = torch.cuda.current_stream()
+    shapes = [(name, K, N, synth.LLAMA3_8B_LAYERS, j) for j, (name, K, N) in enumerate(synth.LLAMA3_8B_LAYER)]
+    shapes.append((synth.LLAMA3_8B_HEAD[0], *synth.LLAMA3_8B_HEAD[1:], 1, 0))
+    res = {}
+    total_w = total_mse_s = total_abs_s = 0.0
+    for name, K, N, count, j in shapes:
+        w = synth.normal_bf16_device((K, N), synth.weight_seed(0 if count > 1 else 32, j),
+                                     synth.WEIGHT_STD, dev)
+        packed = torch.empty(K * N // 8, dtype=torch.int32, device=dev)
+        scales = torch.empty(K // 128 * N, dtype=torch.int16, device=dev)
+
+        def timed(fn, n):
+            for _ in range(args.warmup if n > 3 else 1):
+                fn()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(n):
+                fn()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / n
+
+        ms_abs = timed(lambda: ops.pack_int4_g128(w, K, N, packed, scales), args.steps)
+        ms_mse = timed(lambda: ops.pack_int4_g128_mse(w, K, N, MSE_GRID, packed, scales), reps)
+        # summed squared error of both packings (exact fp32 reconstruction on the GPU)
+        errs = []
+        for grid in (0, MSE_GRID):
+            wt = ops.Int4G128Weight.from_bf16(w, mse_grid=grid)
+            _, codes = wt.dequant(with_codes=True)
+            G = K // 128
+            s = wt.scales.view(torch.bfloat16).float().view(N // 16, G, 16).permute(1, 0, 2).reshape(G, N)
+            what = (codes.float() - 8.0).view(G, 128, N) * s[:, None, :]
+            errs.append(float(((w.float().view(G, 128, N) - what) ** 2).double().sum()))
+            del wt, codes, what
+        res[name] = {"K": K, "N": N, "count": count, "abs_max_ms": round(ms_abs, 4),
+                     "abs_max_GB_s": round((2.5 + 1 / 64) * K * N / (ms_abs * 1e-3) / 1e9, 1),
+                     "mse_ms": round(ms_mse, 3),
+                     "mse_Gweights_s": round(K * N / (ms_mse * 1e-3) / 1e9, 2),
+                     "sq_error_mse_over_abs_max": round(errs[1] / errs[0], 4)}
+        print(f"[bench] pack {name}: {res[name]}", file=sys.stderr, flush=True)
+        total_w += count * K * N
+        total_mse_s += count * ms_mse * 1e-3
+        total_abs_s += count * ms_abs * 1e-3
+        del w, packed, scales
+    gw = total_w / total_mse_s / 1e9
+    achieved = gw * 1e9 * MSE_GRID / 1e12                        # T (weight, grid point) pairs / s
+    peak = VALU_LANE_CLOCKS / (MSE_FP32_OPS_PER_POINT / VALU_FP32_PER_CLK
+                               + MSE_FP64_OPS_PER_POINT / VALU_FP64_PER_CLK) / 1e12
+    out = {"metric": "Llama-3-8B INT4 g128 packing with MSE-optimal clipping: weights per second",
+           "value": round(gw, 3), "unit": "Gweights/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+           "ms_per_step": round(total_mse_s * 1e3, 2), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16 in, fp32 search, fp64 error sums", "data": "synthetic N(0, 0.02^2)",
+           "config": {"workload": f"Llama-3-8B linear weights (32 x qkv/o/gate_up/down + LM head, "
+                                  f"{int(total_w)} weights), {MSE_GRID}-point clipping grid",
+                      "abs_max_pack_ms": round(total_abs_s * 1e3, 2)},
+           "by_shape": res,
+           "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3),
+                        "unit": "T weight-grid-points/s", "frac": round(achieved / peak, 4),
+                        "traffic": None, "kernel": "int4_mse_scale_kernel (+ the packer, about 1 %)",
+                        "fp32_ops_per_point": MSE_FP32_OPS_PER_POINT,
+                        "fp64_ops_per_point": MSE_FP64_OPS_PER_POINT}}
+    if not args.no_cpu_baseline:
+        rate, threads, sample = cpu_baseline_pack_mse()
+        out["cpu_baseline"] = {"value": round(rate / 1e9, 6), "unit": "Gweights/s", "cores": threads,
+                               "kind": "oracle", "sample": sample}
     print(json.dumps(out), flush=True)
 
 

@@ -121,6 +121,8 @@ __global__ __launch_bounds__(64) void int4_mse_scale_kernel(const uint16_t* __re
         const uint32_t sb = f32_to_bf16_rne((amax * (float)i) / denom);
         const float s = bf16_to_f32(sb);
         const double s64 = (double)s;
+        const bool live = s != 0.0f;
+        const float s_div = live ? s : 1.0f;    // no branch per weight
         double err = 0.0;
         {
 #pragma clang fp contract(off)              // one rounding for the square, one for the sum
@@ -128,7 +130,8 @@ __global__ __launch_bounds__(64) void int4_mse_scale_kernel(const uint16_t* __re
             for (int j = 0; j < 128; ++j) {
                 const uint32_t bits = (j & 1) ? (xb[j >> 1] >> 16) : (xb[j >> 1] & 0xffffu);
                 const float x = bf16_to_f32(bits);
-                const float q = s != 0.0f ? fminf(fmaxf(rintf(x / s), -7.0f), 7.0f) : 0.0f;
+                float q = fminf(fmaxf(rintf(x / s_div), -7.0f), 7.0f);
+                q = live ? q : 0.0f;
                 const double d = (double)x - (double)q * s64;     // exact
                 const double d2 = d * d;
                 err = err + d2;

@@ -264,6 +264,25 @@ def gemm_ref(a_bits, codes, scale_bits):
     return a @ w
 
 
+def grouped_gemm_ref(a_bits, offsets, experts):
+    """The expert-grouped W4A16 product in fp64.
+
+    A mixture-of-experts layer sends each routed row through its own expert's
+    weight ("When quantization pays", the mixture-of-experts section: a batch
+    of B tokens gives every expert about B k / E rows).  Rows are grouped by
+    expert: expert e owns rows offsets[e] .. offsets[e+1]-1 of a_bits [T, K],
+    and its output rows are those rows times that expert's dequantized weight.
+
+    experts: {e: (codes, scale_bits)} as returned by quantize(); only the
+    listed experts are computed.  Returns {e: Y64 [rows_e, N]}.
+    """
+    out = {}
+    for e, (codes, s) in experts.items():
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        out[e] = gemm_ref(a_bits[r0:r1], codes, s)
+    return out
+
+
 def gemm_ref_bf16_operand(a_bits, codes, scale_bits):
     """Diagnostic variant: the product with the bf16-rounded dequantized operand."""
     a = bf16_bits_to_f32(a_bits).astype(np.float64)

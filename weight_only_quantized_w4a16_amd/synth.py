@@ -28,6 +28,29 @@ LLAMA3_70B_HEAD = ("lm_head", 8192, 128256)
 LLAMA3_70B_LAYERS = 80
 
 
+# Qwen3-30B-A3B routed experts: 48 layers of 128 experts, top-8 routing;
+# each expert holds gate_up 2048 -> 2 x 768 and down 768 -> 2048.
+QWEN3_MOE_LAYERS = 48
+QWEN3_MOE_EXPERTS = 128
+QWEN3_MOE_TOPK = 8
+QWEN3_MOE_SHAPES = (("gate_up", 2048, 1536), ("down", 768, 2048))
+
+
+def moe_routing(B, E, k, seed):
+    """Uniform top-k routing of B tokens to E experts, k distinct experts per token
+    (seeded).  Returns (token_of_row [B*k], offsets [E+1]): the routed rows grouped
+    by expert (ascending), tokens ascending inside an expert; expert e owns rows
+    offsets[e] .. offsets[e+1]-1."""
+    rng = np.random.default_rng(seed)
+    choice = np.argsort(rng.random((B, E)), axis=1)[:, :k]          # k distinct experts per token
+    expert = choice.reshape(-1)
+    token = np.repeat(np.arange(B), k)
+    order = np.lexsort((token, expert))
+    counts = np.bincount(expert, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return token[order].astype(np.int32), offsets
+
+
 def stack_shapes(model="8b", with_head=True):
     """Every GEMM of one decode step, in execution order: list of (name, K, N)."""
     if model == "8b":

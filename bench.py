@@ -1,7 +1,7 @@
 """Benchmark: Llama-3-8B W4A16 decode step (129 quantized linears) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
-                    [--workload decode|large-batch|fp8|70b|pack-mse]
+                    [--workload decode|large-batch|fp8|70b|pack-mse|moe]
 
 One step is one pass of the whole hot path over one batch: the 129 W4A16
 GEMMs of a Llama-3-8B decode step (32 layers of qkv 4096->6144, o 4096->4096,
@@ -20,6 +20,9 @@ listed under "by_batch".  Other workloads (one line each):
   70b          the Llama-3-70B W4A16 stack on one GPU
   pack-mse     offline INT4 g128 packing of the Llama-3-8B weights with
                MSE-optimal clipping (100-point grid), against abs-max packing
+  moe          the routed-expert GEMMs of a Qwen3-30B-A3B decode step (48
+               layers x {gate_up, down} over 128 experts, top-8 routing),
+               expert-grouped W4A16
 
 Algorithmic bytes of one W4A16 GEMM: K*N/2 (codes) + 2*N*K/128 (scales) +
 2*M*K (activations) + 2*M*N (outputs); flops: 2*M*N*K.
@@ -69,7 +72,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--batch", type=int, default=16)
-    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "70b", "pack-mse"])
+    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "70b", "pack-mse", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-chain", action="store_true",
                    help="decode workload: skip the chained-launch timing")
@@ -361,6 +364,8 @@ def main():
         run_fp8(args, torch, ops, synth)
     elif args.workload == "pack-mse":
         run_pack_mse(args, torch, ops, synth)
+    elif args.workload == "moe":
+        run_moe(args, torch, ops, synth)
     else:
         run_70b(args, torch, ops, synth)
 
@@ -616,6 +621,98 @@ def run_pack_mse(args, torch, ops, synth):
         rate, threads, sample = cpu_baseline_pack_mse()
         out["cpu_baseline"] = {"value": round(rate / 1e9, 6), "unit": "Gweights/s", "cores": threads,
                                "kind": "oracle", "sample": sample}
+    print(json.dumps(out), flush=True)
+
+
+def moe_bytes(offsets, K, N):
+    """Algorithmic bytes of one grouped GEMM: the weights of the experts that
+    receive rows, their activations and outputs."""
+    active = int(np.sum(np.diff(offsets) > 0))
+    T = int(offsets[-1])
+    return active * (K * N // 2 + 2 * N * (K // 128)) + 2 * T * K + 2 * T * N
+
+
+def cpu_baseline_moe(B):
+    """The oracle on layer 0 of the expert stack at batch B: both grouped GEMMs
+    over the first 16 experts that receive rows (quantization untimed), scaled
+    by the number of experts with rows and by 48 layers."""
+    from oracle import int4_g128 as q4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    from weight_only_quantized_w4a16_amd import synth
+    E, k = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK
+    token, offsets = synth.moe_routing(B, E, k, seed=B)
+    total = 0.0
+    for j, (name, K, N) in enumerate(synth.QWEN3_MOE_SHAPES):
+        a = synth.activations(B, K, seed=synth.activation_seed(0, j))[token]
+        active = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+        ex = {e: q4.quantize(synth.weights(K, N, seed=synth.weight_seed(0, j) * 1000 + e))
+              for e in active[:16]}
+        t = time.perf_counter()
+        q4.grouped_gemm_ref(a, offsets, ex)
+        total += (time.perf_counter() - t) * len(active) / len(ex)
+    return total * synth.QWEN3_MOE_LAYERS, threads
+
+
+def run_moe(args, torch, ops, synth):
+    dev = torch.device("cuda:0")
+    E, k, L = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK, synth.QWEN3_MOE_LAYERS
+    batches = [1, 16, 64, 256, 1024]
+    maxT = max(batches) * k
+    gemms = []
+    for layer in range(L):
+        for j, (name, K, N) in enumerate(synth.QWEN3_MOE_SHAPES):
+            w = synth.normal_bf16_device((E, K, N), synth.weight_seed(layer, j), synth.WEIGHT_STD, dev)
+            gw = ops.GroupedInt4Weight.from_bf16(w)
+            del w
+            a = synth.normal_bf16_device((maxT, K), synth.activation_seed(layer, j), 1.0, dev)
+            y = torch.empty((maxT, N), dtype=torch.bfloat16, device=dev)
+            gemms.append((name, K, N, gw, a, y))
+    torch.cuda.synchronize()
+    res = {}
+    for B in batches:
+        token, offsets = synth.moe_routing(B, E, k, seed=B)
+        T = B * k
+        off = torch.from_numpy(offsets).to(dev)
+        nbytes = sum(moe_bytes(offsets, K, N) for (_, K, N, *_r) in gemms)
+
+        def step():
+            for (_, K, N, gw, a, y) in gemms:
+                gw(a[:T], off, out=y[:T])
+        g = graph_of(torch, step)
+        ms = time_graph(torch, g, args.steps, args.warmup)
+        del g
+        res[str(B)] = {"ms_per_step": round(ms, 4), "rows": T,
+                       "active_experts": int(np.sum(np.diff(offsets) > 0)),
+                       "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3), "bytes": nbytes}
+        print(f"[bench] moe B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
+    B = 16
+    r = res[str(B)]
+    per_launch_us = r["ms_per_step"] * 1e3 / len(gemms)
+    achieved = r["bytes"] / len(gemms) / (per_launch_us * 1e-6) / 1e9
+    out = {"metric": "Qwen3-30B-A3B routed-expert W4A16 decode step: HBM TB/s", "value": r["TB_s"],
+           "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)",
+           "data": "synthetic: weights N(0, 0.02^2), activations N(0, 1), seeded uniform top-8 routing",
+           "config": {"workload": "Qwen3-30B-A3B routed experts: 48 layers x {gate_up 2048->1536, "
+                                  "down 768->2048} x 128 experts, top-8, expert-grouped W4A16 "
+                                  "(attention, router and shared layers excluded)", "batch": B},
+           "by_batch": res,
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "grouped_items_kernel + w4a16_grouped_kernel per GEMM (96 per step)",
+                        "avg_launch_us": round(per_launch_us, 3)}}
+    if not args.no_cpu_baseline:
+        sec, threads = cpu_baseline_moe(B)
+        out["cpu_baseline"] = {"value": round(r["bytes"] / sec / 1e12, 6), "unit": "TB/s", "cores": threads,
+                               "kind": "oracle", "seconds_per_step": round(sec, 2),
+                               "sample": f"B={B}: layer 0, both grouped GEMMs over the first 16 experts "
+                                         f"with rows (fp32 dequant + fp64 matmul per expert), scaled to all "
+                                         f"experts with rows and x48 layers"}
     print(json.dumps(out), flush=True)
 
 

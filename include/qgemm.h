@@ -229,6 +229,43 @@ qg_status qgemm_w4a16_chain(const void *plan_host, const void *plan_device,
                             void *workspace, size_t workspace_bytes, qg_stream stream);
 
 /*
+ * qgemm_w4a16_grouped -- the W4A16 product of a mixture-of-experts layer: each
+ * routed row times its own expert's INT4 g128 weight, bf16 in and out.
+ * [P1, the mixture-of-experts section: a batch of B tokens sends about B k / E
+ *  rows to each expert, so expert GEMMs stay weight-stream bound far longer
+ *  than dense ones; P2 3.4 "Inference with W4A16".]
+ *
+ *   a_bf16     in   [T, K] routed rows grouped by expert.
+ *   offsets    in   device int32 [E + 1]: expert e owns rows
+ *                   offsets[e] .. offsets[e+1] - 1 (offsets[0] = 0,
+ *                   non-decreasing, offsets[E] = T).
+ *   packed     in   E native INT4 weights of [K, N] back to back (expert e at
+ *                   word e * K * N / 8), each from pack_int4_g128.
+ *   scales     in   the E native scale arrays back to back (expert e at
+ *                   element e * (K / 128) * N).
+ *   y_bf16     out  [T, N]: row r = a[r] . w_hat_e for the expert e owning r.
+ *   E          1 .. 1024.   T   routed rows (0: nothing to do).
+ *   workspace  qg_w4a16_grouped_workspace_bytes(E, T, N, K) bytes (4-byte
+ *              aligned): the call's work items (expert, row chunk), rebuilt by
+ *              every call, so no initial contents are needed.  Calls that
+ *              share a workspace must not overlap in time.
+ * Offsets are read on the device and clamped into [0, T] with
+ * offsets[e] <= offsets[e+1] enforced per expert, so malformed offsets never
+ * cause an access out of bounds; rows they leave unassigned keep their old
+ * output, and overlapping ranges give unspecified output rows.
+ * QG_ERR_SHAPE: E outside 1 .. 1024, or shapes as qgemm_w4a16 (T as M), or
+ * more than 65535 work items (about T / 16 + min(E, T)).
+ * Arithmetic per row: exactly that of qgemm_w4a16 for M <= 64 (folded
+ * offset, fp32 accumulation).
+ */
+size_t qg_w4a16_grouped_workspace_bytes(int64_t E, int64_t T, int64_t N, int64_t K);
+qg_status qgemm_w4a16_grouped(const uint16_t *a_bf16, const int32_t *offsets,
+                              const uint32_t *packed, const uint16_t *scales,
+                              uint16_t *y_bf16, int E, int T, int N, int K,
+                              void *workspace, size_t workspace_bytes,
+                              qg_stream stream);
+
+/*
  * quant_act_per_token -- dynamic per-token e4m3 quantization.
  * [P2 3.4 "W8A8-FP", activation quantization: Q(a_i) = s_i * rnd(a_i / s_i),
  *  s_i = max|a_i| / q_max, computed on the fly per row.]

@@ -164,6 +164,32 @@ def test_other_entry_points_validate(lib):
     assert g8(FAKE, FAKE, FAKE, FAKE, None, 0, 4096, 4096, None, 0, None) == QG_OK
 
 
+def test_grouped_entry_point_validates(lib):
+    raw = ctypes.CDLL(LIB)
+    V, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    g = raw.qgemm_w4a16_grouped
+    g.restype, g.argtypes = I, [V, V, V, V, V, I, I, I, I, V, S, V]
+    # E = 128 experts, T = 8 rows: one 16-row chunk per non-empty expert (at most
+    # 8) plus ceil(8 / 16) = 1 -> 9 items of 3 ints after the count
+    assert lib.w4a16_grouped_workspace_bytes(128, 8, 1536, 2048) == (1 + 3 * 9) * 4
+    assert lib.w4a16_grouped_workspace_bytes(128, 0, 1536, 2048) == 0
+    assert lib.w4a16_grouped_workspace_bytes(0, 8, 1536, 2048) == 0          # invalid E
+    need = lib.w4a16_grouped_workspace_bytes(128, 8, 1536, 2048)
+    args = lambda **k: [k.get("a", FAKE), k.get("off", FAKE), k.get("w", FAKE), k.get("s", FAKE),
+                        k.get("y", FAKE), k.get("E", 128), k.get("T", 8), k.get("N", 1536),
+                        k.get("K", 2048), k.get("ws", FAKE), k.get("wsb", need), None]
+    assert g(*args(E=0)) == QG_ERR_SHAPE
+    assert g(*args(E=1025)) == QG_ERR_SHAPE
+    assert g(*args(K=2000)) == QG_ERR_SHAPE
+    assert g(*args(T=0, a=None)) == QG_OK
+    assert g(*args(E=1024, T=1 << 24)) == QG_ERR_SHAPE  # more than 65535 work items
+    assert g(*args(off=None)) == QG_ERR_NULL
+    assert g(*args(ws=None)) == QG_ERR_NULL
+    assert g(*args(off=FAKE + 2)) == QG_ERR_ALIGN
+    assert g(*args(a=FAKE + 8)) == QG_ERR_ALIGN
+    assert g(*args(wsb=need - 4)) == QG_ERR_WORKSPACE
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     a = torch.zeros(4, 128, dtype=torch.bfloat16)

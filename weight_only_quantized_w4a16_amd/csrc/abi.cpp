@@ -23,6 +23,13 @@ bool shape_ok(int64_t M, int64_t N, int64_t K) {
     return true;
 }
 
+// Expert-grouped shapes: E experts of [K, N], T routed rows.
+bool grouped_ok(int64_t E, int64_t T, int64_t N, int64_t K) {
+    if (E < 1 || E > qg::kGroupedMaxExperts || !shape_ok(T, N, K)) return false;
+    if (E * N * K > 64 * kMaxElems) return false;
+    return T == 0 || qg::w4a16_grouped_max_items((int)E, (int)T) <= 65535;
+}
+
 qg_status launched() {
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_HIP;
 }
@@ -72,6 +79,11 @@ const char* qg_w8a8_kernel_for(int64_t M, int64_t N, int64_t K) {
 size_t qg_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (!shape_ok(M, N, K)) return 0;
     return qg::w4a16_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+size_t qg_w4a16_grouped_workspace_bytes(int64_t E, int64_t T, int64_t N, int64_t K) {
+    if (!grouped_ok(E, T, N, K)) return 0;
+    return qg::w4a16_grouped_workspace_bytes((int)E, (int)T);
 }
 
 size_t qg_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -188,6 +200,22 @@ qg_status qgemm_w4a16_chain(const void* plan_host, const void* plan_device, void
         (void)hipGetLastError();
         return QG_ERR_HIP;
     }
+    return launched();
+}
+
+qg_status qgemm_w4a16_grouped(const uint16_t* a_bf16, const int32_t* offsets,
+                              const uint32_t* packed, const uint16_t* scales, uint16_t* y_bf16,
+                              int E, int T, int N, int K, void* workspace, size_t workspace_bytes,
+                              qg_stream stream) {
+    if (!grouped_ok(E, T, N, K)) return QG_ERR_SHAPE;
+    if (T == 0) return QG_OK;
+    if (!a_bf16 || !offsets || !packed || !scales || !y_bf16 || !workspace) return QG_ERR_NULL;
+    if (!aligned(a_bf16, 16) || !aligned(offsets, 4) || !aligned(packed, 16) ||
+        !aligned(scales, 4) || !aligned(y_bf16, 16) || !aligned(workspace, 4))
+        return QG_ERR_ALIGN;
+    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T)) return QG_ERR_WORKSPACE;
+    qg::launch_qgemm_w4a16_grouped(a_bf16, offsets, packed, scales, y_bf16, E, T, N, K, workspace,
+                                   as_stream(stream));
     return launched();
 }
 

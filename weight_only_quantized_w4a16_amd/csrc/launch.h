@@ -20,6 +20,14 @@ const char* w4a16_kernel_for(int M, int N, int K);
 void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_t* scales,
                         uint16_t* y, int M, int N, int K, void* ws, hipStream_t s);
 
+// Expert-grouped W4A16 (w4a16.hip)
+constexpr int kGroupedMaxExperts = 1024;
+int w4a16_grouped_max_items(int E, int T);
+size_t w4a16_grouped_workspace_bytes(int E, int T);
+void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
+                                const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
+                                void* ws, hipStream_t s);
+
 // Chained decode (chain.hip)
 struct ChainDesc {          // one GEMM of a chain as the kernel reads it (64 bytes)
     const uint16_t* a;

@@ -216,16 +216,19 @@ void launch_dequant_int4_g128(const uint32_t* packed, const uint16_t* scales, in
 // (3 shifts + 4 AND-ORs per 8 weights).
 // ---------------------------------------------------------------------------
 
+// The work of one workgroup: column tiles [nt0, nt0 + CT) of y[M, N] =
+// a[M, K] . w_hat[K, N] (M <= 16 * MT).
 template <int MT, int CT, int NWAVE, int U, bool PIPE>
-__global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
-    const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
-    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K) {
+__device__ __forceinline__ void small_m_tile(const uint16_t* __restrict__ a,
+                                             const uint32_t* __restrict__ wq,
+                                             const uint16_t* __restrict__ sc,
+                                             uint16_t* __restrict__ y, int M, int N, int K,
+                                             int nt0) {
     const int G = K >> 7;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
     const int col = lane & 15;
     const int kq = lane >> 4;
-    const int nt0 = blockIdx.x * CT;
     const int g_begin = (G * wave) / NWAVE;
     const int ng = (G * (wave + 1)) / NWAVE - g_begin;
     const int nitems = (ng + U - 1) / U;          // the last item may be partial
@@ -368,6 +371,86 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
         const int n = (nt0 + ct) * 16 + (l & 15);
         y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum);
     }
+}
+
+template <int MT, int CT, int NWAVE, int U, bool PIPE>
+__global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
+    const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int M, int N, int K) {
+    small_m_tile<MT, CT, NWAVE, U, PIPE>(a, wq, sc, y, M, N, K, blockIdx.x * CT);
+}
+
+// ---------------------------------------------------------------------------
+// Expert-grouped W4A16 ("When quantization pays", the mixture-of-experts
+// section: each expert's GEMM sees about B k / E of the batch's rows).  The
+// routed rows arrive grouped by expert, expert e owning rows
+// [offsets[e], offsets[e+1]), and the E expert weights lie back to back in
+// the native layout.  Work items are the R-row chunks of the non-empty
+// experts, numbered expert by expert.  A one-wave pass reads the offsets
+// (each lane loads those of its 16 experts, all in flight at once), counts
+// the chunks, numbers them with a wave prefix sum and writes the items
+// (expert, first row, rows) to the workspace; the GEMM grid then takes one
+// item per blockIdx.y (scalar loads) and runs the small-M tile over that
+// expert's weight.  Experts without rows cost nothing, and an expert's
+// weights are streamed once per chunk.  Offsets are clamped into [0, T]
+// (r0 <= r1), so malformed offsets stay in bounds; items past the bound
+// min(E, T) + ceil(T / R) are dropped.
+// ---------------------------------------------------------------------------
+constexpr int GROUPED_MAX_E = 1024;
+
+__global__ __launch_bounds__(64) void grouped_items_kernel(const int* __restrict__ offsets, int E,
+                                                           int T, int R, int max_items,
+                                                           int* __restrict__ items) {
+    constexpr int PER = GROUPED_MAX_E / 64;          // experts per lane
+    const int lane = threadIdx.x;
+    const int e0 = lane * PER;
+    int bound[PER + 1];
+#pragma unroll
+    for (int i = 0; i <= PER; ++i) bound[i] = offsets[min(e0 + i, E)];
+    int r0[PER], r1[PER], cnt[PER];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const bool ok = e0 + i < E;
+        r0[i] = ok ? min(max(bound[i], 0), T) : 0;
+        r1[i] = ok ? min(max(bound[i + 1], r0[i]), T) : 0;
+        cnt[i] = (r1[i] - r0[i] + R - 1) / R;
+        local += cnt[i];
+    }
+    int incl = local;                                // inclusive prefix over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    int first = incl - local;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        for (int c = 0; c < cnt[i]; ++c) {
+            const int it = first + c;
+            if (it >= max_items) break;
+            items[1 + 3 * it] = e0 + i;
+            items[2 + 3 * it] = r0[i] + c * R;
+            items[3 + 3 * it] = min(R, r1[i] - r0[i] - c * R);
+        }
+        first += cnt[i];
+    }
+    if (lane == 63) items[0] = min(incl, max_items);
+}
+
+template <int MT, int CT, int NWAVE, int U, bool PIPE>
+__global__ __launch_bounds__(NWAVE * 64) void w4a16_grouped_kernel(
+    const uint16_t* __restrict__ a, const int* __restrict__ items, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N, int K) {
+    const int it = blockIdx.y;
+    if (it >= items[0]) return;
+    const int e = items[1 + 3 * it];
+    const int row0 = items[2 + 3 * it];
+    const int rows = items[3 + 3 * it];
+    const size_t words = (size_t)(K / 8) * N;        // one expert's packed words
+    const size_t nsc = (size_t)(K / 128) * N;        // one expert's scales
+    small_m_tile<MT, CT, NWAVE, U, PIPE>(a + (size_t)row0 * K, wq + e * words, sc + e * nsc,
+                                         y + (size_t)row0 * N, rows, N, K, blockIdx.x * CT);
 }
 
 // ---------------------------------------------------------------------------
@@ -992,6 +1075,68 @@ static void launch_small_ct(const uint16_t* a, const uint32_t* wq, const uint16_
         launch_small<MT, 2>(a, wq, sc, y, M, N, K, s);
     else
         launch_small<MT, 1>(a, wq, sc, y, M, N, K, s);
+}
+
+// ---- expert-grouped launch ----
+#ifndef QG_GR_NWAVE                // waves per workgroup (K split inside the workgroup)
+#define QG_GR_NWAVE 4
+#endif
+#ifndef QG_GR_CT                   // column tiles per workgroup (0: the small-M rule)
+#define QG_GR_CT 4
+#endif
+// rows per item: 16 * MT, MT from the mean rows per non-empty expert
+static int grouped_mt(int E, int T) {
+    const int active = T < E ? T : E;
+    const int mean = (T + active - 1) / (active > 0 ? active : 1);
+    return mean <= 16 ? 1 : (mean <= 32 ? 2 : 4);
+}
+
+static int grouped_max_items(int E, int T) {
+    const int R = 16 * grouped_mt(E, T);
+    return (T < E ? T : E) + (T + R - 1) / R;
+}
+
+int w4a16_grouped_max_items(int E, int T) { return T == 0 ? 0 : grouped_max_items(E, T); }
+
+size_t w4a16_grouped_workspace_bytes(int E, int T) {
+    return T == 0 ? 0 : (size_t)(1 + 3 * grouped_max_items(E, T)) * sizeof(int);
+}
+
+template <int MT, int CT>
+static void launch_grouped_mt(const uint16_t* a, const int* items, const uint32_t* wq,
+                              const uint16_t* sc, uint16_t* y, int N, int K, int max_items,
+                              hipStream_t s) {
+    constexpr int NWAVE = QG_GR_NWAVE;
+    constexpr int U = MT == 1 ? QG_SM_U : 1;
+    constexpr bool PIPE = MT <= 2 && CT <= 2;
+    hipLaunchKernelGGL((w4a16_grouped_kernel<MT, CT, NWAVE, U, PIPE>), dim3(N / 16 / CT, max_items),
+                       dim3(NWAVE * 64), 0, s, a, items, wq, sc, y, N, K);
+}
+
+void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
+                                const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
+                                void* ws, hipStream_t s) {
+    const int MT = grouped_mt(E, T);
+    const int max_items = grouped_max_items(E, T);
+    int* items = static_cast<int*>(ws);
+    hipLaunchKernelGGL(grouped_items_kernel, dim3(1), dim3(64), 0, s, offsets, E, T, 16 * MT,
+                       max_items, items);
+    const int NT = N / 16;
+    int ct = QG_GR_CT ? QG_GR_CT : small_ct(NT);
+    while (NT % ct) ct >>= 1;
+    auto go = [&](auto mt) {
+        constexpr int M_T = decltype(mt)::value;
+        // the LDS reduction holds NWAVE * CT * MT KiB
+        constexpr bool fits8 = QG_GR_NWAVE * 8 * M_T <= 64;
+        if (ct == 8 && fits8)
+            launch_grouped_mt<M_T, fits8 ? 8 : 4>(a, items, wq, sc, y, N, K, max_items, s);
+        else if (ct >= 4) launch_grouped_mt<M_T, 4>(a, items, wq, sc, y, N, K, max_items, s);
+        else if (ct == 2) launch_grouped_mt<M_T, 2>(a, items, wq, sc, y, N, K, max_items, s);
+        else              launch_grouped_mt<M_T, 1>(a, items, wq, sc, y, N, K, max_items, s);
+    };
+    if (MT == 1) go(ic<1>{});
+    else if (MT == 2) go(ic<2>{});
+    else go(ic<4>{});
 }
 
 // ---- decode-kernel configuration (M <= 16), a function of the shape only ----

@@ -46,6 +46,8 @@ _SIGS = {
     "qg_w4a16_chain_workspace_bytes": (_SZ, [_I]),
     "qg_w4a16_chain_plan": (_I, [_P, _I, _I, _P, _SZ]),
     "qgemm_w4a16_chain": (_I, [_P, _P, _P, _SZ, _P]),
+    "qg_w4a16_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "qgemm_w4a16_grouped": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
     "quant_act_per_token": (_I, [_P, _I, _I, _P, _P, _P]),
     "quant_weight_fp8_per_channel": (_I, [_P, _I, _I, _P, _P, _P]),
     "qgemm_w8a8_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
@@ -236,6 +238,51 @@ class Fp8Weight:
         scales = torch.empty(N, dtype=torch.float32, device=w.device)
         quant_weight_fp8_per_channel(_bf16(w.contiguous()), K, N, codes, scales, stream)
         return cls(codes, scales, K, N)
+
+
+def w4a16_grouped_workspace_bytes(E, T, N, K):
+    return _lib.qg_w4a16_grouped_workspace_bytes(E, T, N, K)
+
+
+def qgemm_w4a16_grouped(a_bf16, offsets_i32, packed, scales, y_bf16, E, T, N, K, workspace,
+                        workspace_bytes, stream=None):
+    _check("qgemm_w4a16_grouped",
+           _lib.qgemm_w4a16_grouped(_ptr(a_bf16), _ptr(offsets_i32), _ptr(packed), _ptr(scales),
+                                    _ptr(y_bf16), E, T, N, K, _ptr(workspace), workspace_bytes,
+                                    _stream(stream)))
+
+
+class GroupedInt4Weight:
+    """E experts' [K, N] weights packed back to back (device buffers owned by torch)."""
+
+    def __init__(self, packed, scales, E, K, N):
+        self.packed, self.scales, self.E, self.K, self.N = packed, scales, E, K, N
+        self._ws = None
+
+    @classmethod
+    def from_bf16(cls, w, stream=None):
+        """w: [E, K, N] bf16 on the device."""
+        E, K, N = w.shape
+        words, nsc = packed_bytes(K, N) // 4, scale_bytes(K, N) // 2
+        packed = torch.empty(E * words, dtype=torch.int32, device=w.device)
+        scales = torch.empty(E * nsc, dtype=torch.int16, device=w.device)
+        for e in range(E):
+            pack_int4_g128(_bf16(w[e].contiguous()), K, N, packed[e * words:(e + 1) * words],
+                           scales[e * nsc:(e + 1) * nsc], stream)
+        return cls(packed, scales, E, K, N)
+
+    def __call__(self, a, offsets, out=None, stream=None):
+        """a: [T, K] bf16 rows grouped by expert; offsets: int32 [E + 1] on the device."""
+        T, K = a.shape
+        if K != self.K or offsets.numel() != self.E + 1 or offsets.dtype != torch.int32:
+            raise ValueError("grouped GEMM: activation K or offsets do not match the weights")
+        y = out if out is not None else torch.empty((T, self.N), dtype=torch.bfloat16, device=a.device)
+        need = w4a16_grouped_workspace_bytes(self.E, T, self.N, K)
+        if need and (self._ws is None or self._ws.numel() * 4 < need):
+            self._ws = torch.empty((need + 3) // 4, dtype=torch.int32, device=a.device)
+        qgemm_w4a16_grouped(_bf16(a), offsets, self.packed, self.scales, y, self.E, T, self.N, K,
+                            self._ws if need else None, need, stream)
+        return y
 
 
 def quantize_activations(a, stream=None):

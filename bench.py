@@ -1,7 +1,7 @@
 """Benchmark: Llama-3-8B W4A16 decode step (129 quantized linears) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
-                    [--workload decode|large-batch|fp8|70b|pack-mse|moe]
+                    [--workload decode|large-batch|fp8|int8|70b|pack-mse|moe]
 
 One step is one pass of the whole hot path over one batch: the 129 W4A16
 GEMMs of a Llama-3-8B decode step (32 layers of qkv 4096->6144, o 4096->4096,
@@ -17,6 +17,7 @@ listed under "by_batch".  Other workloads (one line each):
   large-batch  the same stack at B in {32 .. 1024} against a dense bf16 stack
                (hipBLASLt through torch.matmul), MFMA utilisation and crossover
   fp8          the W8A8-FP8 stack (per-token activation quantization + fp8 GEMM)
+  int8         the W8A8-INT8 stack (per-token activation quantization + int8 GEMM)
   70b          the Llama-3-70B W4A16 stack on one GPU
   pack-mse     offline INT4 g128 packing of the Llama-3-8B weights with
                MSE-optimal clipping (100-point grid), against abs-max packing
@@ -72,7 +73,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--batch", type=int, default=16)
-    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "70b", "pack-mse", "moe"])
+    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "int8", "70b", "pack-mse", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-chain", action="store_true",
                    help="decode workload: skip the chained-launch timing")
@@ -95,12 +96,13 @@ def parse():
 class Stack:
     """The packed weights, activations and outputs of one decode step."""
 
-    def __init__(self, ops, synth, torch, model, batches, fp8=False):
+    def __init__(self, ops, synth, torch, model, batches, fp8=False, int8=False):
         self.torch = torch
         self.ops = ops
         self.shapes = synth.stack_shapes(model)
         self.batches = batches
         self.fp8 = fp8
+        self.int8 = int8
         dev = torch.device("cuda:0")
         self.layers = []
         maxb = max(batches)
@@ -108,14 +110,24 @@ class Stack:
             layer, j = divmod(idx, 4)
             seed = synth.weight_seed(layer, j)
             w = synth.normal_bf16_device((K, N), seed, synth.WEIGHT_STD, dev)
-            wt = ops.Fp8Weight.from_bf16(w) if fp8 else ops.Int4G128Weight.from_bf16(w)
+            if fp8:
+                wt = ops.Fp8Weight.from_bf16(w)
+            elif int8:
+                wt = ops.Int8Weight.from_bf16(w)
+            else:
+                wt = ops.Int4G128Weight.from_bf16(w)
             del w
             a = synth.normal_bf16_device((maxb, K), synth.activation_seed(layer, j), 1.0, dev)
             y = torch.empty((maxb, N), dtype=torch.bfloat16, device=dev)
-            lin = ops.W8A8Fp8Linear(wt) if fp8 else ops.W4A16Linear(wt)
-            rec = {"name": name, "K": K, "N": N, "w": wt, "a": a, "y": y, "lin": lin}
             if fp8:
-                rec["qa"] = torch.empty((maxb, K), dtype=torch.uint8, device=dev)
+                lin = ops.W8A8Fp8Linear(wt)
+            elif int8:
+                lin = ops.W8A8Int8Linear(wt)
+            else:
+                lin = ops.W4A16Linear(wt)
+            rec = {"name": name, "K": K, "N": N, "w": wt, "a": a, "y": y, "lin": lin}
+            if fp8 or int8:
+                rec["qa"] = torch.empty((maxb, K), dtype=torch.int8 if int8 else torch.uint8, device=dev)
                 rec["sa"] = torch.empty(maxb, dtype=torch.float32, device=dev)
             # allocate the largest workspace up front
             for b in batches:
@@ -130,7 +142,12 @@ class Stack:
                 continue
             a = r["a"][:B]
             y = r["y"][:B]
-            if self.fp8:
+            if self.int8:
+                ops.quant_act_per_token_int8(a, B, r["K"], r["qa"][:B], r["sa"][:B])
+                ws, nb = r["lin"].workspace(B)
+                ops.qgemm_w8a8_int8(r["qa"][:B], r["sa"][:B], r["w"].codes, r["w"].scales, y,
+                                    B, r["N"], r["K"], ws, nb)
+            elif self.fp8:
                 ops.quant_act_per_token(a, B, r["K"], r["qa"][:B], r["sa"][:B])
                 ws, nb = r["lin"].workspace(B)
                 ops.qgemm_w8a8_fp8(r["qa"][:B], r["sa"][:B], r["w"].codes, r["w"].scales, y,
@@ -140,7 +157,7 @@ class Stack:
                 ops.qgemm_w4a16(a, r["w"].packed, r["w"].scales, y, B, r["N"], r["K"], ws, nb)
 
     def bytes(self, B, only=None):
-        f = fp8_bytes if self.fp8 else w4a16_bytes
+        f = fp8_bytes if (self.fp8 or self.int8) else w4a16_bytes
         return sum(f(B, r["K"], r["N"]) for r in self.layers if only is None or only(r))
 
     def flops(self, B):
@@ -360,8 +377,8 @@ def main():
         run_decode(args, torch, ops, synth)
     elif args.workload == "large-batch":
         run_large_batch(args, torch, ops, synth)
-    elif args.workload == "fp8":
-        run_fp8(args, torch, ops, synth)
+    elif args.workload in ("fp8", "int8"):
+        run_fp8(args, torch, ops, synth, int8=args.workload == "int8")
     elif args.workload == "pack-mse":
         run_pack_mse(args, torch, ops, synth)
     elif args.workload == "moe":
@@ -515,9 +532,14 @@ def run_large_batch(args, torch, ops, synth):
     print(json.dumps(out), flush=True)
 
 
-def run_fp8(args, torch, ops, synth):
+INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA
+
+
+def run_fp8(args, torch, ops, synth, int8=False):
     batches = [1, 16, 128, 512, 1024]
-    stack = Stack(ops, synth, torch, "8b", batches, fp8=True)
+    stack = Stack(ops, synth, torch, "8b", batches, fp8=not int8, int8=int8)
+    fmt = "int8" if int8 else "fp8"
+    peak = INT8_PEAK_TOPS if int8 else FP8_PEAK_TFLOPS
     res = {}
     for B in batches:
         g = graph_of(torch, lambda: stack.step(B))
@@ -525,13 +547,16 @@ def run_fp8(args, torch, ops, synth):
         del g
         res[str(B)] = {"ms_per_step": round(ms, 4),
                        "TB_s": round(stack.bytes(B) / (ms * 1e-3) / 1e12, 3),
-                       "fp8_mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (FP8_PEAK_TFLOPS * 1e12), 4)}
-        print(f"[bench] fp8 B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
-    out = {"metric": "Llama-3-8B W8A8-FP8 decode-step ms vs batch", "value": res["16"]["TB_s"],
+                       f"{fmt}_mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (peak * 1e12), 4)}
+        print(f"[bench] {fmt} B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
+    FMT = fmt.upper()
+    out = {"metric": f"Llama-3-8B W8A8-{FMT} decode-step ms vs batch", "value": res["16"]["TB_s"],
            "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": res["16"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "e4m3 x e4m3 -> fp32 acc (fp8 MFMA)", "data": "synthetic",
-           "config": {"workload": "Llama-3-8B W8A8-FP8 stack incl. per-token activation quantization",
+           "vs_baseline": None,
+           "dtype": ("int8 x int8 -> int32 acc (int8 MFMA)" if int8 else "e4m3 x e4m3 -> fp32 acc (fp8 MFMA)"),
+           "data": "synthetic",
+           "config": {"workload": f"Llama-3-8B W8A8-{FMT} stack incl. per-token activation quantization",
                       "batch": 16}, "by_batch": res}
     print(json.dumps(out), flush=True)
 

@@ -313,6 +313,36 @@ qg_status qgemm_w8a8_fp8(const uint8_t *a_e4m3, const float *a_scale,
                          void *workspace, size_t workspace_bytes,
                          qg_stream stream);
 
+/*
+ * W8A8-INT8 -- the integer sibling of the fp8 path.
+ * [P2 3.4 "W8A8-INT": per-output-channel symmetric weights, s = max|w| / 127,
+ *  codes in [-127, 127]; dynamic per-token activations (the scheme the page
+ *  uses at 8B and 405B); 8-bit integer product with a 32-bit integer
+ *  accumulator, dequantized to 16 bits.]
+ *
+ * quant_act_per_token_int8: per row m, s_a[m] = float(amax_m) / 127.0f and
+ *   q = clamp(rne(a / s_a[m]), -127, 127) with an IEEE fp32 quotient; a zero
+ *   row gives s = 0 and codes 0.  K % 8 == 0.
+ * quant_weight_int8_per_channel: per column n the same map over the K rows,
+ *   written in the fp8 path's native order (quant_weight_fp8_per_channel),
+ *   byte for byte.
+ * qgemm_w8a8_int8: y[m, n] = bf16(float(sum_k qa[m,k] qw[k,n]) * s_a[m] * s_w[n]),
+ *   the sum exact in int32 (K <= 131072, else QG_ERR_SHAPE).  Workspace:
+ *   qg_w8a8_int8_workspace_bytes(M, N, K) bytes, zero-filled before first
+ *   use, the same layout and rules as qgemm_w8a8_fp8's (int32 slots).
+ */
+size_t qg_w8a8_int8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+qg_status quant_act_per_token_int8(const uint16_t *a_bf16, int M, int K,
+                                   int8_t *a_i8, float *a_scale, qg_stream stream);
+qg_status quant_weight_int8_per_channel(const uint16_t *w_bf16, int K, int N,
+                                        int8_t *w_i8, float *w_scale,
+                                        qg_stream stream);
+qg_status qgemm_w8a8_int8(const int8_t *a_i8, const float *a_scale,
+                          const int8_t *w_i8, const float *w_scale,
+                          uint16_t *y_bf16, int M, int N, int K,
+                          void *workspace, size_t workspace_bytes,
+                          qg_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

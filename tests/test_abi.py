@@ -190,6 +190,29 @@ def test_grouped_entry_point_validates(lib):
     assert g(*args(wsb=need - 4)) == QG_ERR_WORKSPACE
 
 
+def test_int8_entry_points_validate(lib):
+    raw = ctypes.CDLL(LIB)
+    V, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    g = raw.qgemm_w8a8_int8
+    g.restype, g.argtypes = I, [V, V, V, V, V, I, I, I, V, S, V]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4096, 4000, None, 0, None) == QG_ERR_SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 131072 + 128, None, 0, None) == QG_ERR_SHAPE  # int32 sum bound
+    assert g(FAKE, None, FAKE, FAKE, FAKE, 4, 4096, 4096, None, 0, None) == QG_ERR_NULL
+    assert g(FAKE + 2, FAKE, FAKE, FAKE, FAKE, 4, 4096, 4096, None, 0, None) == QG_ERR_ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, None, 0, 4096, 4096, None, 0, None) == QG_OK
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 200, 4096, 14336, None, 0, None) == QG_ERR_NULL   # needs workspace
+    assert lib.w8a8_int8_workspace_bytes(200, 4096, 14336) == lib.w8a8_workspace_bytes(200, 4096, 14336) > 0
+    assert lib.w8a8_int8_workspace_bytes(200, 16, 131072 + 128) == 0
+    aq = raw.quant_act_per_token_int8
+    aq.restype, aq.argtypes = I, [V, I, I, V, V, V]
+    assert aq(FAKE, 4, 12, FAKE, FAKE, None) == QG_ERR_SHAPE
+    assert aq(FAKE, 4, 4096, FAKE, None, None) == QG_ERR_NULL
+    wq = raw.quant_weight_int8_per_channel
+    wq.restype, wq.argtypes = I, [V, I, I, V, V, V]
+    assert wq(FAKE, 4096, 4100, FAKE, FAKE, None) == QG_ERR_SHAPE
+    assert wq(FAKE, 4096, 4096, FAKE + 1, FAKE, None) == QG_ERR_ALIGN
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     a = torch.zeros(4, 128, dtype=torch.bfloat16)

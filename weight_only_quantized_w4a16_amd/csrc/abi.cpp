@@ -11,6 +11,7 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 24;        // M, N
 constexpr int64_t kMaxK = int64_t(1) << 20;          // K
 constexpr int64_t kMaxElems = int64_t(1) << 38;      // elements of one matrix
+constexpr int64_t kMaxKInt8 = int64_t(1) << 17;      // int8 GEMM: 127^2 * K fits int32
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -255,6 +256,52 @@ qg_status qgemm_w8a8_fp8(const uint8_t* a_e4m3, const float* a_scale, const uint
     }
     qg::launch_qgemm_w8a8_fp8(a_e4m3, a_scale, w_e4m3, w_scale, y_bf16, M, N, K, workspace,
                               as_stream(stream));
+    return launched();
+}
+
+// ---- W8A8-INT8: the same kernels with int8 codes and int32 accumulation ----
+
+size_t qg_w8a8_int8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!shape_ok(M, N, K) || K > kMaxKInt8) return 0;
+    return qg::w8a8_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+qg_status quant_act_per_token_int8(const uint16_t* a_bf16, int M, int K, int8_t* a_i8,
+                                   float* a_scale, qg_stream stream) {
+    if (M < 0 || K <= 0 || K % 8 != 0 || M > kMaxDim || K > kMaxK) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    if (!a_bf16 || !a_i8 || !a_scale) return QG_ERR_NULL;
+    if (!aligned(a_bf16, 16) || !aligned(a_i8, 16) || !aligned(a_scale, 4)) return QG_ERR_ALIGN;
+    qg::launch_quant_act_per_token_i8(a_bf16, M, K, a_i8, a_scale, as_stream(stream));
+    return launched();
+}
+
+qg_status quant_weight_int8_per_channel(const uint16_t* w_bf16, int K, int N, int8_t* w_i8,
+                                        float* w_scale, qg_stream stream) {
+    if (!w_bf16 || !w_i8 || !w_scale) return QG_ERR_NULL;
+    if (!shape_ok(0, N, K)) return QG_ERR_SHAPE;
+    if (!aligned(w_bf16, 16) || !aligned(w_i8, 16) || !aligned(w_scale, 4)) return QG_ERR_ALIGN;
+    qg::launch_quant_weight_i8(w_bf16, K, N, w_i8, w_scale, as_stream(stream));
+    return launched();
+}
+
+qg_status qgemm_w8a8_int8(const int8_t* a_i8, const float* a_scale, const int8_t* w_i8,
+                          const float* w_scale, uint16_t* y_bf16, int M, int N, int K,
+                          void* workspace, size_t workspace_bytes, qg_stream stream) {
+    if (!shape_ok(M, N, K) || K > kMaxKInt8) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    if (!a_i8 || !a_scale || !w_i8 || !w_scale || !y_bf16) return QG_ERR_NULL;
+    if (!aligned(a_i8, 16) || !aligned(a_scale, 4) || !aligned(w_i8, 16) || !aligned(w_scale, 4) ||
+        !aligned(y_bf16, 16))
+        return QG_ERR_ALIGN;
+    const size_t need = qg::w8a8_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace) return QG_ERR_NULL;
+        if (workspace_bytes < need) return QG_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QG_ERR_ALIGN;
+    }
+    qg::launch_qgemm_w8a8_i8(a_i8, a_scale, w_i8, w_scale, y_bf16, M, N, K, workspace,
+                             as_stream(stream));
     return launched();
 }
 

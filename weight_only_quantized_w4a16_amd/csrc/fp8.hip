@@ -1,30 +1,72 @@
-// W8A8-FP8 on gfx950: per-token activation quantization, per-channel weight
-// quantization and the e4m3 x e4m3 GEMM on the fp8 MFMA.
+// W8A8 on gfx950 in two 8-bit formats: per-token activation quantization,
+// per-channel weight quantization and the 8-bit x 8-bit GEMM on the MFMA.
 //
-// Formulas from "Give Me BF16 or Give Me Death", section 3.4 "W8A8-FP":
-// symmetric, no zero point, Q(x) = s * rnd(x / s) with s = max|x| / q_max, one
-// scale per output channel for weights and one per token (row) for
-// activations, computed on the fly.  q_max = 448 (OCP e4m3fn, the fp8 format
-// gfx950 converts to and multiplies natively).  Quotients are IEEE fp32
-// divisions; the hardware conversion rounds to nearest-even and the value is
-// clamped to +-448 first, so the code saturates instead of becoming NaN.
+// Formulas from "Give Me BF16 or Give Me Death", section 3.4 ("W8A8-FP" and
+// "W8A8-INT"): symmetric, no zero point, Q(x) = s * rnd(x / s) with
+// s = max|x| / q_max, one scale per output channel for weights and one per
+// token (row) for activations, computed on the fly.  Quotients are IEEE fp32
+// divisions.
+//   e4m3: q_max = 448 (OCP e4m3fn, the fp8 format gfx950 converts to and
+//         multiplies natively); the hardware conversion rounds to
+//         nearest-even after a clamp to +-448, so the code saturates instead
+//         of becoming NaN; fp32 accumulation.
+//   int8: q_max = 127, codes rne(x / s) clamped to [-127, 127]; exact int32
+//         accumulation (|sum| <= 127^2 K, K <= 131072).
+// Both formats share every kernel: the weight order, the tiling and the LDS
+// pipelines are byte-oriented, and a 128-deep k-tile is one 16x16x128 fp8
+// MFMA or two 16x16x64 int8 MFMAs over the same two 16-byte halves of each
+// lane's operands.
 
 #include "device_common.h"
 #include "launch.h"
 
 namespace qg {
 
-// Two fp32 values -> two e4m3 bytes (low byte = first value).
-__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
-    a = fminf(fmaxf(a, -448.0f), 448.0f);
-    b = fminf(fmaxf(b, -448.0f), 448.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
-}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+struct FmtE4M3 {
+    static constexpr float qmax = 448.0f;
+    using acc_t = f32x4;
+    using elem_t = float;
+    // two fp32 quotients -> two codes (low byte = first value)
+    __device__ static __forceinline__ uint32_t encode2(float a, float b) {
+        a = fminf(fmaxf(a, -448.0f), 448.0f);
+        b = fminf(fmaxf(b, -448.0f), 448.0f);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+    }
+    // acc + A . B over one 128-deep k-tile; a0/b0 hold k = 16*(lane/16) + 0..15,
+    // a1/b1 the same 64 rows further
+    __device__ static __forceinline__ acc_t mma(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, acc_t c) {
+        return mfma_fp8_16x16x128(cat_i32x8(a0, a1), cat_i32x8(b0, b1), c);
+    }
+    __device__ static __forceinline__ acc_t zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ static __forceinline__ float value(elem_t x) { return x; }
+};
+
+struct FmtI8 {
+    static constexpr float qmax = 127.0f;
+    using acc_t = i32x4;
+    using elem_t = int;
+    __device__ static __forceinline__ uint32_t encode2(float a, float b) {
+        const int qa = (int)fminf(fmaxf(rintf(a), -127.0f), 127.0f);   // half to even
+        const int qb = (int)fminf(fmaxf(rintf(b), -127.0f), 127.0f);
+        return ((uint32_t)qa & 0xffu) | (((uint32_t)qb & 0xffu) << 8);
+    }
+    __device__ static __forceinline__ acc_t mma(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, acc_t c) {
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a0),
+                                                  __builtin_bit_cast(i32x4, b0), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a1),
+                                                     __builtin_bit_cast(i32x4, b1), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ acc_t zero() { return i32x4{0, 0, 0, 0}; }
+    __device__ static __forceinline__ float value(elem_t x) { return (float)x; }
+};
 
 // ---------------------------------------------------------------------------
 // quant_act_per_token: one workgroup per row; pass 1 finds the row's amax,
 // pass 2 re-reads the row (L2 resident) and writes codes.
 // ---------------------------------------------------------------------------
+template <class Fmt>
 __global__ __launch_bounds__(256) void quant_act_per_token_kernel(const uint16_t* __restrict__ a,
                                                                   int K, uint8_t* __restrict__ q,
                                                                   float* __restrict__ sa) {
@@ -48,7 +90,7 @@ __global__ __launch_bounds__(256) void quant_act_per_token_kernel(const uint16_t
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = amax / 448.0f;                           // IEEE fp32 quotient
+    const float s = amax / Fmt::qmax;                        // IEEE fp32 quotient
     if (tid == 0) sa[m] = s;
 
     uint2* out = reinterpret_cast<uint2*>(q + (size_t)m * K);
@@ -60,7 +102,7 @@ __global__ __launch_bounds__(256) void quant_act_per_token_kernel(const uint16_t
             uint32_t b[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                b[j] = e4m3x2(bf16_to_f32(w4[j] & 0xffffu) / s, bf16_to_f32(w4[j] >> 16) / s);
+                b[j] = Fmt::encode2(bf16_to_f32(w4[j] & 0xffffu) / s, bf16_to_f32(w4[j] >> 16) / s);
             o.x = b[0] | (b[1] << 16);
             o.y = b[2] | (b[3] << 16);
         }
@@ -70,7 +112,13 @@ __global__ __launch_bounds__(256) void quant_act_per_token_kernel(const uint16_t
 
 void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, float* s,
                                 hipStream_t st) {
-    hipLaunchKernelGGL(quant_act_per_token_kernel, dim3(M), dim3(256), 0, st, a, K, q, s);
+    hipLaunchKernelGGL(quant_act_per_token_kernel<FmtE4M3>, dim3(M), dim3(256), 0, st, a, K, q, s);
+}
+
+void launch_quant_act_per_token_i8(const uint16_t* a, int M, int K, int8_t* q, float* s,
+                                   hipStream_t st) {
+    hipLaunchKernelGGL(quant_act_per_token_kernel<FmtI8>, dim3(M), dim3(256), 0, st, a, K,
+                       reinterpret_cast<uint8_t*>(q), s);
 }
 
 // ---------------------------------------------------------------------------
@@ -79,7 +127,8 @@ void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, flo
 // 2 KiB tile: column 16*nt + l%16, rows 128*kt + 16*(l/16) .. +15 in the first
 // 16 bytes and rows 128*kt + 64 + 16*(l/16) .. +15 in the second.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* __restrict__ w,
+template <class Fmt>
+__global__ __launch_bounds__(256) void quant_weight_per_channel_kernel(const uint16_t* __restrict__ w,
                                                                int K, int N,
                                                                uint8_t* __restrict__ q,
                                                                float* __restrict__ sw) {
@@ -98,7 +147,7 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* _
     if (r == 0) {
         float m = 0.0f;
         for (int i = 0; i < 16; ++i) m = fmaxf(m, red[i][c]);
-        const float s = m / 448.0f;
+        const float s = m / Fmt::qmax;
         scol[c] = s;
         sw[n] = s;
     }
@@ -117,7 +166,7 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* _
             const int k = k0 + 64 * (i >> 3) + 2 * (i & 7);
             uint32_t v = 0u;
             if (s != 0.0f)
-                v = e4m3x2(bf16_to_f32(w[(size_t)k * N + ln]) / s,
+                v = Fmt::encode2(bf16_to_f32(w[(size_t)k * N + ln]) / s,
                            bf16_to_f32(w[(size_t)(k + 1) * N + ln]) / s);
             b[i] = v;
         }
@@ -134,7 +183,12 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const uint16_t* _
 
 void launch_quant_weight_fp8(const uint16_t* w, int K, int N, uint8_t* q, float* s,
                              hipStream_t st) {
-    hipLaunchKernelGGL(quant_weight_fp8_kernel, dim3(N / 16), dim3(256), 0, st, w, K, N, q, s);
+    hipLaunchKernelGGL(quant_weight_per_channel_kernel<FmtE4M3>, dim3(N / 16), dim3(256), 0, st, w, K, N, q, s);
+}
+
+void launch_quant_weight_i8(const uint16_t* w, int K, int N, int8_t* q, float* s, hipStream_t st) {
+    hipLaunchKernelGGL(quant_weight_per_channel_kernel<FmtI8>, dim3(N / 16), dim3(256), 0, st, w, K, N,
+                       reinterpret_cast<uint8_t*>(q), s);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,7 +198,7 @@ void launch_quant_weight_fp8(const uint16_t* w, int K, int N, uint8_t* q, float*
 // pieces of its A row (k = 16q .. +15 and 64 + 16q .. +15 for lane quarter q),
 // so each A load instruction reads 64 contiguous bytes per row.
 // ---------------------------------------------------------------------------
-template <int MT, int CT, int NWAVE, int U>
+template <class Fmt, int MT, int CT, int NWAVE, int U>
 __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
     const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
@@ -157,11 +211,12 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
     const int k_begin = (KT * wave) / NWAVE;
     const int k_end = (KT * (wave + 1)) / NWAVE;
 
-    f32x4 total[CT][MT];
+    using acc_t = typename Fmt::acc_t;
+    acc_t total[CT][MT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) total[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) total[ct][mt] = Fmt::zero();
 
     const u32x4* arow[MT];
     bool rowok[MT];
@@ -198,17 +253,16 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
             if (k0 + u < k_end) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const i32x8 bfr = cat_i32x8(wv[u][ct][0], wv[u][ct][1]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        total[ct][mt] = mfma_fp8_16x16x128(cat_i32x8(av[u][mt][0], av[u][mt][1]), bfr,
-                                                           total[ct][mt]);
+                        total[ct][mt] = Fmt::mma(av[u][mt][0], av[u][mt][1], wv[u][ct][0], wv[u][ct][1],
+                                                 total[ct][mt]);
                 }
             }
         }
     }
 
-    __shared__ f32x4 red[NWAVE][CT][MT][64];
+    __shared__ acc_t red[NWAVE][CT][MT][64];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -223,11 +277,11 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
         const int ct = cm / MT;
         const int m = mt * 16 + 4 * (l >> 4) + i;
         if (m >= M) continue;
-        float sum = 0.0f;
+        typename Fmt::elem_t sum = 0;
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) sum += red[w][ct][mt][l][i];
         const int n = (nt0 + ct) * 16 + (l & 15);
-        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum * sa[m] * sw[n]);
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(Fmt::value(sum) * sa[m] * sw[n]);
     }
 }
 
@@ -272,11 +326,12 @@ static int f8_cu_count() {
 #define QG_F8_NS1 4
 #endif
 
-template <int NS, int NB>
+template <class Fmt, int NS, int NB>
 __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
     const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K, int S,
-    float* __restrict__ part, unsigned* __restrict__ cnt) {
+    typename Fmt::elem_t* __restrict__ part, unsigned* __restrict__ cnt) {
+    using elem_t = typename Fmt::elem_t;
     constexpr int NTB = 8 * NB;                  // column tiles per workgroup
     constexpr int NI = 2 * NB;                   // column tiles per wave
     constexpr int NCOPY = 2 + 2 * NB;            // copies per thread per stage
@@ -341,11 +396,11 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         }
     };
 
-    f32x4 total[4][NI];
+    typename Fmt::acc_t total[4][NI];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) total[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ni = 0; ni < NI; ++ni) total[mi][ni] = Fmt::zero();
 
     int ld_kt = 0;
     auto step = [&](auto slot, bool live) {
@@ -364,11 +419,12 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
             return;
         }
         const Stage& S = stage(slot);
-        i32x8 bfr[NI];
+        u32x4 bfr[NI][2];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
             const int tl = wn * NI + ni;
-            bfr[ni] = cat_i32x8(S.w[tl * 128 + lane * 2], S.w[tl * 128 + lane * 2 + 1]);
+            bfr[ni][0] = S.w[tl * 128 + lane * 2];
+            bfr[ni][1] = S.w[tl * 128 + lane * 2 + 1];
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -385,9 +441,11 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
             }
             const int r = wm * 64 + mi * 16 + col;
             const int sw8 = (r >> 1) & 7;
-            const i32x8 af = cat_i32x8(S.a[r * 8 + (kq ^ sw8)], S.a[r * 8 + ((4 + kq) ^ sw8)]);
+            const u32x4 a0 = S.a[r * 8 + (kq ^ sw8)];
+            const u32x4 a1 = S.a[r * 8 + ((4 + kq) ^ sw8)];
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) total[mi][ni] = mfma_fp8_16x16x128(af, bfr[ni], total[mi][ni]);
+            for (int ni = 0; ni < NI; ++ni)
+                total[mi][ni] = Fmt::mma(a0, a1, bfr[ni][0], bfr[ni][1], total[mi][ni]);
         }
     };
 
@@ -415,13 +473,14 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const int m = m0 + wm * 64 + mi * 16 + 4 * kq + i;
                     if (m < M)
-                        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][ni][i] * sa[m] * swn);
+                        y[(size_t)m * N + n] =
+                            (uint16_t)f32_to_bf16_rne(Fmt::value(total[mi][ni][i]) * sa[m] * swn);
                 }
             }
         }
         return;
     }
-    // K split: unscaled fp32 totals to this slice's slot with agent-scope
+    // K split: unscaled totals (fp32 or int32) to this slice's slot with agent-scope
     // stores (coherent across the XCDs' L2s without cache maintenance)
     __shared__ int last_flag;
 #pragma unroll
@@ -453,19 +512,19 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         const int m = m0 + e / BN;
         const int n = n0 + e % BN;
         if (m >= M || n >= N) continue;
-        const float* src = part + (size_t)m * N + n;
-        float v = 0.0f;
+        const elem_t* src = part + (size_t)m * N + n;
+        elem_t v = 0;
         for (int k0 = 0; k0 < S; k0 += 4) {      // four loads in flight, then add in slice order
-            float pv[4];
+            elem_t pv[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 pv[k] = k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * M * N, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT)
-                                   : 0.0f;
+                                   : elem_t(0);
 #pragma unroll
             for (int k = 0; k < 4; ++k) v += pv[k];
         }
-        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v * sa[m] * sw[n]);
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(Fmt::value(v) * sa[m] * sw[n]);
     }
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -530,46 +589,60 @@ size_t w8a8_workspace_bytes(int M, int N, int K) {
     return f8_plan(M, N, K).bytes;
 }
 
-template <int MT, int CT>
+template <class Fmt, int MT, int CT>
 static void launch_small(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                          uint16_t* y, int M, int N, int K, hipStream_t st) {
     constexpr int NWAVE = 8;
     constexpr int U = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
-    hipLaunchKernelGGL((w8a8_small_m_kernel<MT, CT, NWAVE, U>), dim3(N / 16 / CT), dim3(NWAVE * 64),
-                       0, st, a, sa, w, sw, y, M, N, K);
+    hipLaunchKernelGGL((w8a8_small_m_kernel<Fmt, MT, CT, NWAVE, U>), dim3(N / 16 / CT),
+                       dim3(NWAVE * 64), 0, st, a, sa, w, sw, y, M, N, K);
 }
 
-template <int MT>
+template <class Fmt, int MT>
 static void launch_small_ct(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                             uint16_t* y, int M, int N, int K, hipStream_t st) {
     const int NT = N / 16;
     if (NT % 2 == 0 && NT >= 1024)
-        launch_small<MT, 2>(a, sa, w, sw, y, M, N, K, st);
+        launch_small<Fmt, MT, 2>(a, sa, w, sw, y, M, N, K, st);
     else
-        launch_small<MT, 1>(a, sa, w, sw, y, M, N, K, st);
+        launch_small<Fmt, MT, 1>(a, sa, w, sw, y, M, N, K, st);
+}
+
+template <class Fmt>
+static void launch_w8a8(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                        uint16_t* y, int M, int N, int K, void* ws, hipStream_t st) {
+    if (M <= 16) {
+        launch_small_ct<Fmt, 1>(a, sa, w, sw, y, M, N, K, st);
+    } else if (M <= 32) {
+        launch_small_ct<Fmt, 2>(a, sa, w, sw, y, M, N, K, st);
+    } else if (M <= 64) {
+        launch_small_ct<Fmt, 4>(a, sa, w, sw, y, M, N, K, st);
+    } else {
+        using elem_t = typename Fmt::elem_t;
+        static_assert(sizeof(elem_t) == sizeof(float), "slot size of the workspace plan");
+        const F8Plan p = f8_plan(M, N, K);
+        char* wsb = static_cast<char*>(ws);
+        elem_t* part = p.S > 1 ? reinterpret_cast<elem_t*>(wsb) : nullptr;
+        unsigned* cnt = p.S > 1 ? reinterpret_cast<unsigned*>(wsb + p.cnt_off) : nullptr;
+        const dim3 grid((unsigned)(p.tiles * p.S));
+        if (p.nb == 1)
+            hipLaunchKernelGGL((w8a8_large_m_kernel<Fmt, QG_F8_NS1, 1>), grid, dim3(512), 0, st, a, sa, w,
+                               sw, y, M, N, K, p.S, part, cnt);
+        else
+            hipLaunchKernelGGL((w8a8_large_m_kernel<Fmt, QG_F8_NS, 2>), grid, dim3(512), 0, st, a, sa, w,
+                               sw, y, M, N, K, p.S, part, cnt);
+    }
 }
 
 void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                            uint16_t* y, int M, int N, int K, void* ws, hipStream_t st) {
-    if (M <= 16) {
-        launch_small_ct<1>(a, sa, w, sw, y, M, N, K, st);
-    } else if (M <= 32) {
-        launch_small_ct<2>(a, sa, w, sw, y, M, N, K, st);
-    } else if (M <= 64) {
-        launch_small_ct<4>(a, sa, w, sw, y, M, N, K, st);
-    } else {
-        const F8Plan p = f8_plan(M, N, K);
-        char* wsb = static_cast<char*>(ws);
-        float* part = p.S > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
-        unsigned* cnt = p.S > 1 ? reinterpret_cast<unsigned*>(wsb + p.cnt_off) : nullptr;
-        const dim3 grid((unsigned)(p.tiles * p.S));
-        if (p.nb == 1)
-            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS1, 1>), grid, dim3(512), 0, st, a, sa, w, sw, y,
-                               M, N, K, p.S, part, cnt);
-        else
-            hipLaunchKernelGGL((w8a8_large_m_kernel<QG_F8_NS, 2>), grid, dim3(512), 0, st, a, sa, w, sw, y,
-                               M, N, K, p.S, part, cnt);
-    }
+    launch_w8a8<FmtE4M3>(a, sa, w, sw, y, M, N, K, ws, st);
+}
+
+void launch_qgemm_w8a8_i8(const int8_t* a, const float* sa, const int8_t* w, const float* sw,
+                          uint16_t* y, int M, int N, int K, void* ws, hipStream_t st) {
+    launch_w8a8<FmtI8>(reinterpret_cast<const uint8_t*>(a), sa, reinterpret_cast<const uint8_t*>(w), sw,
+                       y, M, N, K, ws, st);
 }
 
 }  // namespace qg

@@ -59,7 +59,12 @@ void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, flo
                                 hipStream_t st);
 void launch_quant_weight_fp8(const uint16_t* w, int K, int N, uint8_t* q, float* s,
                              hipStream_t st);
-size_t w8a8_workspace_bytes(int M, int N, int K);
+void launch_quant_act_per_token_i8(const uint16_t* a, int M, int K, int8_t* q, float* s,
+                                   hipStream_t st);
+void launch_quant_weight_i8(const uint16_t* w, int K, int N, int8_t* q, float* s, hipStream_t st);
+void launch_qgemm_w8a8_i8(const int8_t* a, const float* sa, const int8_t* w, const float* sw,
+                          uint16_t* y, int M, int N, int K, void* ws, hipStream_t st);
+size_t w8a8_workspace_bytes(int M, int N, int K);   // both 8-bit formats
 const char* w8a8_kernel_for(int M, int N, int K);
 void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w,
                            const float* sw, uint16_t* y, int M, int N, int K, void* ws,

@@ -51,6 +51,10 @@ _SIGS = {
     "quant_act_per_token": (_I, [_P, _I, _I, _P, _P, _P]),
     "quant_weight_fp8_per_channel": (_I, [_P, _I, _I, _P, _P, _P]),
     "qgemm_w8a8_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "qg_w8a8_int8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "quant_act_per_token_int8": (_I, [_P, _I, _I, _P, _P, _P]),
+    "quant_weight_int8_per_channel": (_I, [_P, _I, _I, _P, _P, _P]),
+    "qgemm_w8a8_int8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -161,6 +165,29 @@ def qgemm_w8a8_fp8(a_e4m3, a_scale, w_e4m3, w_scale, y_bf16, M, N, K, workspace=
                                                  _ptr(w_scale), _ptr(y_bf16), M, N, K,
                                                  _ptr(workspace), workspace_bytes,
                                                  _stream(stream)))
+
+
+def w8a8_int8_workspace_bytes(M, N, K):
+    return _lib.qg_w8a8_int8_workspace_bytes(M, N, K)
+
+
+def quant_act_per_token_int8(a_bf16, M, K, a_i8, a_scale, stream=None):
+    _check("quant_act_per_token_int8",
+           _lib.quant_act_per_token_int8(_ptr(a_bf16), M, K, _ptr(a_i8), _ptr(a_scale), _stream(stream)))
+
+
+def quant_weight_int8_per_channel(w_bf16, K, N, w_i8, w_scale, stream=None):
+    _check("quant_weight_int8_per_channel",
+           _lib.quant_weight_int8_per_channel(_ptr(w_bf16), K, N, _ptr(w_i8), _ptr(w_scale),
+                                              _stream(stream)))
+
+
+def qgemm_w8a8_int8(a_i8, a_scale, w_i8, w_scale, y_bf16, M, N, K, workspace=None,
+                    workspace_bytes=0, stream=None):
+    _check("qgemm_w8a8_int8", _lib.qgemm_w8a8_int8(_ptr(a_i8), _ptr(a_scale), _ptr(w_i8),
+                                                   _ptr(w_scale), _ptr(y_bf16), M, N, K,
+                                                   _ptr(workspace), workspace_bytes,
+                                                   _stream(stream)))
 
 
 # ---- tensor-level helpers (allocate outputs with torch, then call the above) --
@@ -317,6 +344,55 @@ class W8A8Fp8Linear:
                                                     device=a.device)
         ws, need = self.workspace(M)
         qgemm_w8a8_fp8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
+        return y
+
+
+class Int8Weight:
+    """A [K, N] weight as native per-channel int8 codes plus fp32 channel scales."""
+
+    def __init__(self, codes, scales, K, N):
+        self.codes, self.scales, self.K, self.N = codes, scales, K, N
+
+    @classmethod
+    def from_bf16(cls, w, stream=None):
+        K, N = w.shape
+        codes = torch.empty(K * N, dtype=torch.int8, device=w.device)
+        scales = torch.empty(N, dtype=torch.float32, device=w.device)
+        quant_weight_int8_per_channel(_bf16(w.contiguous()), K, N, codes, scales, stream)
+        return cls(codes, scales, K, N)
+
+
+def quantize_activations_int8(a, stream=None):
+    M, K = a.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=a.device)
+    s = torch.empty(M, dtype=torch.float32, device=a.device)
+    quant_act_per_token_int8(_bf16(a), M, K, q, s, stream)
+    return q, s
+
+
+class W8A8Int8Linear:
+    """y = bf16(s_a s_w (qa @ qw)) with int8 codes, per-token quantization of a on every call."""
+
+    def __init__(self, weight: Int8Weight):
+        self.w = weight
+        self._ws = None
+
+    def workspace(self, M):
+        need = w8a8_int8_workspace_bytes(M, self.w.N, self.w.K)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.w.codes.device)
+        return (self._ws, need) if need else (None, 0)
+
+    def __call__(self, a, out=None, stream=None, qa=None, sa=None):
+        M, K = a.shape
+        if K != self.w.K:
+            raise ValueError(f"activation K={K} != weight K={self.w.K}")
+        if qa is None:
+            qa, sa = quantize_activations_int8(a, stream)
+        y = out if out is not None else torch.empty((M, self.w.N), dtype=torch.bfloat16,
+                                                    device=a.device)
+        ws, need = self.workspace(M)
+        qgemm_w8a8_int8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
         return y
 
 

@@ -1,7 +1,7 @@
 """Benchmark: Llama-3-8B W4A16 decode step (129 quantized linears) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
-                    [--workload decode|large-batch|fp8|int8|70b|pack-mse|moe]
+                    [--workload decode|large-batch|fp8|int8|70b|pack-mse|moe|moe-w4a8]
 
 One step is one pass of the whole hot path over one batch: the 129 W4A16
 GEMMs of a Llama-3-8B decode step (32 layers of qkv 4096->6144, o 4096->4096,
@@ -24,6 +24,8 @@ listed under "by_batch".  Other workloads (one line each):
   moe          the routed-expert GEMMs of a Qwen3-30B-A3B decode step (48
                layers x {gate_up, down} over 128 experts, top-8 routing),
                expert-grouped W4A16
+  moe-w4a8     the same expert GEMMs as W4A8-FP8: per-token e4m3 quantization
+               of each GEMM's rows, then the grouped INT4 x e4m3 GEMM
 
 Algorithmic bytes of one W4A16 GEMM: K*N/2 (codes) + 2*N*K/128 (scales) +
 2*M*K (activations) + 2*M*N (outputs); flops: 2*M*N*K.
@@ -73,7 +75,8 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--batch", type=int, default=16)
-    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "int8", "70b", "pack-mse", "moe"])
+    p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "int8", "70b", "pack-mse", "moe",
+                                                     "moe-w4a8"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-chain", action="store_true",
                    help="decode workload: skip the chained-launch timing")
@@ -381,8 +384,8 @@ def main():
         run_fp8(args, torch, ops, synth, int8=args.workload == "int8")
     elif args.workload == "pack-mse":
         run_pack_mse(args, torch, ops, synth)
-    elif args.workload == "moe":
-        run_moe(args, torch, ops, synth)
+    elif args.workload in ("moe", "moe-w4a8"):
+        run_moe(args, torch, ops, synth, w4a8=args.workload == "moe-w4a8")
     else:
         run_70b(args, torch, ops, synth)
 
@@ -649,19 +652,23 @@ def run_pack_mse(args, torch, ops, synth):
     print(json.dumps(out), flush=True)
 
 
-def moe_bytes(offsets, K, N):
+def moe_bytes(offsets, K, N, w4a8=False):
     """Algorithmic bytes of one grouped GEMM: the weights of the experts that
-    receive rows, their activations and outputs."""
+    receive rows, their activations (bf16, or e4m3 codes + row scales) and
+    outputs."""
     active = int(np.sum(np.diff(offsets) > 0))
     T = int(offsets[-1])
-    return active * (K * N // 2 + 2 * N * (K // 128)) + 2 * T * K + 2 * T * N
+    act = T * K + 4 * T if w4a8 else 2 * T * K
+    return active * (K * N // 2 + 2 * N * (K // 128)) + act + 2 * T * N
 
 
-def cpu_baseline_moe(B):
+def cpu_baseline_moe(B, w4a8=False):
     """The oracle on layer 0 of the expert stack at batch B: both grouped GEMMs
     over the first 16 experts that receive rows (quantization untimed), scaled
     by the number of experts with rows and by 48 layers."""
     from oracle import int4_g128 as q4
+    from oracle import fp8_e4m3 as f8
+    from oracle import w4a8 as o_w4a8
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -677,12 +684,16 @@ def cpu_baseline_moe(B):
         ex = {e: q4.quantize(synth.weights(K, N, seed=synth.weight_seed(0, j) * 1000 + e))
               for e in active[:16]}
         t = time.perf_counter()
-        q4.grouped_gemm_ref(a, offsets, ex)
+        if w4a8:
+            qa, sa = f8.quant_act_per_token(a)
+            o_w4a8.grouped_gemm_ref(qa, sa, offsets, ex)
+        else:
+            q4.grouped_gemm_ref(a, offsets, ex)
         total += (time.perf_counter() - t) * len(active) / len(ex)
     return total * synth.QWEN3_MOE_LAYERS, threads
 
 
-def run_moe(args, torch, ops, synth):
+def run_moe(args, torch, ops, synth, w4a8=False):
     dev = torch.device("cuda:0")
     E, k, L = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK, synth.QWEN3_MOE_LAYERS
     batches = [1, 16, 64, 256, 1024]
@@ -695,18 +706,24 @@ def run_moe(args, torch, ops, synth):
             del w
             a = synth.normal_bf16_device((maxT, K), synth.activation_seed(layer, j), 1.0, dev)
             y = torch.empty((maxT, N), dtype=torch.bfloat16, device=dev)
-            gemms.append((name, K, N, gw, a, y))
+            q = (torch.empty((maxT, K), dtype=torch.uint8, device=dev),
+                 torch.empty(maxT, dtype=torch.float32, device=dev)) if w4a8 else None
+            gemms.append((name, K, N, gw, a, y, q))
     torch.cuda.synchronize()
     res = {}
     for B in batches:
         token, offsets = synth.moe_routing(B, E, k, seed=B)
         T = B * k
         off = torch.from_numpy(offsets).to(dev)
-        nbytes = sum(moe_bytes(offsets, K, N) for (_, K, N, *_r) in gemms)
+        nbytes = sum(moe_bytes(offsets, K, N, w4a8) for (_, K, N, *_r) in gemms)
 
         def step():
-            for (_, K, N, gw, a, y) in gemms:
-                gw(a[:T], off, out=y[:T])
+            for (_, K, N, gw, a, y, q) in gemms:
+                if w4a8:
+                    ops.quant_act_per_token(a[:T], T, K, q[0][:T], q[1][:T])
+                    gw.w4a8(q[0][:T], q[1][:T], off, out=y[:T])
+                else:
+                    gw(a[:T], off, out=y[:T])
         g = graph_of(torch, step)
         ms = time_graph(torch, g, args.steps, args.warmup)
         del g
@@ -718,25 +735,32 @@ def run_moe(args, torch, ops, synth):
     r = res[str(B)]
     per_launch_us = r["ms_per_step"] * 1e3 / len(gemms)
     achieved = r["bytes"] / len(gemms) / (per_launch_us * 1e-6) / 1e9
-    out = {"metric": "Qwen3-30B-A3B routed-expert W4A16 decode step: HBM TB/s", "value": r["TB_s"],
+    fmt = "W4A8-FP8" if w4a8 else "W4A16"
+    out = {"metric": f"Qwen3-30B-A3B routed-expert {fmt} decode step: HBM TB/s", "value": r["TB_s"],
            "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)",
+           "vs_baseline": None,
+           "dtype": ("int4-g128 x e4m3 -> fp32 acc (fp8 MFMA)" if w4a8
+                     else "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)"),
            "data": "synthetic: weights N(0, 0.02^2), activations N(0, 1), seeded uniform top-8 routing",
            "config": {"workload": "Qwen3-30B-A3B routed experts: 48 layers x {gate_up 2048->1536, "
-                                  "down 768->2048} x 128 experts, top-8, expert-grouped W4A16 "
-                                  "(attention, router and shared layers excluded)", "batch": B},
+                                  f"down 768->2048}} x 128 experts, top-8, expert-grouped {fmt}"
+                                  + (" incl. per-token e4m3 quantization of each GEMM's rows" if w4a8 else "")
+                                  + " (attention, router and shared layers excluded)", "batch": B},
            "by_batch": res,
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                        "kernel": "grouped_items_kernel + w4a16_grouped_kernel per GEMM (96 per step)",
+                        "kernel": ("quant_act_per_token + grouped_items_kernel + w4a8_grouped_kernel"
+                                   if w4a8 else "grouped_items_kernel + w4a16_grouped_kernel")
+                                  + " per GEMM (96 per step)",
                         "avg_launch_us": round(per_launch_us, 3)}}
     if not args.no_cpu_baseline:
-        sec, threads = cpu_baseline_moe(B)
+        sec, threads = cpu_baseline_moe(B, w4a8)
         out["cpu_baseline"] = {"value": round(r["bytes"] / sec / 1e12, 6), "unit": "TB/s", "cores": threads,
                                "kind": "oracle", "seconds_per_step": round(sec, 2),
                                "sample": f"B={B}: layer 0, both grouped GEMMs over the first 16 experts "
-                                         f"with rows (fp32 dequant + fp64 matmul per expert), scaled to all "
+                                         f"with rows (" + ("per-token e4m3 quantization, " if w4a8 else "")
+                                         + "fp32 dequant + fp64 matmul per expert), scaled to all "
                                          f"experts with rows and x48 layers"}
     print(json.dumps(out), flush=True)
 

@@ -314,6 +314,33 @@ qg_status qgemm_w8a8_fp8(const uint8_t *a_e4m3, const float *a_scale,
                          qg_stream stream);
 
 /*
+ * W4A8-FP8 -- INT4 g128 weights (pack_int4_g128's native format) times
+ * dynamic per-token e4m3 activations (quant_act_per_token), on the fp8 MFMA.
+ * [P1, the mixture-of-experts section: engines pair INT4 weights with FP8
+ *  activations on expert layers; P2 3.4 "W4A16-INT" (weights) and "W8A8-FP"
+ *  (activations).]
+ *
+ * y[m, n] = bf16(s_a[m] * sum_g s_g * sum_{k in g} dec(qa[m,k]) (code[k,n] - 8)),
+ * fp32 accumulation: each 128-row group is one fp8 MFMA on the codes read as
+ * e4m3 bytes (code c is the e4m3 value c * 2^-9) plus the folded offset.
+ *
+ * qgemm_w4a8_fp8: any M >= 0 (rows in chunks of 16, 32 or 64).
+ * qgemm_w4a8_fp8_grouped: rows grouped by expert with device offsets, the
+ *   weights and scales of E experts back to back, and the workspace exactly as
+ *   qgemm_w4a16_grouped (qg_w4a16_grouped_workspace_bytes); a_scale is per
+ *   routed row.
+ */
+qg_status qgemm_w4a8_fp8(const uint8_t *a_e4m3, const float *a_scale,
+                         const uint32_t *packed, const uint16_t *scales,
+                         uint16_t *y_bf16, int M, int N, int K, qg_stream stream);
+qg_status qgemm_w4a8_fp8_grouped(const uint8_t *a_e4m3, const float *a_scale,
+                                 const int32_t *offsets, const uint32_t *packed,
+                                 const uint16_t *scales, uint16_t *y_bf16,
+                                 int E, int T, int N, int K,
+                                 void *workspace, size_t workspace_bytes,
+                                 qg_stream stream);
+
+/*
  * W8A8-INT8 -- the integer sibling of the fp8 path.
  * [P2 3.4 "W8A8-INT": per-output-channel symmetric weights, s = max|w| / 127,
  *  codes in [-127, 127]; dynamic per-token activations (the scheme the page

@@ -1,0 +1,114 @@
+"""GPU parity of the W4A8-FP8 path (INT4 g128 weights x per-token e4m3
+activations) against the oracle, dense and expert-grouped: max |err| <= 2e-2 x
+RMS of the fp64 oracle output per call (per expert for the grouped form)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import announce, assert_close_rms, dev_bf16, host_bits16
+from oracle import fp8_e4m3 as f8
+from oracle import int4_g128 as q4
+from oracle import w4a8
+from oracle.bf16 import f32_to_bf16_bits
+from weight_only_quantized_w4a16_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from weight_only_quantized_w4a16_amd import ops as _ops
+    return _ops
+
+
+def _dense(ops, a_bits, w_bits):
+    lin = ops.W4A8Linear(ops.Int4G128Weight.from_bf16(dev_bf16(w_bits)))
+    y = lin(dev_bf16(a_bits))
+    torch.cuda.synchronize()
+    return host_bits16(y)
+
+
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 48), (1280, 144), (4096, 512)])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 40, 64, 100])
+def test_w4a8_parity(ops, M, K, N):
+    announce(f"qgemm_w4a8_fp8 M={M} K={K} N={N}")
+    w = synth.weights(K, N, seed=17 + K + N)
+    a = synth.activations(M, K, seed=19 + M)
+    qa, sa = f8.quant_act_per_token(a)
+    codes, s = q4.quantize(w)
+    y = _dense(ops, a, w)
+    assert_close_rms(y, w4a8.gemm_ref(qa, sa, codes, s), what=f"w4a8 M={M} K={K} N={N}")
+
+
+def test_w4a8_every_code_and_subnormal_activation(ops):
+    """Weights that take all 15 abs-max codes (1..15; the codes 1..7 are e4m3
+    subnormals on the MFMA), and activation rows that hold e4m3 subnormals."""
+    announce("qgemm_w4a8_fp8 all codes, subnormal activations")
+    K, N = 256, 32
+    rng = np.random.default_rng(2)
+    levels = np.arange(-7, 8, dtype=np.float32)
+    w = levels[rng.integers(0, 15, (K, N))] * np.float32(0.01)
+    w[0::128, :] = 0.07                              # abs-max 0.07: s = bf16(0.01), every level reachable
+    wb = f32_to_bf16_bits(w)
+    table = f8.e4m3_decode_table()
+    a = rng.choice(table[1:16], size=(8, K)) * rng.choice([-1.0, 1.0], size=(8, K))
+    a[:, 0] = 448.0                                  # s_a = 1: codes are the values themselves
+    ab = f32_to_bf16_bits(a)
+    qa, sa = f8.quant_act_per_token(ab)
+    assert np.all(sa == 1.0)
+    codes, s = q4.quantize(wb)
+    assert len(np.unique(codes)) == 15
+    y = _dense(ops, ab, wb)
+    assert_close_rms(y, w4a8.gemm_ref(qa, sa, codes, s), what="w4a8 all codes")
+
+
+@pytest.mark.parametrize("j,name,K,N", [(0, "qkv", 4096, 6144), (3, "down", 14336, 4096)])
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_w4a8_llama3_shapes_sampled(ops, B, j, name, K, N):
+    announce(f"qgemm_w4a8_fp8 8B {name} B={B}")
+    w = synth.weights(K, N, seed=synth.weight_seed(0, j))
+    a = synth.activations(B, K, seed=synth.activation_seed(0, j))
+    y = _dense(ops, a, w)
+    cols = np.unique(np.random.default_rng(B).integers(0, N, 96))
+    qa, sa = f8.quant_act_per_token(a)
+    codes, s = q4.quantize(w[:, cols])
+    assert_close_rms(y[:, cols], w4a8.gemm_ref(qa, sa, codes, s), what=f"w4a8 {name} B={B}")
+
+
+@pytest.mark.parametrize("sizes,K,N", [([0, 1, 17, 0, 40, 3, 70, 5], 256, 64),
+                                       ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48)])
+def test_w4a8_grouped_ragged(ops, sizes, K, N):
+    announce(f"qgemm_w4a8_fp8_grouped sizes={sizes} K={K} N={N}")
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = int(offsets[-1])
+    w_list = [synth.weights(K, N, seed=400 + e) for e in range(len(sizes))]
+    a = synth.activations(T, K, seed=T + 3)
+    gw = ops.GroupedInt4Weight.from_bf16(torch.stack([dev_bf16(x) for x in w_list]))
+    qa_d, sa_d = ops.quantize_activations(dev_bf16(a))
+    y = host_bits16(gw.w4a8(qa_d, sa_d, torch.from_numpy(offsets).cuda()))
+    qa, sa = f8.quant_act_per_token(a)
+    for e in range(len(sizes)):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            ref = w4a8.grouped_gemm_ref(qa, sa, offsets, {e: q4.quantize(w_list[e])})[e]
+            assert_close_rms(y[r0:r1], ref, what=f"w4a8 expert {e}")
+
+
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_w4a8_grouped_qwen3_shapes(ops, B):
+    E, k = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK
+    name, K, N = synth.QWEN3_MOE_SHAPES[0]
+    announce(f"qgemm_w4a8_fp8_grouped qwen3 {name} B={B}")
+    token, offsets = synth.moe_routing(B, E, k, seed=B)
+    a = synth.activations(B, K, seed=11 + B)[token]
+    w = synth.normal_bf16_device((E, K, N), seed=77, std=synth.WEIGHT_STD, device="cuda")
+    gw = ops.GroupedInt4Weight.from_bf16(w)
+    qa_d, sa_d = ops.quantize_activations(dev_bf16(a))
+    y = host_bits16(gw.w4a8(qa_d, sa_d, torch.from_numpy(offsets).cuda()))
+    qa, sa = f8.quant_act_per_token(a)
+    nonempty = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+    for e in nonempty[:: max(1, len(nonempty) // 5)]:
+        r0, r1 = offsets[e], offsets[e + 1]
+        ref = w4a8.grouped_gemm_ref(qa, sa, offsets, {e: q4.quantize(host_bits16(w[e]))})[e]
+        assert_close_rms(y[r0:r1], ref, what=f"w4a8 qwen3 B={B} expert {e}")

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libqgemm.so")
-SOURCES = ["abi.cpp", "w4a16.hip", "fp8.hip", "chain.hip"]
+SOURCES = ["abi.cpp", "w4a16.hip", "fp8.hip", "w4a8.hip", "chain.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

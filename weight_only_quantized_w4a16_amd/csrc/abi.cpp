@@ -259,6 +259,38 @@ qg_status qgemm_w8a8_fp8(const uint8_t* a_e4m3, const float* a_scale, const uint
     return launched();
 }
 
+// ---- W4A8-FP8: INT4 g128 weights x per-token e4m3 activations ----
+
+qg_status qgemm_w4a8_fp8(const uint8_t* a_e4m3, const float* a_scale, const uint32_t* packed,
+                         const uint16_t* scales, uint16_t* y_bf16, int M, int N, int K,
+                         qg_stream stream) {
+    if (!shape_ok(M, N, K) || (M + 63) / 64 > 65535) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    if (!a_e4m3 || !a_scale || !packed || !scales || !y_bf16) return QG_ERR_NULL;
+    if (!aligned(a_e4m3, 16) || !aligned(a_scale, 4) || !aligned(packed, 16) || !aligned(scales, 4) ||
+        !aligned(y_bf16, 16))
+        return QG_ERR_ALIGN;
+    qg::launch_qgemm_w4a8_fp8(a_e4m3, a_scale, packed, scales, y_bf16, M, N, K, as_stream(stream));
+    return launched();
+}
+
+qg_status qgemm_w4a8_fp8_grouped(const uint8_t* a_e4m3, const float* a_scale, const int32_t* offsets,
+                                 const uint32_t* packed, const uint16_t* scales, uint16_t* y_bf16,
+                                 int E, int T, int N, int K, void* workspace, size_t workspace_bytes,
+                                 qg_stream stream) {
+    if (!grouped_ok(E, T, N, K)) return QG_ERR_SHAPE;
+    if (T == 0) return QG_OK;
+    if (!a_e4m3 || !a_scale || !offsets || !packed || !scales || !y_bf16 || !workspace)
+        return QG_ERR_NULL;
+    if (!aligned(a_e4m3, 16) || !aligned(a_scale, 4) || !aligned(offsets, 4) || !aligned(packed, 16) ||
+        !aligned(scales, 4) || !aligned(y_bf16, 16) || !aligned(workspace, 4))
+        return QG_ERR_ALIGN;
+    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T)) return QG_ERR_WORKSPACE;
+    qg::launch_qgemm_w4a8_fp8_grouped(a_e4m3, a_scale, offsets, packed, scales, y_bf16, E, T, N, K,
+                                      workspace, as_stream(stream));
+    return launched();
+}
+
 // ---- W8A8-INT8: the same kernels with int8 codes and int32 accumulation ----
 
 size_t qg_w8a8_int8_workspace_bytes(int64_t M, int64_t N, int64_t K) {

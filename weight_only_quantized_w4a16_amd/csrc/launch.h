@@ -23,10 +23,20 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
 // Expert-grouped W4A16 (w4a16.hip)
 constexpr int kGroupedMaxExperts = 1024;
 int w4a16_grouped_max_items(int E, int T);
+int w4a16_grouped_rows_per_item(int E, int T);
+void launch_grouped_items(const int* offsets, int E, int T, int R, int max_items, int* items,
+                          hipStream_t s);
 size_t w4a16_grouped_workspace_bytes(int E, int T);
 void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
                                 const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
                                 void* ws, hipStream_t s);
+
+// W4A8-FP8 (w4a8.hip)
+void launch_qgemm_w4a8_fp8(const uint8_t* qa, const float* sa, const uint32_t* wq,
+                           const uint16_t* sc, uint16_t* y, int M, int N, int K, hipStream_t s);
+void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int* offsets,
+                                   const uint32_t* wq, const uint16_t* sc, uint16_t* y, int E, int T,
+                                   int N, int K, void* ws, hipStream_t s);
 
 // Chained decode (chain.hip)
 struct ChainDesc {          // one GEMM of a chain as the kernel reads it (64 bytes)

@@ -1113,14 +1113,21 @@ static void launch_grouped_mt(const uint16_t* a, const int* items, const uint32_
                        dim3(NWAVE * 64), 0, s, a, items, wq, sc, y, N, K);
 }
 
+int w4a16_grouped_rows_per_item(int E, int T) { return 16 * grouped_mt(E, T); }
+
+void launch_grouped_items(const int* offsets, int E, int T, int R, int max_items, int* items,
+                          hipStream_t s) {
+    hipLaunchKernelGGL(grouped_items_kernel, dim3(1), dim3(64), 0, s, offsets, E, T, R, max_items,
+                       items);
+}
+
 void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
                                 const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
                                 void* ws, hipStream_t s) {
     const int MT = grouped_mt(E, T);
     const int max_items = grouped_max_items(E, T);
     int* items = static_cast<int*>(ws);
-    hipLaunchKernelGGL(grouped_items_kernel, dim3(1), dim3(64), 0, s, offsets, E, T, 16 * MT,
-                       max_items, items);
+    launch_grouped_items(offsets, E, T, 16 * MT, max_items, items, s);
     const int NT = N / 16;
     int ct = QG_GR_CT ? QG_GR_CT : small_ct(NT);
     while (NT % ct) ct >>= 1;

@@ -51,6 +51,8 @@ _SIGS = {
     "quant_act_per_token": (_I, [_P, _I, _I, _P, _P, _P]),
     "quant_weight_fp8_per_channel": (_I, [_P, _I, _I, _P, _P, _P]),
     "qgemm_w8a8_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "qgemm_w4a8_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "qgemm_w4a8_fp8_grouped": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
     "qg_w8a8_int8_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "quant_act_per_token_int8": (_I, [_P, _I, _I, _P, _P, _P]),
     "quant_weight_int8_per_channel": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -165,6 +167,19 @@ def qgemm_w8a8_fp8(a_e4m3, a_scale, w_e4m3, w_scale, y_bf16, M, N, K, workspace=
                                                  _ptr(w_scale), _ptr(y_bf16), M, N, K,
                                                  _ptr(workspace), workspace_bytes,
                                                  _stream(stream)))
+
+
+def qgemm_w4a8_fp8(a_e4m3, a_scale, packed, scales, y_bf16, M, N, K, stream=None):
+    _check("qgemm_w4a8_fp8", _lib.qgemm_w4a8_fp8(_ptr(a_e4m3), _ptr(a_scale), _ptr(packed), _ptr(scales),
+                                                 _ptr(y_bf16), M, N, K, _stream(stream)))
+
+
+def qgemm_w4a8_fp8_grouped(a_e4m3, a_scale, offsets_i32, packed, scales, y_bf16, E, T, N, K, workspace,
+                           workspace_bytes, stream=None):
+    _check("qgemm_w4a8_fp8_grouped",
+           _lib.qgemm_w4a8_fp8_grouped(_ptr(a_e4m3), _ptr(a_scale), _ptr(offsets_i32), _ptr(packed),
+                                       _ptr(scales), _ptr(y_bf16), E, T, N, K, _ptr(workspace),
+                                       workspace_bytes, _stream(stream)))
 
 
 def w8a8_int8_workspace_bytes(M, N, K):
@@ -311,6 +326,19 @@ class GroupedInt4Weight:
                             self._ws if need else None, need, stream)
         return y
 
+    def w4a8(self, qa, sa, offsets, out=None, stream=None):
+        """The W4A8-FP8 product: qa [T, K] e4m3 codes and sa [T] from quant_act_per_token."""
+        T, K = qa.shape
+        if K != self.K or offsets.numel() != self.E + 1 or offsets.dtype != torch.int32:
+            raise ValueError("grouped GEMM: activation K or offsets do not match the weights")
+        y = out if out is not None else torch.empty((T, self.N), dtype=torch.bfloat16, device=qa.device)
+        need = w4a16_grouped_workspace_bytes(self.E, T, self.N, K)
+        if need and (self._ws is None or self._ws.numel() * 4 < need):
+            self._ws = torch.empty((need + 3) // 4, dtype=torch.int32, device=qa.device)
+        qgemm_w4a8_fp8_grouped(qa, sa, offsets, self.packed, self.scales, y, self.E, T, self.N, K,
+                               self._ws if need else None, need, stream)
+        return y
+
 
 def quantize_activations(a, stream=None):
     M, K = a.shape
@@ -344,6 +372,23 @@ class W8A8Fp8Linear:
                                                     device=a.device)
         ws, need = self.workspace(M)
         qgemm_w8a8_fp8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
+        return y
+
+
+class W4A8Linear:
+    """y = bf16(s_a (qa @ w_hat)) for a packed INT4 g128 weight and e4m3 per-token activations."""
+
+    def __init__(self, weight: "Int4G128Weight"):
+        self.w = weight
+
+    def __call__(self, a, out=None, stream=None, qa=None, sa=None):
+        M, K = a.shape
+        if K != self.w.K:
+            raise ValueError(f"activation K={K} != weight K={self.w.K}")
+        if qa is None:
+            qa, sa = quantize_activations(a, stream)
+        y = out if out is not None else torch.empty((M, self.w.N), dtype=torch.bfloat16, device=a.device)
+        qgemm_w4a8_fp8(qa, sa, self.w.packed, self.w.scales, y, M, self.w.N, K, stream)
         return y
 
 

@@ -45,8 +45,9 @@ def _check(y, a_bits, offsets, w_list, experts=None):
 @pytest.mark.parametrize("sizes,K,N", [
     ([0, 1, 17, 0, 40, 3, 70, 5], 256, 64),          # mean 17 rows -> 32-row chunks
     ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48),        # mean <= 16 -> 16-row chunks
-    ([90, 33, 0, 65, 128], 128, 16),                   # mean > 32 -> 64-row chunks
-    ([0, 0, 200, 0], 512, 272),                        # one expert owns every row
+    ([90, 33, 0, 65, 128], 128, 16),                   # mean > 32 -> 128-row large-M items
+    ([0, 0, 200, 0], 512, 272),                        # one expert owns every row (large-M)
+    ([300, 0, 129, 40, 7], 1024, 1040),                # large-M: multi-chunk expert, ragged N
 ])
 def test_grouped_ragged(ops, sizes, K, N):
     announce(f"qgemm_w4a16_grouped sizes={sizes} K={K} N={N}")
@@ -58,7 +59,7 @@ def test_grouped_ragged(ops, sizes, K, N):
     _check(y, a, offsets, w_list)
 
 
-@pytest.mark.parametrize("B", [1, 16, 64, 256])
+@pytest.mark.parametrize("B", [1, 16, 64, 256, 1024])
 @pytest.mark.parametrize("name,K,N", synth.QWEN3_MOE_SHAPES)
 def test_grouped_qwen3_moe_shapes(ops, B, name, K, N):
     """128 experts of the real shape, seeded top-8 routing of B tokens; the

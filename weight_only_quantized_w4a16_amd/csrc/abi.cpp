@@ -84,7 +84,7 @@ size_t qg_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 size_t qg_w4a16_grouped_workspace_bytes(int64_t E, int64_t T, int64_t N, int64_t K) {
     if (!grouped_ok(E, T, N, K)) return 0;
-    return qg::w4a16_grouped_workspace_bytes((int)E, (int)T);
+    return qg::w4a16_grouped_workspace_bytes((int)E, (int)T, (int)K);
 }
 
 size_t qg_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -214,7 +214,7 @@ qg_status qgemm_w4a16_grouped(const uint16_t* a_bf16, const int32_t* offsets,
     if (!aligned(a_bf16, 16) || !aligned(offsets, 4) || !aligned(packed, 16) ||
         !aligned(scales, 4) || !aligned(y_bf16, 16) || !aligned(workspace, 4))
         return QG_ERR_ALIGN;
-    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T)) return QG_ERR_WORKSPACE;
+    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T, K)) return QG_ERR_WORKSPACE;
     qg::launch_qgemm_w4a16_grouped(a_bf16, offsets, packed, scales, y_bf16, E, T, N, K, workspace,
                                    as_stream(stream));
     return launched();
@@ -285,7 +285,7 @@ qg_status qgemm_w4a8_fp8_grouped(const uint8_t* a_e4m3, const float* a_scale, co
     if (!aligned(a_e4m3, 16) || !aligned(a_scale, 4) || !aligned(offsets, 4) || !aligned(packed, 16) ||
         !aligned(scales, 4) || !aligned(y_bf16, 16) || !aligned(workspace, 4))
         return QG_ERR_ALIGN;
-    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T)) return QG_ERR_WORKSPACE;
+    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T, K)) return QG_ERR_WORKSPACE;
     qg::launch_qgemm_w4a8_fp8_grouped(a_e4m3, a_scale, offsets, packed, scales, y_bf16, E, T, N, K,
                                       workspace, as_stream(stream));
     return launched();

@@ -543,6 +543,9 @@ const char* w8a8_kernel_for(int M, int N, int K) {
 }
 
 // Large-M plan: tile width, K split and workspace layout (slots | counters).
+#ifndef QG_F8_FORCE_NB             // 1 or 2: fixed tile width (0: chosen by launch rounds)
+#define QG_F8_FORCE_NB 0
+#endif
 #ifndef QG_F8_MAX_SPLIT            // largest K split of the large-M kernel
 #define QG_F8_MAX_SPLIT 8
 #endif
@@ -565,7 +568,7 @@ static F8Plan f8_plan(int M, int N, int K) {
     // 128-column tiles when 256-column tiles would take fewer, emptier rounds
     const int rounds256 = ((N + 255) / 256 * mb + cus - 1) / cus;
     const int rounds128 = ((N + 127) / 128 * mb + cus - 1) / cus;
-    p.nb = 8 * rounds128 < 14 * rounds256 ? 1 : 2;
+    p.nb = QG_F8_FORCE_NB ? QG_F8_FORCE_NB : (8 * rounds128 < 14 * rounds256 ? 1 : 2);
     p.tiles = (N + 128 * p.nb - 1) / (128 * p.nb) * mb;
     p.S = 1;
     if (p.tiles < cus && KT >= QG_F8_SPLIT_MIN_KT) {

@@ -26,7 +26,7 @@ int w4a16_grouped_max_items(int E, int T);
 int w4a16_grouped_rows_per_item(int E, int T);
 void launch_grouped_items(const int* offsets, int E, int T, int R, int max_items, int* items,
                           hipStream_t s);
-size_t w4a16_grouped_workspace_bytes(int E, int T);
+size_t w4a16_grouped_workspace_bytes(int E, int T, int K);
 void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
                                 const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
                                 void* ws, hipStream_t s);

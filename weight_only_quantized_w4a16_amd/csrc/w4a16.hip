@@ -752,11 +752,13 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 // ---------------------------------------------------------------------------
 constexpr int LM_BM = 128;
 
+// The work of one workgroup: output tile `tile` (of `tiles`) of K slice `split`.
 template <int NS, int NB>
-__global__ __launch_bounds__(512) void w4a16_large_m_kernel(
+__device__ __forceinline__ void large_m_tile(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
-    int M, int Mp, int N, int K, int S, float* __restrict__ part, unsigned* __restrict__ cnt) {
+    int M, int Mp, int N, int K, int S, float* __restrict__ part, unsigned* __restrict__ cnt,
+    int tiles, int split, int tile) {
     constexpr int BM = LM_BM;
     constexpr int NTB = 8 * NB;                  // column tiles per workgroup (NB 32-column blocks per wave)
     constexpr int NCOPY = 4 + NB;                // copies per thread per stage (wave 0: one more)
@@ -786,10 +788,8 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int mb = (M + BM - 1) / BM;
-    // grid = tiles x S K-slices; slice s holds groups [s*G/S, (s+1)*G/S)
-    const int tiles = gridDim.x / S;
-    const int split = blockIdx.x / tiles;
-    const int tile = xcd_tile(blockIdx.x - split * tiles, tiles);
+    // slice `split` holds groups [split*G/S, (split+1)*G/S)
+    (void)tiles;
     const int G = (K >> 7) / S;                  // groups of this slice (host: S divides K/128)
     const int gb = split * G;                    // first group of the slice
     const int Gall = K >> 7;
@@ -1012,10 +1012,48 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// grid = tiles x S K-slices
+template <int NS, int NB>
+__global__ __launch_bounds__(512) void w4a16_large_m_kernel(
+    const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
+    int M, int Mp, int N, int K, int S, float* __restrict__ part, unsigned* __restrict__ cnt) {
+    const int tiles = gridDim.x / S;
+    const int split = blockIdx.x / tiles;
+    const int tile = xcd_tile(blockIdx.x - split * tiles, tiles);
+    large_m_tile<NS, NB>(a, wq, sc, corr, y, M, Mp, N, K, S, part, cnt, tiles, split, tile);
+}
+
+// Expert-grouped, many rows per expert: one work item (expert, up to 128 rows)
+// per blockIdx.y, the expert's 128 x 128·NB column tiles along blockIdx.x; the
+// offset terms of all routed rows come from one pre-pass (corr[g][row], rows
+// padded so that a 128-row read from any item start stays inside).
+template <int NS, int NB>
+__global__ __launch_bounds__(512) void w4a16_grouped_large_kernel(
+    const uint16_t* __restrict__ a, const int* __restrict__ items, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
+    int Tp, int N, int K) {
+    const int it = blockIdx.y;
+    if (it >= items[0]) return;
+    const int e = items[1 + 3 * it];
+    const int r0 = items[2 + 3 * it];
+    const int rows = items[3 + 3 * it];
+    const size_t words = (size_t)(K / 8) * N;
+    const size_t nsc = (size_t)(K / 128) * N;
+    large_m_tile<NS, NB>(a + (size_t)r0 * K, wq + e * words, sc + e * nsc, corr + r0,
+                         y + (size_t)r0 * N, rows, Tp, N, K, 1, nullptr, nullptr, gridDim.x, 0,
+                         xcd_tile(blockIdx.x, gridDim.x));
+}
+
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple of this
+#ifndef QG_LM_NS                   // pipeline stages of the large-M kernel
+#define QG_LM_NS 3
+#endif
 
 
 // Tuning knobs of the small-M dispatch (compile-time; defaults measured on MI355X).
@@ -1098,8 +1136,27 @@ static int grouped_max_items(int E, int T) {
 
 int w4a16_grouped_max_items(int E, int T) { return T == 0 ? 0 : grouped_max_items(E, T); }
 
-size_t w4a16_grouped_workspace_bytes(int E, int T) {
-    return T == 0 ? 0 : (size_t)(1 + 3 * grouped_max_items(E, T)) * sizeof(int);
+// Many rows per expert: the large-M tile (128 x 256 per workgroup, the
+// activation tile shared by 256 columns) instead of the small-M tile, whose
+// workgroups each re-read all of their rows' activations for 64 columns.
+#ifndef QG_GR_LARGE_MIN            // mean rows per non-empty expert from which it runs
+#define QG_GR_LARGE_MIN 33
+#endif
+static bool grouped_large(int E, int T) {
+    const int active = T < E ? T : E;
+    return active > 0 && (T + active - 1) / active >= QG_GR_LARGE_MIN;
+}
+static int grouped_tp(int T) { return round_up(T + LM_BM, LM_MAX_BM); }   // corr rows
+static size_t grouped_corr_bytes(int E, int T, int K) {
+    if (!grouped_large(E, T)) return 0;
+    return ((size_t)(K / 128) * grouped_tp(T) * sizeof(float) + 255) / 256 * 256;
+}
+
+// corr (large path only) then the items; the item bound of the small tiles is
+// the larger one, so the same size serves every grouped path
+size_t w4a16_grouped_workspace_bytes(int E, int T, int K) {
+    if (T == 0) return 0;
+    return grouped_corr_bytes(E, T, K) + (size_t)(1 + 3 * grouped_max_items(E, T)) * sizeof(int);
 }
 
 template <int MT, int CT>
@@ -1124,6 +1181,24 @@ void launch_grouped_items(const int* offsets, int E, int T, int R, int max_items
 void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
                                 const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
                                 void* ws, hipStream_t s) {
+    if (grouped_large(E, T)) {
+        const int Tp = grouped_tp(T);
+        const int G = K / 128;
+        float* corr = static_cast<float*>(ws);
+        int* items = reinterpret_cast<int*>(static_cast<char*>(ws) + grouped_corr_bytes(E, T, K));
+        const int max_items = (T < E ? T : E) + (T + LM_BM - 1) / LM_BM;
+        const size_t n = (size_t)G * Tp;
+        hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           a, T, Tp, K, corr);
+        launch_grouped_items(offsets, E, T, LM_BM, max_items, items, s);
+        if (N >= 1024)
+            hipLaunchKernelGGL((w4a16_grouped_large_kernel<QG_LM_NS, 2>), dim3((N + 255) / 256, max_items),
+                               dim3(512), 0, s, a, items, wq, sc, corr, y, Tp, N, K);
+        else
+            hipLaunchKernelGGL((w4a16_grouped_large_kernel<QG_LM_NS, 1>), dim3((N + 127) / 128, max_items),
+                               dim3(512), 0, s, a, items, wq, sc, corr, y, Tp, N, K);
+        return;
+    }
     const int MT = grouped_mt(E, T);
     const int max_items = grouped_max_items(E, T);
     int* items = static_cast<int*>(ws);
@@ -1340,10 +1415,6 @@ static void launch_decode(const uint16_t* a, const uint32_t* wq, const uint16_t*
 }
 
 
-constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple of this
-#ifndef QG_LM_NS                   // pipeline stages of the large-M kernel
-#define QG_LM_NS 3
-#endif
 
 static int large_m_nb(int M, int N) {
     // One workgroup per CU at a time: a launch takes about ceil(tiles / CUs)

@@ -198,6 +198,20 @@ def time_graph(torch, g, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
+def replay_percentiles(torch, g, n=50):
+    """p10 / median / p90 of single replays, each bracketed by its own HIP events
+    (a pass of its own after the timed region)."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    return [round(float(np.percentile(t, q)), 4) for q in (10, 50, 90)]
+
+
 DOMINANT_KERNEL = "w4a16_decode_kernel"
 
 
@@ -431,6 +445,7 @@ def run_decode(args, torch, ops, synth):
             rec["chain_ms"] = round(ms_c, 4)
         g = graph_of(torch, lambda: stack.step(B))
         ms_g = time_graph(torch, g, args.steps, args.warmup)
+        rec["step_ms_p10_p50_p90"] = replay_percentiles(torch, g)
         del g
         rec["graph_ms"] = round(ms_g, 4)
         ms = ms_g

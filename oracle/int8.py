@@ -61,9 +61,16 @@ def quant_weight_per_channel(w_bits):
 
 
 def gemm_ref(qa, sa, qw, sw):
-    """Y64[m, n] = s_a[m] * s_w[n] * sum_k qa[m, k] qw[k, n] (I4): exact integer sum."""
-    acc = np.asarray(qa, np.int64) @ np.asarray(qw, np.int64)
-    return acc.astype(np.float64) * np.asarray(sa, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
+    """Y64[m, n] = s_a[m] * s_w[n] * sum_k qa[m, k] qw[k, n] (I4): exact integer sum.
+
+    The sum is formed by an fp64 matrix product, which is exact here: every
+    product and every partial sum is an integer of magnitude at most
+    127^2 * K < 2^31, far inside fp64's 2^53 exact-integer range.
+    """
+    if qa.shape[1] > MAX_K:
+        raise ValueError(f"K={qa.shape[1]} exceeds the int32 accumulator bound {MAX_K}")
+    acc = np.asarray(qa, np.float64) @ np.asarray(qw, np.float64)
+    return acc * np.asarray(sa, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
 
 
 def gemm_bruteforce(qa, sa, qw, sw):

@@ -106,6 +106,9 @@ def test_fp8_gemm_parity(ops, M, K, N):
     assert_close_rms(y, f8.gemm_ref(qa, sa, qw, sw), what=f"fp8 M={M} K={K} N={N}")
 
 
+_QW = {}
+
+
 @pytest.mark.parametrize("B", [1, 16, 128, 512, 1024])
 @pytest.mark.parametrize("j,name,K,N", [(1, "o", 4096, 4096), (3, "down", 14336, 4096)])
 def test_fp8_gemm_llama3_8b_shapes(ops, B, j, name, K, N):
@@ -115,7 +118,9 @@ def test_fp8_gemm_llama3_8b_shapes(ops, B, j, name, K, N):
     y = _fp8_gemm(ops, a, w)
     rows = np.unique(np.random.default_rng(B).integers(0, B, 32))
     qa, sa = f8.quant_act_per_token(a[rows])
-    qw, sw = f8.quant_weight_per_channel(w)
+    if j not in _QW:                                   # the oracle's weight codes, once per shape
+        _QW[j] = f8.quant_weight_per_channel(w)
+    qw, sw = _QW[j]
     assert_close_rms(y[rows], f8.gemm_ref(qa, sa, qw, sw), what=f"fp8 {name} B={B}")
 
 

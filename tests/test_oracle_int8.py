@@ -89,3 +89,16 @@ def test_roundtrip_error_bound():
 
 def test_accumulator_bound():
     assert 127 * 127 * i8.MAX_K < 2 ** 31 <= 127 * 127 * (i8.MAX_K * 2)
+
+
+def test_fp64_product_equals_the_integer_sum():
+    """Extreme codes (+-127 everywhere, K at the bound's scale): the fp64
+    product equals the exact integer sum computed with python integers."""
+    rng = np.random.default_rng(5)
+    K = 8192
+    qa = rng.choice(np.array([-127, 127], dtype=np.int8), size=(2, K))
+    qw = rng.choice(np.array([-127, -126, 125, 127], dtype=np.int8), size=(K, 3))
+    y = i8.gemm_ref(qa, np.ones(2, np.float32), qw, np.ones(3, np.float32))
+    for m in range(2):
+        for n in range(3):
+            assert y[m, n] == sum(int(a) * int(b) for a, b in zip(qa[m], qw[:, n]))

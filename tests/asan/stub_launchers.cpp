@@ -1,0 +1,60 @@
+// Host-only stand-ins for the gfx950 launchers of libqgemm (test
+// infrastructure): they record each call and touch no memory, so that the
+// C-ABI layer (abi.cpp) can be built and exercised under AddressSanitizer and
+// UndefinedBehaviorSanitizer on a machine without a GPU.  Size queries return
+// simple fixed formulas; the driver only relies on their being consistent
+// with what abi.cpp checks.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+int g_launches = 0;
+
+namespace qg {
+
+void launch_pack_int4_g128(const uint16_t*, int, int, uint32_t*, uint16_t*, hipStream_t) { ++g_launches; }
+void launch_pack_int4_g128_mse(const uint16_t*, int, int, int, uint32_t*, uint16_t*, hipStream_t) { ++g_launches; }
+void launch_dequant_int4_g128(const uint32_t*, const uint16_t*, int, int, uint16_t*, uint8_t*, hipStream_t) { ++g_launches; }
+size_t w4a16_workspace_bytes(int M, int, int) { return M > 64 ? 4096 : 0; }
+const char* w4a16_kernel_for(int, int, int) { return "stub"; }
+void launch_qgemm_w4a16(const uint16_t*, const uint32_t*, const uint16_t*, uint16_t*, int, int, int, void*,
+                        hipStream_t) { ++g_launches; }
+int w4a16_grouped_max_items(int E, int T) { return (T < E ? T : E) + (T + 15) / 16; }
+int w4a16_grouped_rows_per_item(int, int) { return 16; }
+void launch_grouped_items(const int*, int, int, int, int, int*, hipStream_t) { ++g_launches; }
+size_t w4a16_grouped_workspace_bytes(int E, int T, int) {
+    return T == 0 ? 0 : (size_t)(1 + 3 * w4a16_grouped_max_items(E, T)) * sizeof(int);
+}
+void launch_qgemm_w4a16_grouped(const uint16_t*, const int*, const uint32_t*, const uint16_t*, uint16_t*, int,
+                                int, int, int, void*, hipStream_t) { ++g_launches; }
+void launch_qgemm_w4a8_fp8(const uint8_t*, const float*, const uint32_t*, const uint16_t*, uint16_t*, int, int,
+                           int, hipStream_t) { ++g_launches; }
+void launch_qgemm_w4a8_fp8_grouped(const uint8_t*, const float*, const int*, const uint32_t*, const uint16_t*,
+                                   uint16_t*, int, int, int, int, void*, hipStream_t) { ++g_launches; }
+int chain_grid() { return 256; }
+bool chain_plan_one(int, int N, int K, int, ChainDesc* d, size_t* lds) {
+    d->N = N;
+    d->K = K;
+    d->units = 1;
+    d->kw = 1;
+    d->u = 1;
+    d->nchunks = 1;
+    *lds = 1024;
+    return true;
+}
+hipError_t launch_chain(const ChainDesc*, int, int, size_t, unsigned*, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+void launch_quant_act_per_token(const uint16_t*, int, int, uint8_t*, float*, hipStream_t) { ++g_launches; }
+void launch_quant_weight_fp8(const uint16_t*, int, int, uint8_t*, float*, hipStream_t) { ++g_launches; }
+void launch_quant_act_per_token_i8(const uint16_t*, int, int, int8_t*, float*, hipStream_t) { ++g_launches; }
+void launch_quant_weight_i8(const uint16_t*, int, int, int8_t*, float*, hipStream_t) { ++g_launches; }
+void launch_qgemm_w8a8_i8(const int8_t*, const float*, const int8_t*, const float*, uint16_t*, int, int, int,
+                          void*, hipStream_t) { ++g_launches; }
+size_t w8a8_workspace_bytes(int M, int, int) { return M > 64 ? 2048 : 0; }
+const char* w8a8_kernel_for(int, int, int) { return "stub"; }
+void launch_qgemm_w8a8_fp8(const uint8_t*, const float*, const uint8_t*, const float*, uint16_t*, int, int,
+                           int, void*, hipStream_t) { ++g_launches; }
+
+}  // namespace qg

@@ -81,7 +81,15 @@ def test_size_queries(lib):
     assert lib.w4a16_workspace_bytes(4, 4096, 4096) == 0
     assert lib.w4a16_workspace_bytes(32, 4096, 4096) == 0          # M <= 64: in-workgroup split-K
     assert lib.w4a16_workspace_bytes(1024, 4096, 4096) == 32 * 1024 * 4
-    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == 32 * 256 * 4   # offset terms, rows padded to 256
+    # short K, M = 100: 32 column tiles of 128 fill at most a quarter of the 256
+    # CUs, so K (32 groups) splits 4 ways, at least 8 groups per slice: offset
+    # terms (rows padded to 256), 4 fp32 slots of [M, N], one counter per tile
+    corr = 32 * 256 * 4
+    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == (corr + 4 * 100 * 4096 * 4 + 255) // 256 * 256 + 32 * 4
+    # short K with more tiles (M = 300: 3 x 32 tiles) does not split
+    assert lib.w4a16_workspace_bytes(300, 4096, 4096) == 32 * 512 * 4
+    assert lib.w8a8_workspace_bytes(100, 4096, 4096) == (4 * 100 * 4096 * 4 + 255) // 256 * 256 + 32 * 4
+    assert lib.w8a8_workspace_bytes(300, 4096, 4096) == 0
     # long K: offset terms, then K split 8 ways (32 column tiles of 128 on 256
     # CUs): 8 fp32 slots of [M, N], then one counter per tile
     corr = 112 * 256 * 4

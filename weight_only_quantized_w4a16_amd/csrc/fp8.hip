@@ -508,23 +508,42 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     if (!last_flag) return;
     constexpr int BN = 128 * NB;
     const int n0 = nt0 * 16;
-    for (int e = tid; e < F8_BM * BN; e += 512) {
-        const int m = m0 + e / BN;
-        const int n = n0 + e % BN;
-        if (m >= M || n >= N) continue;
-        const elem_t* src = part + (size_t)m * N + n;
-        elem_t v = 0;
-        for (int k0 = 0; k0 < S; k0 += 4) {      // four loads in flight, then add in slice order
-            elem_t pv[4];
+    // EB elements per thread at once, all their slot loads in flight together
+    // (one memory round trip per EB elements); each element adds its slots in
+    // slice order
+    constexpr int EB = 8;
+    for (int e0 = tid; e0 < F8_BM * BN; e0 += 512 * EB) {
+        elem_t v[EB];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                pv[k] = k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * M * N, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                   : elem_t(0);
+        for (int b = 0; b < EB; ++b) v[b] = elem_t(0);
+        for (int k0 = 0; k0 < S; k0 += 4) {
+            elem_t pv[EB][4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v += pv[k];
+            for (int b = 0; b < EB; ++b) {
+                const int e = e0 + b * 512;
+                const int m = m0 + e / BN;
+                const int n = n0 + e % BN;
+                const bool ok = e < F8_BM * BN && m < M && n < N;
+                const elem_t* src = part + (size_t)m * N + n;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    pv[b][k] = ok && k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * M * N,
+                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                : elem_t(0);
+            }
+#pragma unroll
+            for (int b = 0; b < EB; ++b)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[b] += pv[b][k];
         }
-        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(Fmt::value(v) * sa[m] * sw[n]);
+#pragma unroll
+        for (int b = 0; b < EB; ++b) {
+            const int e = e0 + b * 512;
+            const int m = m0 + e / BN;
+            const int n = n0 + e % BN;
+            if (e < F8_BM * BN && m < M && n < N)
+                y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(Fmt::value(v[b]) * sa[m] * sw[n]);
+        }
     }
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -555,6 +574,9 @@ const char* w8a8_kernel_for(int M, int N, int K) {
 #ifndef QG_F8_SPLIT_MIN_KPS        // ... keeping at least this many per slice
 #define QG_F8_SPLIT_MIN_KPS 14
 #endif
+#ifndef QG_F8_SHORT_MIN_KPS        // k-tiles per slice when short K is split
+#define QG_F8_SHORT_MIN_KPS 8
+#endif
 struct F8Plan {
     int nb, S, tiles;
     size_t cnt_off, bytes;
@@ -571,9 +593,15 @@ static F8Plan f8_plan(int M, int N, int K) {
     p.nb = QG_F8_FORCE_NB ? QG_F8_FORCE_NB : (8 * rounds128 < 14 * rounds256 ? 1 : 2);
     p.tiles = (N + 128 * p.nb - 1) / (128 * p.nb) * mb;
     p.S = 1;
-    if (p.tiles < cus && KT >= QG_F8_SPLIT_MIN_KT) {
+    // long K: split until the grid fills the CUs; short K only when the tiles
+    // would fill at most a quarter of the CUs (the fp32 partial sums are
+    // S x M x N written and read again)
+    const bool long_k = KT >= QG_F8_SPLIT_MIN_KT;
+    const bool sparse = 4LL * p.tiles <= cus && KT >= 2 * QG_F8_SHORT_MIN_KPS;
+    if (p.tiles < cus && (long_k || sparse)) {
+        const int min_kps = long_k ? QG_F8_SPLIT_MIN_KPS : QG_F8_SHORT_MIN_KPS;
         int best = 1;
-        for (int d = 2; d <= QG_F8_MAX_SPLIT && KT / d >= QG_F8_SPLIT_MIN_KPS; ++d) {
+        for (int d = 2; d <= QG_F8_MAX_SPLIT && KT / d >= min_kps; ++d) {
             if (KT % d) continue;
             best = d;
             if ((long long)p.tiles * d >= cus) break;

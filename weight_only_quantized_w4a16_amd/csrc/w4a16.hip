@@ -666,24 +666,42 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
                                             __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1));
     __syncthreads();
     if (!last_flag) return;
-    for (int e = tid; e < T * 256; e += DK_NWAVE * 64) {
-        const int tl = e >> 8;
-        const int r = e & 255;
-        const float* src = part + ((size_t)t0 + tl) * 256 + r;
-        float v = 0.0f;
-        for (int k0 = 0; k0 < S; k0 += 8) {      // 8 independent loads in flight, then add in order
-            float pv[8];
+    // each thread reduces EB elements at once: the loads of all of them (8 slots
+    // each) are in flight together, so the tail pays one memory round trip per
+    // EB elements; every element still adds its slots in slice order
+    constexpr int EB = 4;
+    for (int e0 = tid; e0 < T * 256; e0 += DK_NWAVE * 64 * EB) {
+        float v[EB];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                pv[k] = k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * NT * 256,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+        for (int b = 0; b < EB; ++b) v[b] = 0.0f;
+        for (int k0 = 0; k0 < S; k0 += 8) {
+            float pv[EB][8];
+#pragma unroll
+            for (int b = 0; b < EB; ++b) {
+                const int e = e0 + b * DK_NWAVE * 64;
+                const float* src = part + (size_t)t0 * 256 + e;
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    pv[b][k] = e < T * 256 && k0 + k < S
+                                   ? __hip_atomic_load(src + (size_t)(k0 + k) * NT * 256, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
                                    : 0.0f;
+            }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v += pv[k];
+            for (int b = 0; b < EB; ++b)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[b] += pv[b][k];
         }
-        const int m = 4 * ((r >> 2) >> 4) + (r & 3);
-        const int n = (t0 + tl) * 16 + ((r >> 2) & 15);
-        if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+#pragma unroll
+        for (int b = 0; b < EB; ++b) {
+            const int e = e0 + b * DK_NWAVE * 64;
+            if (e >= T * 256) continue;
+            const int tl = e >> 8;
+            const int r = e & 255;
+            const int m = 4 * ((r >> 2) >> 4) + (r & 3);
+            const int n = (t0 + tl) * 16 + ((r >> 2) & 15);
+            if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v[b]);
+        }
     }
     if (tid == 0)                                // leave the counter zero for the next call
         __hip_atomic_store(&cnt[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -991,23 +1009,41 @@ __device__ __forceinline__ void large_m_tile(
     if (!last_flag) return;
     constexpr int BN = 128 * NB;
     const int n0 = nt0 * 16;
-    for (int e = tid; e < BM * BN; e += 512) {
-        const int m = m0 + e / BN;
-        const int n = n0 + e % BN;
-        if (m >= M || n >= N) continue;
-        const float* src = part + (size_t)m * N + n;
-        float v = 0.0f;
-        for (int k0 = 0; k0 < S; k0 += 4) {      // four loads in flight, then add in slice order
-            float pv[4];
+    // EB elements per thread at once, all their slot loads in flight together
+    // (one memory round trip per EB elements); each element adds its slots in
+    // slice order
+    constexpr int EB = 8;
+    for (int e0 = tid; e0 < BM * BN; e0 += 512 * EB) {
+        float v[EB];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                pv[k] = k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * M * N, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                   : 0.0f;
+        for (int b = 0; b < EB; ++b) v[b] = 0.0f;
+        for (int k0 = 0; k0 < S; k0 += 4) {
+            float pv[EB][4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v += pv[k];
+            for (int b = 0; b < EB; ++b) {
+                const int e = e0 + b * 512;
+                const int m = m0 + e / BN;
+                const int n = n0 + e % BN;
+                const bool ok = e < BM * BN && m < M && n < N;
+                const float* src = part + (size_t)m * N + n;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    pv[b][k] = ok && k0 + k < S ? __hip_atomic_load(src + (size_t)(k0 + k) * M * N,
+                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                : 0.0f;
+            }
+#pragma unroll
+            for (int b = 0; b < EB; ++b)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[b] += pv[b][k];
         }
-        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+#pragma unroll
+        for (int b = 0; b < EB; ++b) {
+            const int e = e0 + b * 512;
+            const int m = m0 + e / BN;
+            const int n = n0 + e % BN;
+            if (e < BM * BN && m < M && n < N) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v[b]);
+        }
     }
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1068,6 +1104,9 @@ constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple 
 #endif
 #ifndef QG_LM_SPLIT_MIN_GPS        // ... keeping at least this many per slice
 #define QG_LM_SPLIT_MIN_GPS 14
+#endif
+#ifndef QG_LM_SHORT_MIN_GPS        // groups per slice when short K is split
+#define QG_LM_SHORT_MIN_GPS 8
 #endif
 #ifndef QG_SM_NWAVE
 #define QG_SM_NWAVE 8
@@ -1443,12 +1482,17 @@ static LargePlan large_plan(int M, int N, int K) {
     p.Mp = round_up(M, LM_MAX_BM);
     p.S = 1;
     const int cus = device_cu_count();
-    // split long K (measured: with 32 groups the shorter slices and the partial
-    // sums cost more than the idle CUs) until the grid fills the CUs, keeping
-    // at least QG_LM_SPLIT_MIN_GPS groups per slice
-    if (p.tiles < cus && G >= QG_LM_SPLIT_MIN_G) {
+    // split long K until the grid fills the CUs, keeping at least
+    // QG_LM_SPLIT_MIN_GPS groups per slice.  Short K (32 groups) only when the
+    // tiles would fill at most a quarter of the CUs (measured: qkv and o at
+    // M = 128..256 gain 25-30 %; with more tiles the fp32 partial sums, S x M x N
+    // written and read again, cost more than the idle CUs)
+    const bool long_k = G >= QG_LM_SPLIT_MIN_G;
+    const bool sparse = M > 64 && 4LL * p.tiles <= cus && G >= 2 * QG_LM_SHORT_MIN_GPS;
+    if (p.tiles < cus && (long_k || sparse)) {
+        const int min_gps = long_k ? QG_LM_SPLIT_MIN_GPS : QG_LM_SHORT_MIN_GPS;
         int best = 1;
-        for (int d = 2; d <= QG_LM_MAX_SPLIT && G / d >= QG_LM_SPLIT_MIN_GPS; ++d) {
+        for (int d = 2; d <= QG_LM_MAX_SPLIT && G / d >= min_gps; ++d) {
             if (G % d) continue;
             best = d;
             if ((long long)p.tiles * d >= cus) break;

@@ -1291,6 +1291,9 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
 #ifndef QG_DK_SPLIT_TPS           // column tiles per strip when K is split across workgroups
 #define QG_DK_SPLIT_TPS 4
 #endif
+#ifndef QG_DK_SPLIT_KW            // most waves per tile when K is split across workgroups
+#define QG_DK_SPLIT_KW 2
+#endif
 #ifndef QG_DK_SPLIT_TARGET        // workgroups a K split aims for
 #define QG_DK_SPLIT_TARGET 256
 #endif
@@ -1388,19 +1391,24 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
         c.lds = lds; c.ok = true;
         return c;
     }
-    // narrow, slice too large for LDS: strips of SPLIT_TPS tiles, one wave per
-    // tile, the smallest K split that fits and gives enough workgroups
+    // narrow, slice too large for LDS: strips of SPLIT_TPS tiles, KW waves per
+    // tile (as many as keep every wave streaming), the smallest K split that
+    // fits and gives enough workgroups
     const int NS = NT / QG_DK_SPLIT_TPS > 0 ? NT / QG_DK_SPLIT_TPS : 1;
     const int tmax = (NT + NS - 1) / NS;
+    int kw1 = 1;
+    while (kw1 * 2 <= QG_DK_SPLIT_KW && kw1 * 2 * tmax <= DK_NWAVE) kw1 *= 2;
     // first pass: two workgroups fit per CU; second pass: one
     for (const size_t budget : {(size_t)QG_DK_SPLIT_LDS, (size_t)QG_DK_LDS_BUDGET}) {
         for (int S = 2; S <= G; ++S) {
             if (G % S) continue;
-            const size_t lds = decode_lds(M, G / S, tmax, 1, false);
+            int kw = kw1;
+            while (kw > 1 && (G / S) % kw) kw >>= 1;
+            const size_t lds = decode_lds(M, G / S, tmax, kw, false);
             if (lds > budget) continue;
             if ((long long)NS * S < QG_DK_SPLIT_TARGET && S < G) continue;
-            c.S = S; c.NS = NS; c.KW = 1; c.D = QG_DK_WIDE_D;
-            c.U = largest_u(G / S, ring_umax(c.D));
+            c.S = S; c.NS = NS; c.KW = kw; c.D = kw == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D;
+            c.U = largest_u(G / S / kw, ring_umax(c.D));
             c.lds = lds; c.ok = true;
             return c;
         }

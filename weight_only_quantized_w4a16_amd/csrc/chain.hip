@@ -169,21 +169,9 @@ __device__ void chain_gemm(const ChainDesc& d, int M, unsigned char* lds, unsign
                 *reinterpret_cast<u32x4*>(lds + (size_t)r * rowb + cc * 16) = v;
             }
             __syncthreads();
-            for (int p = tid; p < Gc * M; p += CH_NWAVE * 64) {
-                const int g = p / M;
-                const int m = p - g * M;
-                const u32x4* row = reinterpret_cast<const u32x4*>(lds + (size_t)m * rowb + g * 256);
-                float sum = 0.0f;
-#pragma unroll 4
-                for (int i = 0; i < 16; ++i) {
-                    const u32x4 v = row[i];
-                    sum += bf16_to_f32(v.x & 0xffffu) + bf16_to_f32(v.x >> 16);
-                    sum += bf16_to_f32(v.y & 0xffffu) + bf16_to_f32(v.y >> 16);
-                    sum += bf16_to_f32(v.z & 0xffffu) + bf16_to_f32(v.z >> 16);
-                    sum += bf16_to_f32(v.w & 0xffffu) + bf16_to_f32(v.w >> 16);
-                }
-                corr[g * 16 + m] = -136.0f * sum;
-            }
+            // the offset terms exactly as the single-GEMM decode kernel forms them
+            decode_offset_terms(lds, rowb, corr, lds + (size_t)min(col, M - 1) * rowb + kq * 16, M, Gc, tid,
+                                wave, col, kq, CH_NWAVE);
             __syncthreads();
         }
         // this chunk's items: each step prefetches the wave's next item (which

@@ -191,4 +191,44 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Offset terms of a staged activation slice: corr[g * 16 + m] = -136 * (sum of
+// row m's 128 activations of group g).  Above 8 rows on the MFMA: the staged
+// fragments (arow: this lane's row min(col, M-1), k-quarter kq) times a B
+// operand of bf16 -136 (exact products) give every column the same row sums,
+// and lane (col 0, kq) of the result holds rows 4kq .. 4kq+3.  Up to 8 rows a
+// thread per (group, row) adds the 128 values in order (measured: cheaper than
+// the MFMA pass when few rows need it).  The chained decode kernel uses the
+// same function, so both produce the same bits.
+__device__ __forceinline__ void decode_offset_terms(const unsigned char* lds, int rowb, float* corr,
+                                                    const unsigned char* arow, int M, int G, int tid,
+                                                    int wave, int col, int kq, int nwave) {
+    if (M > 8) {
+        const bf16x8 neg136 = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
+        for (int g = wave; g < G; g += nwave) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc = mfma_bf16_16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(arow + g * 256 + t * 64)),
+                                         neg136, acc);
+            if (col == 0) *reinterpret_cast<f32x4*>(corr + g * 16 + 4 * kq) = acc;
+        }
+        return;
+    }
+    for (int p = tid; p < G * M; p += nwave * 64) {
+        const int g = p / M;
+        const int m = p - g * M;
+        const u32x4* row = reinterpret_cast<const u32x4*>(lds + (size_t)m * rowb + g * 256);
+        float sum = 0.0f;
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const u32x4 v = row[i];
+            sum += bf16_to_f32(v.x & 0xffffu) + bf16_to_f32(v.x >> 16);
+            sum += bf16_to_f32(v.y & 0xffffu) + bf16_to_f32(v.y >> 16);
+            sum += bf16_to_f32(v.z & 0xffffu) + bf16_to_f32(v.z >> 16);
+            sum += bf16_to_f32(v.w & 0xffffu) + bf16_to_f32(v.w >> 16);
+        }
+        corr[g * 16 + m] = -136.0f * sum;
+    }
+}
+
 }  // namespace qg

@@ -566,25 +566,11 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
         }
     }
     __syncthreads();
-    for (int p = tid; p < Gs * M; p += DK_NWAVE * 64) {   // offset terms
-        const int g = p / M;
-        const int m = p - g * M;
-        const u32x4* row = reinterpret_cast<const u32x4*>(lds + (size_t)m * rowb + g * 256);
-        float sum = 0.0f;
-#pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-            const u32x4 v = row[i];
-            sum += bf16_to_f32(v.x & 0xffffu) + bf16_to_f32(v.x >> 16);
-            sum += bf16_to_f32(v.y & 0xffffu) + bf16_to_f32(v.y >> 16);
-            sum += bf16_to_f32(v.z & 0xffffu) + bf16_to_f32(v.z >> 16);
-            sum += bf16_to_f32(v.w & 0xffffu) + bf16_to_f32(v.w >> 16);
-        }
-        corr[g * 16 + m] = -136.0f * sum;
-    }
+    const unsigned char* arow = lds + (size_t)min(col, M - 1) * rowb + kq * 16;
+    decode_offset_terms(lds, rowb, corr, arow, M, Gs, tid, wave, col, kq, DK_NWAVE);
     __syncthreads();
 
     const Int4Unpacker unpack;
-    const unsigned char* arow = lds + (size_t)min(col, M - 1) * rowb + kq * 16;
     const float* crow = corr + 4 * kq;
     const int sidx = (col >> 1) << 2;            // ds_bpermute byte address of lane col/2
     const int shalf = (col & 1) << 4;

@@ -24,7 +24,10 @@ def ops():
     return _ops
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (4, 4096), (16, 14336), (37, 1000), (256, 4096)])
+# K spans every launch form: one wave per row (K <= 2048, 4096, 8192), one
+# workgroup per row (14336, 28672) and the two-pass kernel for longer rows
+@pytest.mark.parametrize("M,K", [(1, 128), (4, 4096), (16, 14336), (37, 1000), (256, 4096), (3, 8192),
+                                 (5, 28672), (2, 40960)])
 def test_act_quant_bit_exact(ops, M, K):
     announce(f"quant_act_per_token_int8 M={M} K={K}")
     a = synth.activations(M, K, seed=M + 2 * K)

@@ -110,15 +110,93 @@ __global__ __launch_bounds__(256) void quant_act_per_token_kernel(const uint16_t
     }
 }
 
+// The same quantization with the row held in registers between the amax and
+// the encoding, so the row is read from memory once: NT threads per row (64:
+// one wave per row, four rows per workgroup, no barrier; 256: one row per
+// workgroup), CPT 16-byte chunks per thread.  Codes and scales are those of the
+// two-pass kernel above (same operations on the same values).
+template <class Fmt, int NT, int CPT>
+__global__ __launch_bounds__(256) void quant_act_per_token_reg_kernel(const uint16_t* __restrict__ a,
+                                                                      int M, int K,
+                                                                      uint8_t* __restrict__ q,
+                                                                      float* __restrict__ sa) {
+    const int tid = threadIdx.x % NT;
+    const int m = NT == 64 ? blockIdx.x * 4 + (int)(threadIdx.x >> 6) : (int)blockIdx.x;
+    if (m >= M) return;                                      // whole waves (NT = 64) or workgroups
+    const u32x4* row = reinterpret_cast<const u32x4*>(a + (size_t)m * K);
+    const int chunks = K >> 3;
+    u32x4 v[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        v[i] = c < chunks ? row[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32(w4[j] & 0xffffu)));
+            amax = fmaxf(amax, fabsf(bf16_to_f32(w4[j] >> 16)));
+        }
+    }
+    amax = wave_max(amax);
+    if constexpr (NT == 256) {
+        __shared__ float red[4];
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+    const float s = amax / Fmt::qmax;                        // IEEE fp32 quotient
+    if (tid == 0) sa[m] = s;
+    uint2* out = reinterpret_cast<uint2*>(q + (size_t)m * K);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        if (c >= chunks) break;
+        uint2 o = make_uint2(0u, 0u);
+        if (s != 0.0f) {
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            uint32_t b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = Fmt::encode2(bf16_to_f32(w4[j] & 0xffffu) / s, bf16_to_f32(w4[j] >> 16) / s);
+            o.x = b[0] | (b[1] << 16);
+            o.y = b[2] | (b[3] << 16);
+        }
+        out[c] = o;
+    }
+}
+
+// rows up to 64 x 16 chunks (K <= 8192) on one wave each, up to 256 x 16
+// chunks (K <= 32768) on one workgroup each, longer rows on the two-pass kernel
+template <class Fmt>
+static void launch_quant_act(const uint16_t* a, int M, int K, uint8_t* q, float* s, hipStream_t st) {
+    const int chunks = K / 8;
+    const dim3 blk(256);
+    if (chunks <= 64 * 4)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 64, 4>), dim3((M + 3) / 4), blk, 0, st, a, M, K, q, s);
+    else if (chunks <= 64 * 8)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 64, 8>), dim3((M + 3) / 4), blk, 0, st, a, M, K, q, s);
+    else if (chunks <= 64 * 16)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 64, 16>), dim3((M + 3) / 4), blk, 0, st, a, M, K, q, s);
+    else if (chunks <= 256 * 8)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 256, 8>), dim3(M), blk, 0, st, a, M, K, q, s);
+    else if (chunks <= 256 * 16)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 256, 16>), dim3(M), blk, 0, st, a, M, K, q, s);
+    else
+        hipLaunchKernelGGL(quant_act_per_token_kernel<Fmt>, dim3(M), blk, 0, st, a, K, q, s);
+}
+
 void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, float* s,
                                 hipStream_t st) {
-    hipLaunchKernelGGL(quant_act_per_token_kernel<FmtE4M3>, dim3(M), dim3(256), 0, st, a, K, q, s);
+    launch_quant_act<FmtE4M3>(a, M, K, q, s, st);
 }
 
 void launch_quant_act_per_token_i8(const uint16_t* a, int M, int K, int8_t* q, float* s,
                                    hipStream_t st) {
-    hipLaunchKernelGGL(quant_act_per_token_kernel<FmtI8>, dim3(M), dim3(256), 0, st, a, K,
-                       reinterpret_cast<uint8_t*>(q), s);
+    launch_quant_act<FmtI8>(a, M, K, reinterpret_cast<uint8_t*>(q), s, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -81,20 +81,26 @@ def test_size_queries(lib):
     assert lib.w4a16_workspace_bytes(4, 4096, 4096) == 0
     assert lib.w4a16_workspace_bytes(32, 4096, 4096) == 0          # M <= 64: in-workgroup split-K
     assert lib.w4a16_workspace_bytes(1024, 4096, 4096) == 32 * 1024 * 4
-    # short K, M = 100: 32 column tiles of 128 fill at most a quarter of the 256
-    # CUs, so K (32 groups) splits 4 ways, at least 8 groups per slice: offset
-    # terms (rows padded to 256), 4 fp32 slots of [M, N], one counter per tile
+    # short K, M = 100: 128-row tiles would fill under half of the 256 CUs, so
+    # the tiles are 64 rows (2 x 32 tiles of 64 x 128); they fill at most a
+    # quarter, so K (32 groups) splits 4 ways, at least 8 groups per slice:
+    # offset terms (rows padded to 256), 4 fp32 slots of [M, N], one counter per tile
     corr = 32 * 256 * 4
-    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == (corr + 4 * 100 * 4096 * 4 + 255) // 256 * 256 + 32 * 4
-    # short K with more tiles (M = 300: 3 x 32 tiles) does not split
+    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == (corr + 4 * 100 * 4096 * 4 + 255) // 256 * 256 + 64 * 4
+    # short K with more tiles (M = 300: 5 x 32 tiles of 64 rows) does not split
     assert lib.w4a16_workspace_bytes(300, 4096, 4096) == 32 * 512 * 4
     assert lib.w8a8_workspace_bytes(100, 4096, 4096) == (4 * 100 * 4096 * 4 + 255) // 256 * 256 + 32 * 4
     assert lib.w8a8_workspace_bytes(300, 4096, 4096) == 0
-    # long K: offset terms, then K split 8 ways (32 column tiles of 128 on 256
-    # CUs): 8 fp32 slots of [M, N], then one counter per tile
+    # long K: offset terms, then K split 4 ways (2 x 32 tiles of 64 x 128 on
+    # 256 CUs): 4 fp32 slots of [M, N], then one counter per tile
     corr = 112 * 256 * 4
-    slots = 8 * 100 * 4096 * 4
-    assert lib.w4a16_workspace_bytes(100, 4096, 14336) == (corr + slots + 255) // 256 * 256 + 32 * 4
+    slots = 4 * 100 * 4096 * 4
+    assert lib.w4a16_workspace_bytes(100, 4096, 14336) == (corr + slots + 255) // 256 * 256 + 64 * 4
+    # 128-row tiles where they fill more than half of the CUs (M = 384, N = 8192:
+    # 3 x 64 tiles), K split 2 ways
+    corr = 224 * 512 * 4
+    slots = 2 * 384 * 8192 * 4
+    assert lib.w4a16_workspace_bytes(384, 8192, 28672) == (corr + slots + 255) // 256 * 256 + 192 * 4
     assert lib.w8a8_workspace_bytes(1024, 4096, 4096) == 0
     assert lib.w8a8_workspace_bytes(64, 4096, 14336) == 0             # small M: no split
     assert lib.w8a8_workspace_bytes(1024, 4096, 14336) == 0           # 256 tiles fill the CUs

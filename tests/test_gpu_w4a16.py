@@ -202,9 +202,12 @@ def test_gemm_llama3_70b_layer_shapes_sampled(ops, B, j, name, K, N):
     assert_close_rms(y[:, cols], q4.gemm_ref(a, codes, s), what=f"70B {name} B={B}")
 
 
-@pytest.mark.parametrize("B", [32, 48, 64, 128, 512, 1024])
-@pytest.mark.parametrize("j,name,K,N", [(0, "qkv", 4096, 6144), (2, "gate_up", 4096, 28672),
-                                        (3, "down", 14336, 4096)])
+# B spans the small-M kernels (17..64 rows where the large-M grid would not
+# cover the CUs), 64-row large-M tiles (M <= 64, or 128-row tiles filling at
+# most half of the CUs) and 128-row tiles
+@pytest.mark.parametrize("B", [24, 32, 48, 64, 96, 128, 192, 256, 512, 1024])
+@pytest.mark.parametrize("j,name,K,N", [(0, "qkv", 4096, 6144), (1, "o", 4096, 4096),
+                                        (2, "gate_up", 4096, 28672), (3, "down", 14336, 4096)])
 def test_gemm_large_batch_sampled_rows(ops, B, j, name, K, N):
     announce(f"qgemm_w4a16 8B {name} B={B}")
     w = synth.weights(K, N, seed=synth.weight_seed(0, j))
@@ -327,9 +330,11 @@ def test_decode_workspace_counters_reset(ops, M, K, N):
         assert np.array_equal(y, first)
 
 
-# tiles: 128-row x 128-column tiles these shapes use (too few for 256 CUs, so K is split)
-@pytest.mark.parametrize("M,K,N,tiles", [(200, 14336, 4096, 64), (48, 14336, 4096, 32),
-                                          (256, 28672, 8192, 128)])
+# tiles: output tiles these shapes use (too few for 256 CUs, so K is split):
+# 64 x 128 tiles at M = 200 (4 x 32) and M = 48 (1 x 32), 128 x 128 tiles at
+# M = 384, N = 8192 (3 x 64)
+@pytest.mark.parametrize("M,K,N,tiles", [(200, 14336, 4096, 128), (48, 14336, 4096, 32),
+                                          (384, 28672, 8192, 192)])
 def test_large_m_split_counters_reset(ops, M, K, N, tiles):
     """Large-M shapes whose tiles cannot fill the GPU split K across workgroups
     and count arrivals per tile (one 32-bit counter each, at the end of the

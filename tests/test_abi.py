@@ -89,7 +89,7 @@ def test_size_queries(lib):
     assert lib.w4a16_workspace_bytes(100, 4096, 4096) == (corr + 4 * 100 * 4096 * 4 + 255) // 256 * 256 + 64 * 4
     # short K with more tiles (M = 300: 5 x 32 tiles of 64 rows) does not split
     assert lib.w4a16_workspace_bytes(300, 4096, 4096) == 32 * 512 * 4
-    assert lib.w8a8_workspace_bytes(100, 4096, 4096) == (4 * 100 * 4096 * 4 + 255) // 256 * 256 + 32 * 4
+    assert lib.w8a8_workspace_bytes(100, 4096, 4096) == (4 * 100 * 4096 * 4 + 255) // 256 * 256 + 64 * 4
     assert lib.w8a8_workspace_bytes(300, 4096, 4096) == 0
     # long K: offset terms, then K split 4 ways (2 x 32 tiles of 64 x 128 on
     # 256 CUs): 4 fp32 slots of [M, N], then one counter per tile
@@ -104,9 +104,9 @@ def test_size_queries(lib):
     assert lib.w8a8_workspace_bytes(1024, 4096, 4096) == 0
     assert lib.w8a8_workspace_bytes(64, 4096, 14336) == 0             # small M: no split
     assert lib.w8a8_workspace_bytes(1024, 4096, 14336) == 0           # 256 tiles fill the CUs
-    # 64 tiles of 128 x 128, 112 k-tiles split 4 ways: 4 fp32 slots of [M, N],
-    # then one counter per tile
-    assert lib.w8a8_workspace_bytes(200, 4096, 14336) == (4 * 200 * 4096 * 4 + 255) // 256 * 256 + 64 * 4
+    # 128-row tiles would fill a quarter of the CUs: 128 tiles of 64 x 128, 112
+    # k-tiles split 2 ways: 2 fp32 slots of [M, N], then one counter per tile
+    assert lib.w8a8_workspace_bytes(200, 4096, 14336) == (2 * 200 * 4096 * 4 + 255) // 256 * 256 + 128 * 4
 
 
 FAKE = 0x100000          # 16-byte aligned, never dereferenced (validation fails first)

@@ -150,11 +150,12 @@ def test_fp8_deterministic(ops, M):
     assert np.array_equal(y1, y2)
 
 
-# (M, K, N, tiles, S): shapes whose 128 x 128 tiles cannot fill 256 CUs, so K
-# is split S ways; N = 1040 leaves a ragged last column tile, S = 5 a partial
-# group of four slots in the final reduction
-@pytest.mark.parametrize("M,K,N,tiles,S", [(200, 14336, 4096, 64, 4), (100, 14336, 1040, 9, 8),
-                                            (100, 10240, 1040, 9, 5), (300, 14336, 4096, 96, 4)])
+# (M, K, N, tiles, S): shapes whose tiles cannot fill 256 CUs, so K is split S
+# ways: 64 x 128 tiles where 128-row tiles would fill at most a quarter of the
+# CUs (M = 200, 100), 128 x 128 tiles at M = 300; N = 1040 leaves a ragged last
+# column tile, S = 5 a partial group of four slots in the final reduction
+@pytest.mark.parametrize("M,K,N,tiles,S", [(200, 14336, 4096, 128, 2), (100, 14336, 1040, 18, 8),
+                                            (100, 10240, 1040, 18, 5), (300, 14336, 4096, 96, 4)])
 def test_fp8_large_m_split_counters_reset(ops, M, K, N, tiles, S):
     """The K split writes unscaled fp32 slots and counts arrivals per tile (one
     32-bit counter each, after the slots); the last arriver applies the scales.

@@ -114,7 +114,8 @@ def test_int8_exact_integer_sums(ops):
         assert np.all(yf == 4096.0)
 
 
-@pytest.mark.parametrize("M,K,N,tiles,S", [(200, 14336, 4096, 64, 4), (100, 10240, 1040, 9, 5)])
+# 64 x 128 tiles (128-row tiles would fill at most a quarter of the CUs), K split S ways
+@pytest.mark.parametrize("M,K,N,tiles,S", [(200, 14336, 4096, 128, 2), (100, 10240, 1040, 18, 5)])
 def test_int8_large_m_split_counters_reset(ops, M, K, N, tiles, S):
     announce(f"qgemm_w8a8_int8 large-M split M={M} K={K} N={N}")
     nbytes = ops.w8a8_int8_workspace_bytes(M, N, K)

@@ -1294,6 +1294,9 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
 #ifndef QG_DK_SPLIT_TPS           // column tiles per strip when K is split across workgroups
 #define QG_DK_SPLIT_TPS 4
 #endif
+#ifndef QG_DK_SPLIT_MIN_M         // K split across workgroups from this many rows (else small-M)
+#define QG_DK_SPLIT_MIN_M 9
+#endif
 #ifndef QG_DK_SPLIT_KW            // most waves per tile when K is split across workgroups
 #define QG_DK_SPLIT_KW 2
 #endif
@@ -1361,8 +1364,11 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
         }
         for (int kw = kw0; kw >= 1; kw >>= 1) {
             if (G % kw) continue;
-            // strips: as many as the LDS allows resident, up to WIDE_PER_CU per CU
-            int per_cu = QG_DK_WIDE_PER_CU;
+            // strips: as many as the LDS allows resident, up to WIDE_PER_CU per CU;
+            // one per CU when each CU gets 4..15 tiles (measured: gate_up at
+            // B = 4 / 8 -4 / -7 %; the LM head with 31 tiles per CU and 70B qkv
+            // with 2.5 lose 1-26 %)
+            int per_cu = (NT >= 4 * cus && NT < 16 * cus) ? 1 : QG_DK_WIDE_PER_CU;
             size_t lds = 0;
             int NS = 0;
             for (; per_cu >= 1; --per_cu) {
@@ -1397,6 +1403,9 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
     // narrow, slice too large for LDS: strips of SPLIT_TPS tiles, KW waves per
     // tile (as many as keep every wave streaming), the smallest K split that
     // fits and gives enough workgroups
+    // up to 8 rows the small-M kernel, which reads a from L2, is faster (measured:
+    // 8B down at B = 8 12.1 -> 11.2 us, 70B down at B = 4 / 8 -5 / -7 %)
+    if (M < QG_DK_SPLIT_MIN_M) return c;
     const int NS = NT / QG_DK_SPLIT_TPS > 0 ? NT / QG_DK_SPLIT_TPS : 1;
     const int tmax = (NT + NS - 1) / NS;
     int kw1 = 1;

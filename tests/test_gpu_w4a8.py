@@ -76,8 +76,11 @@ def test_w4a8_llama3_shapes_sampled(ops, B, j, name, K, N):
     assert_close_rms(y[:, cols], w4a8.gemm_ref(qa, sa, codes, s), what=f"w4a8 {name} B={B}")
 
 
+# means of 23, 2.5 and 61 rows per non-empty expert: 16-, 32- and 64-row items;
+# 64-row items split the columns over the waves (N a multiple of 128)
 @pytest.mark.parametrize("sizes,K,N", [([0, 1, 17, 0, 40, 3, 70, 5], 256, 64),
-                                       ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48)])
+                                       ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48),
+                                       ([0, 65, 33, 0, 128, 7, 70], 384, 256)])
 def test_w4a8_grouped_ragged(ops, sizes, K, N):
     announce(f"qgemm_w4a8_fp8_grouped sizes={sizes} K={K} N={N}")
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -95,7 +98,7 @@ def test_w4a8_grouped_ragged(ops, sizes, K, N):
             assert_close_rms(y[r0:r1], ref, what=f"w4a8 expert {e}")
 
 
-@pytest.mark.parametrize("B", [1, 16, 64])
+@pytest.mark.parametrize("B", [1, 16, 64, 1024])
 def test_w4a8_grouped_qwen3_shapes(ops, B):
     E, k = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK
     name, K, N = synth.QWEN3_MOE_SHAPES[0]

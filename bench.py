@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--workload", default="decode", choices=["decode", "large-batch", "fp8", "int8", "70b", "pack-mse", "moe",
                                                      "moe-w4a8"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--batches", default="",
+                   help="large-batch workload: extra batch sizes to time, comma separated")
     p.add_argument("--no-chain", action="store_true",
                    help="decode workload: skip the chained-launch timing")
     p.add_argument("--only-batch", action="store_true",
@@ -512,6 +514,9 @@ def run_decode(args, torch, ops, synth):
 
 def run_large_batch(args, torch, ops, synth):
     batches = [32, 64, 128, 256, 384, 512, 1024]
+    if args.batches:
+        # extra batches (e.g. a finer sweep around the crossover), timed alongside
+        batches = sorted(set(batches) | {int(x) for x in args.batches.split(",")})
     stack = Stack(ops, synth, torch, "8b", batches)
     dev = torch.device("cuda:0")
     # the dense bf16 baseline: the same shapes, fresh bf16 weights (15.0 GB)
@@ -537,7 +542,12 @@ def run_large_batch(args, torch, ops, synth):
                        "bf16_mfma_frac": round(fl / (ms16 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
                        "w4a16_TB_s": round(stack.bytes(B) / (ms4 * 1e-3) / 1e12, 3)}
         print(f"[bench] B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
-    cross = next((int(b) for b in res if res[b]["w4a16_ms"] >= res[b]["bf16_ms"]), None)
+    # the smallest measured batch from which W4A16 is not faster at every larger one
+    cross = None
+    for b in sorted(res, key=int, reverse=True):
+        if res[b]["w4a16_ms"] < res[b]["bf16_ms"]:
+            break
+        cross = int(b)
     B = 512
     out = {"metric": "Llama-3-8B W4A16 decode-step ms & HBM TB/s vs batch; MFMA util at B>=512",
            "value": res["512"]["w4a16_mfma_frac"], "unit": "fraction of bf16 MFMA peak at B=512",

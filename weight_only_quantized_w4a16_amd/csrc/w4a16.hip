@@ -1517,10 +1517,24 @@ static LargePlan large_plan(int M, int N, int K) {
     const int G = K / 128;
     p.bm = large_m_bm(M, N, K);
     p.nb = large_m_nb(M, N, p.bm);
+    const int cus = device_cu_count();
+    // More than one launch round of 128-row tiles: 64 x 256 tiles when their
+    // rounds x group-step time is lower (the last round of 128-row tiles can be
+    // nearly empty: gate_up at M = 576 has 560 tiles of 128 x 256 on 256 CUs).
+    // Group-step times measured per GEMM (ns): 128 x 256 2030, 128 x 128
+    // 1200, 64 x 256 1220.
+    if (p.bm == LM_BM) {
+        auto tiles_of = [&](int bm, int nb) { return (N + 128 * nb - 1) / (128 * nb) * ((M + bm - 1) / bm); };
+        const int t_cur = tiles_of(LM_BM, p.nb);
+        if (t_cur > cus) {
+            const long long est_cur = (long long)((t_cur + cus - 1) / cus) * (p.nb == 2 ? 2030 : 1200);
+            const long long est_64 = (long long)((tiles_of(64, 2) + cus - 1) / cus) * 1220;
+            if (100 * est_64 < 97 * est_cur) { p.bm = 64; p.nb = 2; }
+        }
+    }
     p.tiles = ((N + 128 * p.nb - 1) / (128 * p.nb)) * ((M + p.bm - 1) / p.bm);
     p.Mp = round_up(M, LM_MAX_BM);
     p.S = 1;
-    const int cus = device_cu_count();
     // split long K until the grid fills the CUs, keeping at least
     // QG_LM_SPLIT_MIN_GPS groups per slice.  Short K (32 groups) only when the
     // tiles would fill at most a quarter of the CUs (measured: qkv and o at

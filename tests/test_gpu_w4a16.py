@@ -203,9 +203,10 @@ def test_gemm_llama3_70b_layer_shapes_sampled(ops, B, j, name, K, N):
 
 
 # B spans the small-M kernels (17..64 rows where the large-M grid would not
-# cover the CUs), 64-row large-M tiles (M <= 64, or 128-row tiles filling at
-# most half of the CUs) and 128-row tiles
-@pytest.mark.parametrize("B", [24, 32, 48, 64, 96, 128, 192, 256, 512, 1024])
+# cover the CUs), 64-row large-M tiles (M <= 64, 128-row tiles filling at most
+# half of the CUs, and gate_up at 570 / 576 rows where 64 x 256 tiles take
+# fewer launch rounds; 570 leaves a ragged last tile) and 128-row tiles
+@pytest.mark.parametrize("B", [24, 32, 48, 64, 96, 128, 192, 256, 512, 570, 576, 1024])
 @pytest.mark.parametrize("j,name,K,N", [(0, "qkv", 4096, 6144), (1, "o", 4096, 4096),
                                         (2, "gate_up", 4096, 28672), (3, "down", 14336, 4096)])
 def test_gemm_large_batch_sampled_rows(ops, B, j, name, K, N):

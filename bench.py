@@ -92,6 +92,9 @@ def parse():
                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                    help="derive HBM bytes per dominant-kernel launch from four rocprofv3 --pmc "
                         "runs and write the traffic summary under profiles/, then exit")
+    p.add_argument("--summarize-mfma", metavar="DIR",
+                   help="print the MFMA busy share per kernel from a rocprofv3 --pmc run of "
+                        "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE and exit")
     p.add_argument("--command", default="", help="command line recorded in summaries")
     return p.parse_args()
 
@@ -353,6 +356,51 @@ def summarize_traffic(dirs, command):
     print("\n".join(lines))
 
 
+def summarize_mfma(dirname, command):
+    """MFMA busy share of the library's kernels from one rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA and GRBM_GUI_ACTIVE: busy cycles over
+    the SIMD cycles of each dispatch (GRBM_GUI_ACTIVE counts every XCD's cycles,
+    so one XCD's clock count is GRBM_GUI_ACTIVE / 8; the GPU has 256 CUs x 4
+    SIMDs), and the clock that implies."""
+    import collections
+    rows = _pmc_rows(dirname)
+    per = collections.defaultdict(lambda: collections.defaultdict(dict))
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "qg::" not in name or "pack_" in name:   # the offline weight packing is setup
+            continue
+        d = per[name.split("(")[0].replace("void ", "")][r["Dispatch_Id"]]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    simds, xcds = 256 * 4, 8
+    print("# MFMA busy share per kernel, rocprofv3 counters")
+    print(f"# command: {command}")
+    print("# busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8); clock = GRBM_GUI_ACTIVE / 8 / duration")
+    print("# (the counter window is longer than a dispatch's timestamps: short dispatches read a high clock")
+    print("# and a low busy share; the long GEMM dispatches give the step's figures)")
+    print(f"{'kernel':60s} {'disp':>5s} {'avg_us':>8s} {'busy':>6s} {'GHz':>5s} {'share_of_time':>13s}")
+    tot_busy = tot_cyc = tot_ns = 0.0
+    summary = []
+    for k, ds in per.items():
+        ds = [d for d in ds.values() if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d]
+        if not ds:
+            continue
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds)
+        cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / xcds * simds
+        ns = sum(d["ns"] for d in ds)
+        tot_busy += busy
+        tot_cyc += cyc
+        tot_ns += ns
+        summary.append((ns, k, len(ds), ns / len(ds) / 1e3, busy / cyc,
+                        sum(d["GRBM_GUI_ACTIVE"] for d in ds) / xcds / ns))
+    if not summary:
+        print("no dispatch carries all three counters")
+        return
+    for ns, k, n, us, b, ghz in sorted(summary, reverse=True):
+        print(f"{k[:60]:60s} {n:5d} {us:8.2f} {b:6.3f} {ghz:5.2f} {ns / tot_ns:13.3f}")
+    print(f"{'all library kernels':60s} {'':5s} {'':8s} {tot_busy / tot_cyc:6.3f}")
+
+
 def summarize_stats(csv_path, command):
     import csv
     rows = list(csv.DictReader(open(csv_path)))
@@ -374,6 +422,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic, args.command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -515,8 +566,10 @@ def run_decode(args, torch, ops, synth):
 def run_large_batch(args, torch, ops, synth):
     batches = [32, 64, 128, 256, 384, 512, 1024]
     if args.batches:
-        # extra batches (e.g. a finer sweep around the crossover), timed alongside
-        batches = sorted(set(batches) | {int(x) for x in args.batches.split(",")})
+        # extra batches (e.g. a finer sweep around the crossover), timed alongside;
+        # with --only-batch only these (short profiled runs)
+        extra = {int(x) for x in args.batches.split(",")}
+        batches = sorted(extra if args.only_batch else set(batches) | extra)
     stack = Stack(ops, synth, torch, "8b", batches)
     dev = torch.device("cuda:0")
     # the dense bf16 baseline: the same shapes, fresh bf16 weights (15.0 GB)
@@ -548,11 +601,11 @@ def run_large_batch(args, torch, ops, synth):
         if res[b]["w4a16_ms"] < res[b]["bf16_ms"]:
             break
         cross = int(b)
-    B = 512
+    B = 512 if "512" in res else batches[-1]
     out = {"metric": "Llama-3-8B W4A16 decode-step ms & HBM TB/s vs batch; MFMA util at B>=512",
-           "value": res["512"]["w4a16_mfma_frac"], "unit": "fraction of bf16 MFMA peak at B=512",
+           "value": res[str(B)]["w4a16_mfma_frac"], "unit": f"fraction of bf16 MFMA peak at B={B}",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": res["512"]["w4a16_ms"], "higher_is_better": True, "scaling": "weak",
+           "ms_per_step": res[str(B)]["w4a16_ms"], "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)",
            "data": "synthetic", "config": {"workload": "Llama-3-8B W4A16 stack vs dense bf16 stack (torch.matmul)",
                                            "batch": B},

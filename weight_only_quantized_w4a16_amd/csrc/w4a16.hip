@@ -697,29 +697,32 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
 // Large M: -136 * (row sum over each group) for every row, once per call, into
 // the workspace as corr[g][m] (rows padded to a multiple of 128 with zeros).
 // ---------------------------------------------------------------------------
+// Sixteen lanes per (group, row): each loads 16 bytes (8 activations) and adds
+// them in order, then the lanes' sums are added pairwise (xor 8, 4, 2, 1), so
+// the launch fills the GPU and pays one memory round trip.
 __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t* __restrict__ a,
                                                                  int M, int Mp, int K,
                                                                  float* __restrict__ corr) {
     const int G = K >> 7;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (size_t)G * Mp) return;
-    const int m = (int)(idx % Mp);
-    const int g = (int)(idx / Mp);
+    const size_t team = idx >> 4;                // (group, row) = (team / Mp, team % Mp)
+    const int sub = (int)(idx & 15);
+    const bool valid = team < (size_t)G * Mp;   // whole 16-lane teams share this
+    const int m = valid ? (int)(team % Mp) : 0;
+    const int g = valid ? (int)(team / Mp) : 0;
     float s = 0.0f;
-    if (m < M) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(a + (size_t)m * K + (size_t)g * 128);
-#pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-            const u32x4 v = p[i];
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    if (valid && m < M) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(a + (size_t)m * K + (size_t)g * 128)[sub];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s += bf16_to_f32(w4[j] & 0xffffu);
-                s += bf16_to_f32(w4[j] >> 16);
-            }
+        for (int j = 0; j < 4; ++j) {
+            s += bf16_to_f32(w4[j] & 0xffffu);
+            s += bf16_to_f32(w4[j] >> 16);
         }
     }
-    corr[idx] = -136.0f * s;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (valid && sub == 0) corr[team] = -136.0f * s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1229,7 +1232,7 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
         int* items = reinterpret_cast<int*>(static_cast<char*>(ws) + grouped_corr_bytes(E, T, K));
         constexpr int R = QG_GR_BM;              // rows per item = tile rows
         const int max_items = (T < E ? T : E) + (T + R - 1) / R;
-        const size_t n = (size_t)G * Tp;
+        const size_t n = (size_t)G * Tp * 16;      // 16 lanes per (group, row)
         hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            a, T, Tp, K, corr);
         launch_grouped_items(offsets, E, T, R, max_items, items, s);
@@ -1627,7 +1630,7 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
         const int Mp = round_up(M, LM_MAX_BM);
         const int G = K / 128;
         float* corr = static_cast<float*>(ws);
-        const size_t n = (size_t)G * Mp;
+        const size_t n = (size_t)G * Mp * 16;      // 16 lanes per (group, row)
         hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
                            0, s, a, M, Mp, K, corr);
         launch_large(a, packed, scales, ws, y, M, N, K, s);

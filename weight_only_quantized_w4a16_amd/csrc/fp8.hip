@@ -364,16 +364,17 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large M (M > 64): 128 x 128·NB output tile per workgroup (NB = 2, or 1 when
-// 256-column tiles would leave CUs idle), eight waves in a 2 x 4 grid of
-// 64 x 32·NB (4 x 2NB MFMA tiles of 16x16x128 e4m3), K walked one
-// 128-row k-tile at a time through an NS-stage pipeline in LDS (three stages
-// of 48 KiB with 256-column tiles, four of 32 KiB with 128-column tiles).  Stage
-// kt % NS holds, for k-tile kt, the activation tile (128 rows x 128 bytes,
+// Large M (M > 64): BM x 128·NB output tile per workgroup (BM = 128, or 64 where
+// 128-row tiles would leave the CUs under-filled; NB = 2, or 1 when 256-column
+// tiles would leave CUs idle), eight waves in a 2 x 4 grid of BM/2 x 32·NB
+// (BM/32 x 2NB MFMA tiles of 16x16x128 e4m3), K walked one 128-row k-tile at
+// a time through an NS-stage pipeline in LDS (three stages with 256-column
+// tiles, four with 128-column tiles).  Stage kt % NS holds, for k-tile kt, the
+// activation tile (BM rows x 128 bytes,
 // 16-byte chunk c of row r at c ^ ((r / 2) % 8): two 128-byte rows share one
 // pass over the 64 banks) and the 8·NB weight tiles of the columns in their
 // native fragment order (2 KiB each).  Everything is copied with 128-bit
-// direct-to-LDS loads, 2 + 2·NB per thread per stage, issued NS - 1 k-tiles ahead
+// direct-to-LDS loads, BM/64 + 2·NB per thread per stage, issued NS - 1 k-tiles ahead
 // and spread over the previous k-tile's MFMAs; a k-tile step waits until at
 // most (NS - 2) steps of copies are outstanding (so its stage has landed),
 // then a barrier publishes the stage and frees the one read a step earlier.

@@ -726,24 +726,26 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
-// Large M (M > 64): 128 x 128·NB output tile per workgroup (NB = 2, or 1 when
-// 256-column tiles would leave CUs idle), eight waves in a 2 x 4 grid of
-// 64 x 32·NB, K walked one group (128 rows) at a time through an NS-stage
-// pipeline in LDS.  Stage g % NS holds, for group g:
-//   * the activation tile a[m0 : m0+128, 128g : 128g+128] (32 KiB), stored with
-//     a 16-byte XOR swizzle (chunk c of row r at c ^ (r % 16)) so fragment
-//     reads are conflict free;
+// Large M (M > 64, and 17..64 rows when the grid covers the CUs): BM x 128·NB
+// output tile per workgroup (BM = 128, or 64 for few rows and for grids that
+// 128-row tiles would leave idle; NB = 2, or 1 when 256-column tiles would
+// leave CUs idle), eight waves in a 2 x 4 grid of BM/2 x 32·NB, K walked one
+// group (128 rows) at a time through an NS-stage pipeline in LDS.  Stage g % NS
+// holds, for group g:
+//   * the activation tile a[m0 : m0+BM, 128g : 128g+128] (BM/4 KiB), stored
+//     with a 16-byte XOR swizzle (chunk c of row r at c ^ (r % 16)) so
+//     fragment reads are conflict free;
 //   * the 8·NB weight tiles of the columns in their native fragment order (a
 //     wave reads its fragment of a tile with one 128-bit LDS read);
-//   * their bf16 scales and the offset terms corr[g][m0 : m0+128].
-// Everything is copied with 128-bit direct-to-LDS loads, six per thread per
+//   * their bf16 scales and the offset terms corr[g][m0 : m0+BM].
+// Everything is copied with 128-bit direct-to-LDS loads, BM/32 + NB per thread per
 // stage (scales and offset terms share one more copy by wave 0), issued NS - 1
 // groups ahead and spread over the previous group's math: a direct-to-LDS copy
 // occupies the CU's address unit for about 40 cycles whatever its size, so the
 // copies pace the loop unless they overlap the MFMAs.  A group step waits until at most
 // (NS - 2) stages of copies are outstanding, so this stage has landed, then a
 // barrier publishes it (and frees the stage read one step earlier, which the
-// next copies refill).  A wave's tile is 2 x NB blocks of 32 x 32 on
+// next copies refill).  A wave's tile is BM/64 x NB blocks of 32 x 32 on
 // v_mfma_f32_32x32x16_bf16 (on gfx950 the 16x16x32 form sustains only about
 // half the bf16 rate); per group and 16-k step it unpacks one weight word per
 // 32-column block and reads one A fragment per 32-row block.  Every block's
@@ -1054,8 +1056,8 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     large_m_tile<NS, NB, BM>(a, wq, sc, corr, y, M, Mp, N, K, S, part, cnt, tiles, split, tile);
 }
 
-// Expert-grouped, many rows per expert: one work item (expert, up to 128 rows)
-// per blockIdx.y, the expert's 128 x 128·NB column tiles along blockIdx.x; the
+// Expert-grouped, many rows per expert: one work item (expert, up to BM rows)
+// per blockIdx.y, the expert's BM x 128·NB column tiles along blockIdx.x; the
 // offset terms of all routed rows come from one pre-pass (corr[g][row], rows
 // padded so that a 128-row read from any item start stays inside).
 template <int NS, int NB, int BM>

@@ -39,8 +39,14 @@
  * M == 0 is valid and launches nothing.  On success the work is enqueued on
  * `stream` (a hipStream_t; NULL = the default stream) and the call returns
  * QG_OK without waiting for it.  Device-side data conditions are not checked:
- * non-finite inputs are outside the contract.  Calls are thread-safe; the
- * library holds no state.
+ * non-finite inputs are outside the contract.
+ *
+ * Host state: the library keeps per-device caches only (each device's compute
+ * unit count and which kernels have their LDS limit raised on it), set
+ * idempotently without locks, so calls from several threads and for several
+ * devices are safe.  Kernel plans, and with them the workspace sizes, depend
+ * on the current device's compute unit count: make a workspace size query
+ * with the device current that the call will run on.
  */
 #ifndef QGEMM_H
 #define QGEMM_H
@@ -80,8 +86,12 @@ size_t qg_int4_g128_packed_bytes(int64_t K, int64_t N);
 size_t qg_int4_g128_scale_bytes(int64_t K, int64_t N);
 
 /*
- * Name of the kernel qgemm_w4a16 / qgemm_w8a8_fp8 launches for this shape on
- * the current device (host only; static string; "" for an invalid shape).
+ * Name and configuration of the kernel qgemm_w4a16 / qgemm_w8a8_fp8 launches
+ * for this shape on the current device (host only; the text lives in a
+ * per-thread buffer valid until the thread's next call; "" for an invalid
+ * shape), e.g. "w4a16_decode_kernel<KW, U, D> S=s", "w4a16_small_m_kernel<MT,
+ * CT>", "w4a16_large_m_kernel<NS, NB, BM> S=s", "w8a8_small_m_kernel<MT, CT>",
+ * "w8a8_large_m_kernel<NS, NB, BM> S=s" (S: K slices across workgroups).
  * Useful to match profiler records to calls.
  */
 const char *qg_w4a16_kernel_for(int64_t M, int64_t N, int64_t K);
@@ -164,11 +174,15 @@ qg_status dequant_int4_g128(const uint32_t *packed, const uint16_t *scales,
  *   scales     in   native bf16 scales from pack_int4_g128.
  *   y_bf16     out  [M, N].
  *   workspace  scratch of qg_w4a16_workspace_bytes(M, N, K) bytes (may be
- *              NULL when that is 0).  It must be zero-filled before its
- *              first use.  It holds fp32 partial sums (scratch) followed by
- *              completion counters that every call resets to zero, so one
- *              workspace stays valid for later calls of any shape.  Calls
- *              that share a workspace must not overlap in time.
+ *              NULL when that is 0), 16-byte aligned.  It must be zero-filled
+ *              before its first use.  Its first 64 KiB hold completion
+ *              counters (one per output tile or column strip that is split
+ *              across workgroups), which every call leaves at zero; the
+ *              per-call offset terms and fp32 partial sums follow.  The
+ *              counters sit at the same offset for every shape, so one
+ *              workspace, sized for the largest call, stays valid for later
+ *              calls of any shape.  Calls that share a workspace must not
+ *              overlap in time.
  *
  * Numerics (folded offset): the MFMA multiplies the bf16 activations with the
  * exact bf16 values 128 + code; per group and row the kernel adds
@@ -181,52 +195,6 @@ qg_status qgemm_w4a16(const uint16_t *a_bf16, const uint32_t *packed,
                       int M, int N, int K,
                       void *workspace, size_t workspace_bytes,
                       qg_stream stream);
-
-/*
- * Chained decode -- the W4A16 GEMMs of one decode step (M <= 16) in a single
- * persistent, cooperative launch: one workgroup per compute unit, all GEMMs in
- * order, each GEMM's weight stream starting while the previous GEMM finishes.
- * Same arithmetic as qgemm_w4a16 (decode path) for every GEMM.
- * [P1 "The three regimes": at small B the step is the weight stream; P2 3.4
- *  "Inference with W4A16".]
- *
- * Usage: describe the chain (qg_w4a16_chain_gemm, host memory), build a plan
- * with qg_w4a16_chain_plan (host memory, qg_w4a16_chain_plan_bytes bytes),
- * copy the plan byte for byte to device memory, then call qgemm_w4a16_chain
- * with both copies as often as needed.  A plan is valid for the device that is
- * current when it is made.
- *
- * after_previous != 0 declares that the GEMM reads memory the previous GEMM
- * of the chain writes (e.g. its activations are the previous outputs): it then
- * starts reading activations only after every workgroup has finished the
- * previous GEMM.  Outputs are written and activations read with accesses that
- * are coherent across the GPU, so such chains are exact.
- *
- * Plan errors: QG_ERR_SHAPE also when M > 16, count < 1, or a GEMM does not
- * fit the chained kernel (run it with qgemm_w4a16 instead).
- * Workspace: qg_w4a16_chain_workspace_bytes(count) bytes, zero-filled before
- * first use; each call leaves it zero-filled except the error word (32-bit
- * word 1), which becomes nonzero if a dependency wait exceeded its bound (the
- * results of that call are then invalid; every wave still exits).  Calls that
- * share a workspace must not overlap.  A launch that cannot keep every
- * workgroup resident fails with QG_ERR_HIP instead of running.
- */
-typedef struct {
-    const uint16_t *a_bf16;     /* [M, K] activations */
-    const uint32_t *packed;     /* native INT4 words (pack_int4_g128) */
-    const uint16_t *scales;     /* native bf16 scales */
-    uint16_t *y_bf16;           /* [M, N] outputs */
-    int32_t N, K;
-    int32_t after_previous;
-    int32_t reserved;           /* must be 0 */
-} qg_w4a16_chain_gemm;
-
-size_t qg_w4a16_chain_plan_bytes(int count);
-size_t qg_w4a16_chain_workspace_bytes(int count);
-qg_status qg_w4a16_chain_plan(const qg_w4a16_chain_gemm *gemms, int count, int M,
-                              void *plan, size_t plan_bytes);
-qg_status qgemm_w4a16_chain(const void *plan_host, const void *plan_device,
-                            void *workspace, size_t workspace_bytes, qg_stream stream);
 
 /*
  * qgemm_w4a16_grouped -- the W4A16 product of a mixture-of-experts layer: each
@@ -305,7 +273,10 @@ qg_status quant_weight_fp8_per_channel(const uint16_t *w_bf16, int K, int N,
  *   a_e4m3, a_scale   in  from quant_act_per_token ([M, K], [M]).
  *   w_e4m3, w_scale   in  from quant_weight_fp8_per_channel.
  *   y_bf16            out [M, N].
- *   workspace         scratch of qg_w8a8_workspace_bytes(M, N, K) bytes.
+ *   workspace         scratch of qg_w8a8_workspace_bytes(M, N, K) bytes (NULL
+ *                     when that is 0), zero-filled before its first use, with
+ *                     the layout and rules of qgemm_w4a16's workspace (64 KiB
+ *                     of counters, then fp32 partial sums).
  */
 qg_status qgemm_w8a8_fp8(const uint8_t *a_e4m3, const float *a_scale,
                          const uint8_t *w_e4m3, const float *w_scale,

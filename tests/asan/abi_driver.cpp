@@ -101,19 +101,6 @@ int main() {
     EXPECT_STATUS(qgemm_w8a8_int8(i8, f32, i8, f32, y16, 4, 32, 131072 + 128, nullptr, 0, nullptr),
                   QG_ERR_SHAPE);
 
-    // chained decode: plan on the host, then a launch
-    qg_w4a16_chain_gemm g[2] = {{a16, w32, s16, y16, 32, 256, 0, 0}, {y16, w32, s16, a16, 32, 256, 1, 0}};
-    std::vector<unsigned char> plan(qg_w4a16_chain_plan_bytes(2));
-    EXPECT(qg_w4a16_chain_plan(g, 2, 4, plan.data(), plan.size()) == QG_OK);
-    EXPECT(qg_w4a16_chain_plan(g, 2, 17, plan.data(), plan.size()) == QG_ERR_SHAPE);
-    EXPECT(qg_w4a16_chain_plan(g, 2, 4, plan.data(), plan.size() - 1) == QG_ERR_WORKSPACE);
-    g[1].reserved = 1;
-    EXPECT(qg_w4a16_chain_plan(g, 2, 4, plan.data(), plan.size()) == QG_ERR_SHAPE);
-    g[1].reserved = 0;
-    EXPECT(qg_w4a16_chain_plan(g, 2, 4, plan.data(), plan.size()) == QG_OK);
-    EXPECT_LAUNCH(qgemm_w4a16_chain(plan.data(), base, ws, qg_w4a16_chain_workspace_bytes(2), nullptr));
-    EXPECT_STATUS(qgemm_w4a16_chain(plan.data(), base, ws, 4, nullptr), QG_ERR_WORKSPACE);
-
     // strings
     EXPECT(qg_status_string(QG_OK) != nullptr && qg_status_string(1234) != nullptr);
     EXPECT(qg_version() != nullptr);

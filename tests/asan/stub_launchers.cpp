@@ -31,21 +31,6 @@ void launch_qgemm_w4a8_fp8(const uint8_t*, const float*, const uint32_t*, const 
                            int, hipStream_t) { ++g_launches; }
 void launch_qgemm_w4a8_fp8_grouped(const uint8_t*, const float*, const int*, const uint32_t*, const uint16_t*,
                                    uint16_t*, int, int, int, int, void*, hipStream_t) { ++g_launches; }
-int chain_grid() { return 256; }
-bool chain_plan_one(int, int N, int K, int, ChainDesc* d, size_t* lds) {
-    d->N = N;
-    d->K = K;
-    d->units = 1;
-    d->kw = 1;
-    d->u = 1;
-    d->nchunks = 1;
-    *lds = 1024;
-    return true;
-}
-hipError_t launch_chain(const ChainDesc*, int, int, size_t, unsigned*, hipStream_t) {
-    ++g_launches;
-    return hipSuccess;
-}
 void launch_quant_act_per_token(const uint16_t*, int, int, uint8_t*, float*, hipStream_t) { ++g_launches; }
 void launch_quant_weight_fp8(const uint16_t*, int, int, uint8_t*, float*, hipStream_t) { ++g_launches; }
 void launch_quant_act_per_token_i8(const uint16_t*, int, int, int8_t*, float*, hipStream_t) { ++g_launches; }

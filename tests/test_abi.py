@@ -56,16 +56,21 @@ def test_status_strings_and_version(lib):
 
 
 def test_kernel_selection_query(lib):
-    assert lib.w4a16_kernel_for(1, 28672, 4096) == "w4a16_decode_kernel"
-    assert lib.w4a16_kernel_for(16, 4096, 14336) == "w4a16_decode_kernel"
+    # names carry the template configuration and the K split
+    assert lib.w4a16_kernel_for(1, 28672, 4096).startswith("w4a16_decode_kernel<")
+    assert lib.w4a16_kernel_for(1, 28672, 4096).endswith(" S=1")
+    assert lib.w4a16_kernel_for(16, 4096, 14336).startswith("w4a16_decode_kernel<")
+    assert not lib.w4a16_kernel_for(16, 4096, 14336).endswith(" S=1")
     # narrow outputs whose activation slice fits in LDS: in-workgroup split-K
     assert lib.w4a16_kernel_for(4, 4096, 14336).startswith("w4a16_small_m_kernel<1")
     assert lib.w4a16_kernel_for(1, 16, 128).startswith("w4a16_small_m_kernel<1")
     assert lib.w4a16_kernel_for(17, 4096, 4096).startswith("w4a16_small_m_kernel<2")
     assert lib.w4a16_kernel_for(32, 4096, 4096).startswith("w4a16_small_m_kernel<2")
-    assert lib.w4a16_kernel_for(512, 4096, 4096) == "w4a16_large_m_kernel"
+    assert lib.w4a16_kernel_for(512, 4096, 4096).startswith("w4a16_large_m_kernel<")
     assert lib.w4a16_kernel_for(4, 4096, 4000) == ""                 # invalid shape
-    assert lib.w8a8_kernel_for(512, 4096, 4096) == "w8a8_large_m_kernel"
+    assert lib.w8a8_kernel_for(512, 4096, 4096).startswith("w8a8_large_m_kernel<")
+    assert lib.w8a8_kernel_for(1, 28672, 4096) == "w8a8_small_m_kernel<1, 2>"
+    assert lib.w8a8_kernel_for(1, 4096, 4096) == "w8a8_small_m_kernel<1, 1>"
 
 
 def test_size_queries(lib):
@@ -74,39 +79,38 @@ def test_size_queries(lib):
         assert lib.scale_bytes(K, N) == K // 128 * N * 2
         assert (lib.packed_bytes(K, N) + lib.scale_bytes(K, N)) * 8 == 4.125 * K * N
     assert lib.packed_bytes(100, 16) == 0 and lib.packed_bytes(128, 17) == 0
-    # decode (M <= 16): wide outputs need none, narrow ones fp32 slots + counters
+    # Workspaces: the 64 KiB counter region first (same place for every shape),
+    # then the offset terms (large M, rows padded to 256) and the fp32 slots.
+    CNT = 64 * 1024
+    al = lambda x: (x + 255) // 256 * 256
+    # decode (M <= 16): wide outputs need none, narrow long-K ones counters + slots
+    assert lib.w4a16_workspace_bytes(0, 4096, 14336) == 0
     assert lib.w4a16_workspace_bytes(4, 28672, 4096) == 0
     assert lib.w4a16_workspace_bytes(16, 128256, 4096) == 0
-    assert lib.w4a16_workspace_bytes(16, 4096, 14336) > 0           # long K split across workgroups
+    ws = lib.w4a16_workspace_bytes(16, 4096, 14336)                 # long K split across workgroups
+    assert ws > CNT and (ws - CNT) % (256 * 1024) == 0              # S slots of 256 tiles x 1 KiB
     assert lib.w4a16_workspace_bytes(4, 4096, 4096) == 0
     assert lib.w4a16_workspace_bytes(32, 4096, 4096) == 0          # M <= 64: in-workgroup split-K
-    assert lib.w4a16_workspace_bytes(1024, 4096, 4096) == 32 * 1024 * 4
+    assert lib.w4a16_workspace_bytes(1024, 4096, 4096) == CNT + 32 * 1024 * 4
     # short K, M = 100: 128-row tiles would fill under half of the 256 CUs, so
     # the tiles are 64 rows (2 x 32 tiles of 64 x 128); they fill at most a
-    # quarter, so K (32 groups) splits 4 ways, at least 8 groups per slice:
-    # offset terms (rows padded to 256), 4 fp32 slots of [M, N], one counter per tile
-    corr = 32 * 256 * 4
-    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == (corr + 4 * 100 * 4096 * 4 + 255) // 256 * 256 + 64 * 4
+    # quarter, so K (32 groups) splits 4 ways, at least 8 groups per slice
+    assert lib.w4a16_workspace_bytes(100, 4096, 4096) == al(CNT + 32 * 256 * 4) + 4 * 100 * 4096 * 4
     # short K with more tiles (M = 300: 5 x 32 tiles of 64 rows) does not split
-    assert lib.w4a16_workspace_bytes(300, 4096, 4096) == 32 * 512 * 4
-    assert lib.w8a8_workspace_bytes(100, 4096, 4096) == (4 * 100 * 4096 * 4 + 255) // 256 * 256 + 64 * 4
+    assert lib.w4a16_workspace_bytes(300, 4096, 4096) == CNT + 32 * 512 * 4
+    assert lib.w8a8_workspace_bytes(100, 4096, 4096) == CNT + 4 * 100 * 4096 * 4
     assert lib.w8a8_workspace_bytes(300, 4096, 4096) == 0
-    # long K: offset terms, then K split 4 ways (2 x 32 tiles of 64 x 128 on
-    # 256 CUs): 4 fp32 slots of [M, N], then one counter per tile
-    corr = 112 * 256 * 4
-    slots = 4 * 100 * 4096 * 4
-    assert lib.w4a16_workspace_bytes(100, 4096, 14336) == (corr + slots + 255) // 256 * 256 + 64 * 4
+    # long K: K split 4 ways (2 x 32 tiles of 64 x 128 on 256 CUs)
+    assert lib.w4a16_workspace_bytes(100, 4096, 14336) == al(CNT + 112 * 256 * 4) + 4 * 100 * 4096 * 4
     # 128-row tiles where they fill more than half of the CUs (M = 384, N = 8192:
     # 3 x 64 tiles), K split 2 ways
-    corr = 224 * 512 * 4
-    slots = 2 * 384 * 8192 * 4
-    assert lib.w4a16_workspace_bytes(384, 8192, 28672) == (corr + slots + 255) // 256 * 256 + 192 * 4
+    assert lib.w4a16_workspace_bytes(384, 8192, 28672) == al(CNT + 224 * 512 * 4) + 2 * 384 * 8192 * 4
     assert lib.w8a8_workspace_bytes(1024, 4096, 4096) == 0
     assert lib.w8a8_workspace_bytes(64, 4096, 14336) == 0             # small M: no split
     assert lib.w8a8_workspace_bytes(1024, 4096, 14336) == 0           # 256 tiles fill the CUs
     # 128-row tiles would fill a quarter of the CUs: 128 tiles of 64 x 128, 112
-    # k-tiles split 2 ways: 2 fp32 slots of [M, N], then one counter per tile
-    assert lib.w8a8_workspace_bytes(200, 4096, 14336) == (2 * 200 * 4096 * 4 + 255) // 256 * 256 + 128 * 4
+    # k-tiles split 2 ways
+    assert lib.w8a8_workspace_bytes(200, 4096, 14336) == CNT + 2 * 200 * 4096 * 4
 
 
 FAKE = 0x100000          # 16-byte aligned, never dereferenced (validation fails first)
@@ -232,10 +236,3 @@ def test_binding_refuses_host_tensors(lib):
     a = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         lib.quantize_activations(a)
-
-
-def test_chain_queries(lib):
-    assert lib._lib.qg_w4a16_chain_plan_bytes(129) == 64 + 129 * 64
-    assert lib._lib.qg_w4a16_chain_workspace_bytes(129) == (129 + 2) * 4
-    assert lib._lib.qg_w4a16_chain_plan_bytes(0) == 0
-    assert ctypes.sizeof(lib.ChainGemm) == 48

@@ -119,7 +119,7 @@ def test_int8_exact_integer_sums(ops):
 def test_int8_large_m_split_counters_reset(ops, M, K, N, tiles, S):
     announce(f"qgemm_w8a8_int8 large-M split M={M} K={K} N={N}")
     nbytes = ops.w8a8_int8_workspace_bytes(M, N, K)
-    assert nbytes == (S * M * N * 4 + 255) // 256 * 256 + 4 * tiles
+    assert nbytes == 65536 + S * M * N * 4          # counter region, then S slots
     w = synth.weights(K, N, seed=97)
     a = synth.activations(M, K, seed=101)
     qa, sa = i8.quant_act_per_token(a)
@@ -131,8 +131,55 @@ def test_int8_large_m_split_counters_reset(ops, M, K, N, tiles, S):
     for _ in range(3):
         y = host_bits16(lin(ad))
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(lin._ws[nbytes - 4 * tiles:nbytes])) == 0
+        assert int(torch.count_nonzero(lin._ws[:65536])) == 0      # counters (first 4 * tiles bytes)
         assert_close_rms(y, ref, what=f"int8 split M={M} K={K} N={N}")
         if first is None:
             first = y
         assert np.array_equal(y, first)
+
+
+# ---------------------------------------------------------------- wide shapes
+
+# Weights of the wide Llama-3-8B shapes, drawn on the device (torch's
+# generator; both sides receive the same bits) and quantized once per shape;
+# the oracle gets the bits of 256 sampled columns (per-channel quantization is
+# exact on a column subset) and of up to 32 sampled rows.
+_WIDE = {}
+WIDE_SHAPES = [("qkv", 4096, 6144, 1000), ("gate_up", 4096, 28672, 1002), ("lm_head", 4096, 128256, 1128)]
+
+
+def _wide(ops, name, K, N, seed):
+    if name not in _WIDE:
+        _WIDE.clear()                                   # one shape resident at a time
+        w_dev = synth.normal_bf16_device((K, N), seed, synth.WEIGHT_STD, "cuda")
+        cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(seed).integers(0, N, 254)]))
+        w_cols = host_bits16(w_dev[:, torch.from_numpy(cols).cuda()])
+        wt = ops.Int8Weight.from_bf16(w_dev)
+        del w_dev
+        torch.cuda.synchronize()
+        _WIDE[name] = (wt, cols, i8.quant_weight_per_channel(w_cols))
+    return _WIDE[name]
+
+
+@pytest.mark.parametrize("name,K,N,seed", WIDE_SHAPES)
+@pytest.mark.parametrize("B", [1, 16, 128, 512, 1024])
+def test_int8_gemm_wide_shapes_sampled(ops, name, K, N, seed, B):
+    kern = ops.w8a8_kernel_for(B, N, K)
+    announce(f"qgemm_w8a8_int8 8B {name} B={B} ({kern})")
+    wt, cols, (qw, sw) = _wide(ops, name, K, N, seed)
+    a = synth.activations(B, K, seed=seed + B)
+    y = host_bits16(ops.W8A8Int8Linear(wt)(dev_bf16(a)))
+    torch.cuda.synchronize()
+    rows = np.unique(np.random.default_rng(B).integers(0, B, 32))
+    qa, sa = i8.quant_act_per_token(a[rows])
+    assert_close_rms(y[rows][:, cols], i8.gemm_ref(qa, sa, qw, sw), what=f"int8 {name} B={B} {kern}")
+
+
+def test_int8_wide_shapes_cover_every_instantiation(ops):
+    """The wide-shape cases above run the two-column-tile small-M kernel (CT = 2)
+    and the 256-column large-M tiles (NB = 2) besides the narrow forms."""
+    names = {ops.w8a8_kernel_for(B, N, K) for (_, K, N, _) in WIDE_SHAPES for B in (1, 16, 128, 512, 1024)}
+    assert "w8a8_small_m_kernel<1, 2>" in names and "w8a8_small_m_kernel<1, 1>" in names, names
+    large = [n for n in names if n.startswith("w8a8_large_m_kernel<")]
+    assert any(n.split("<")[1].split(",")[1].strip() == "2" for n in large), names
+    assert any(n.split("<")[1].split(",")[1].strip() == "1" for n in large), names

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libqgemm.so")
-SOURCES = ["abi.cpp", "w4a16.hip", "fp8.hip", "w4a8.hip", "chain.hip"]
+SOURCES = ["abi.cpp", "w4a16.hip", "fp8.hip", "w4a8.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,6 +23,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Wall", "-Wno-unused-command-line-argument",
+    # an inline-asm warning (e.g. a clobbered reserved register) fails the build
+    "-Werror=inline-asm",
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

@@ -139,71 +139,6 @@ qg_status qgemm_w4a16(const uint16_t* a_bf16, const uint32_t* packed, const uint
     return launched();
 }
 
-size_t qg_w4a16_chain_plan_bytes(int count) {
-    if (count < 1 || count > (1 << 20)) return 0;
-    return sizeof(qg::ChainHeader) + (size_t)count * sizeof(qg::ChainDesc);
-}
-
-size_t qg_w4a16_chain_workspace_bytes(int count) {
-    if (count < 1 || count > (1 << 20)) return 0;
-    return (size_t)(count + 2) * sizeof(unsigned);
-}
-
-qg_status qg_w4a16_chain_plan(const qg_w4a16_chain_gemm* gemms, int count, int M, void* plan,
-                              size_t plan_bytes) {
-    if (!gemms || !plan) return QG_ERR_NULL;
-    if (count < 1 || count > (1 << 20) || M < 1 || M > 16) return QG_ERR_SHAPE;
-    if (plan_bytes < qg_w4a16_chain_plan_bytes(count)) return QG_ERR_WORKSPACE;
-    auto* hdr = static_cast<qg::ChainHeader*>(plan);
-    auto* desc = reinterpret_cast<qg::ChainDesc*>(hdr + 1);
-    const int P = qg::chain_grid();
-    size_t lds_max = 0;
-    for (int i = 0; i < count; ++i) {
-        const qg_w4a16_chain_gemm& g = gemms[i];
-        if (!g.a_bf16 || !g.packed || !g.scales || !g.y_bf16) return QG_ERR_NULL;
-        if (!shape_ok(M, g.N, g.K) || g.reserved != 0) return QG_ERR_SHAPE;
-        if (!aligned(g.a_bf16, 16) || !aligned(g.packed, 16) || !aligned(g.scales, 4) ||
-            !aligned(g.y_bf16, 16))
-            return QG_ERR_ALIGN;
-        qg::ChainDesc d{};
-        size_t lds = 0;
-        if (!qg::chain_plan_one(M, g.N, g.K, P, &d, &lds)) return QG_ERR_SHAPE;
-        d.a = g.a_bf16;
-        d.wq = g.packed;
-        d.sc = g.scales;
-        d.y = g.y_bf16;
-        d.after_prev = (i > 0 && g.after_previous) ? 1 : 0;
-        desc[i] = d;
-        lds_max = lds > lds_max ? lds : lds_max;
-    }
-    *hdr = qg::ChainHeader{};
-    hdr->magic = qg::kChainMagic;
-    hdr->count = count;
-    hdr->M = M;
-    hdr->grid = P;
-    hdr->lds = lds_max;
-    return QG_OK;
-}
-
-qg_status qgemm_w4a16_chain(const void* plan_host, const void* plan_device, void* workspace,
-                            size_t workspace_bytes, qg_stream stream) {
-    if (!plan_host || !plan_device || !workspace) return QG_ERR_NULL;
-    const auto* hdr = static_cast<const qg::ChainHeader*>(plan_host);
-    if (hdr->magic != qg::kChainMagic || hdr->count < 1 || hdr->grid != qg::chain_grid())
-        return QG_ERR_SHAPE;
-    if (!aligned(plan_device, 16) || !aligned(workspace, 16)) return QG_ERR_ALIGN;
-    if (workspace_bytes < qg_w4a16_chain_workspace_bytes(hdr->count)) return QG_ERR_WORKSPACE;
-    const auto* dev_desc =
-        reinterpret_cast<const qg::ChainDesc*>(static_cast<const qg::ChainHeader*>(plan_device) + 1);
-    const hipError_t e = qg::launch_chain(dev_desc, hdr->count, hdr->M, (size_t)hdr->lds,
-                                          static_cast<unsigned*>(workspace), as_stream(stream));
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return QG_ERR_HIP;
-    }
-    return launched();
-}
-
 qg_status qgemm_w4a16_grouped(const uint16_t* a_bf16, const int32_t* offsets,
                               const uint32_t* packed, const uint16_t* scales, uint16_t* y_bf16,
                               int E, int T, int N, int K, void* workspace, size_t workspace_bytes,

@@ -160,13 +160,35 @@ __device__ __forceinline__ void ring_prologue(Load&& load) {
 // The same copy issued as inline assembly: the compiler does not track it, so
 // it adds no waits of its own between copies and later LDS accesses (it cannot
 // tell LDS stages apart and would wait for every copy).  The caller waits for
-// the copy with s_waitcnt vmcnt and publishes it with a barrier.
+// the copy with s_waitcnt vmcnt and publishes it with a barrier.  The LDS
+// address goes in through M0 as an input operand, so the compiler itself sets
+// the register and knows its value afterwards.
 __device__ __forceinline__ void lds_copy_b128(const void* src, const void* lds_dst) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(m0)
-                 : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// ---- cross-workgroup handoff ----------------------------------------------------
+// A workgroup has written its partial results with agent-scope atomic stores
+// (written through to the memory side, where every XCD reads them) and now
+// counts its arrival; the workgroup whose increment completes the count reads
+// every slot.  Ordering: each wave first waits until all of its own stores have
+// completed (a workgroup barrier alone orders LDS traffic only, not the other
+// waves' outstanding global stores), the barrier then ensures every wave got
+// there, and only then does one thread increment the counter.  So every slot
+// store of this workgroup is complete before its increment is visible, and the
+// last arriver, which issues its agent-scope slot loads only after its own
+// increment has returned, reads each slot after it was written.  Returns true
+// in every thread of the last-arriving workgroup.
+__device__ __forceinline__ bool arrive_and_check_last(unsigned* counter, unsigned arrivals,
+                                                      int* flag_lds) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *flag_lds = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    arrivals - 1u;
+    __syncthreads();
+    return *flag_lds != 0;
 }
 
 __device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {
@@ -197,8 +219,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // operand of bf16 -136 (exact products) give every column the same row sums,
 // and lane (col 0, kq) of the result holds rows 4kq .. 4kq+3.  Up to 8 rows a
 // thread per (group, row) adds the 128 values in order (measured: cheaper than
-// the MFMA pass when few rows need it).  The chained decode kernel uses the
-// same function, so both produce the same bits.
+// the MFMA pass when few rows need it).
 __device__ __forceinline__ void decode_offset_terms(const unsigned char* lds, int rowb, float* corr,
                                                     const unsigned char* arow, int M, int G, int tid,
                                                     int wave, int col, int kq, int nwave) {

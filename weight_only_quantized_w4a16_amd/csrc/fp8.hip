@@ -17,6 +17,8 @@
 // MFMA or two 16x16x64 int8 MFMAs over the same two 16-byte halves of each
 // lane's operands.
 
+#include <stdio.h>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -388,16 +390,7 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 // ---------------------------------------------------------------------------
 constexpr int F8_BM = 128;
 
-static int f8_cu_count() {
-    static const int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return 256;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return 256;
-        return n;
-    }();
-    return cus;
-}
+static int f8_cu_count() { return device_cu_count(); }
 #ifndef QG_F8_NS                   // stages with 256-column tiles (48 KiB each)
 #define QG_F8_NS 3
 #endif
@@ -568,7 +561,8 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         return;
     }
     // K split: unscaled totals (fp32 or int32) to this slice's slot with agent-scope
-    // stores (coherent across the XCDs' L2s without cache maintenance)
+    // stores (coherent across the XCDs' L2s without cache maintenance); then the
+    // ordered arrival count of arrive_and_check_last
     __shared__ int last_flag;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
@@ -586,13 +580,7 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
             }
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (tid == 0)
-        last_flag = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    (unsigned)(S - 1);
-    __syncthreads();
-    if (!last_flag) return;
+    if (!arrive_and_check_last(&cnt[tile], (unsigned)S, &last_flag)) return;
     constexpr int BN = 128 * NB;
     const int n0 = nt0 * 16;
     // EB elements per thread at once, all their slot loads in flight together
@@ -635,18 +623,8 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-const char* w8a8_kernel_for(int M, int N, int K) {
-    (void)K;
-    if (M == 0) return "none";
-    if (M > 64) return "w8a8_large_m_kernel";
-    const int NT = N / 16;
-    const int ct = (NT % 2 == 0 && NT >= 1024) ? 2 : 1;
-    static const char* names[3][2] = {
-        {"w8a8_small_m_kernel<1, 1>", "w8a8_small_m_kernel<1, 2>"},
-        {"w8a8_small_m_kernel<2, 1>", "w8a8_small_m_kernel<2, 2>"},
-        {"w8a8_small_m_kernel<4, 1>", "w8a8_small_m_kernel<4, 2>"}};
-    return names[M <= 16 ? 0 : M <= 32 ? 1 : 2][ct == 1 ? 0 : 1];
-}
+static int f8_small_ct(int NT) { return (NT % 2 == 0 && NT >= 1024) ? 2 : 1; }
+
 
 // Large-M plan: tile width, K split and workspace layout (slots | counters).
 #ifndef QG_F8_FORCE_NB             // 1 or 2: fixed tile width (0: chosen by launch rounds)
@@ -666,7 +644,7 @@ const char* w8a8_kernel_for(int M, int N, int K) {
 #endif
 struct F8Plan {
     int bm, nb, S, tiles;
-    size_t cnt_off, bytes;
+    size_t part_off, bytes;
 };
 
 // 128-column tiles when 256-column tiles would take fewer, emptier rounds
@@ -705,11 +683,30 @@ static F8Plan f8_plan(int M, int N, int K) {
         }
         p.S = best;
     }
+    if (p.S > 1 && p.tiles > kMaxCounters) p.S = 1;      // one counter per tile
+    // workspace: the counter region, then S slots of M x N partial sums
     if (p.S > 1) {
-        p.cnt_off = ((size_t)p.S * M * N * sizeof(float) + 255) / 256 * 256;
-        p.bytes = p.cnt_off + (size_t)p.tiles * sizeof(unsigned);
+        p.part_off = kCounterBytes;
+        p.bytes = p.part_off + (size_t)p.S * M * N * sizeof(float);
     }
     return p;
+}
+
+// The kernel and its configuration for a shape on the current device, in a
+// per-thread buffer: "w8a8_small_m_kernel<MT, CT>" or
+// "w8a8_large_m_kernel<NS, NB, BM> S=s".
+const char* w8a8_kernel_for(int M, int N, int K) {
+    static thread_local char buf[96];
+    if (M == 0) return "none";
+    if (M <= 64) {
+        snprintf(buf, sizeof buf, "w8a8_small_m_kernel<%d, %d>", M <= 16 ? 1 : M <= 32 ? 2 : 4,
+                 f8_small_ct(N / 16));
+    } else {
+        const F8Plan p = f8_plan(M, N, K);
+        snprintf(buf, sizeof buf, "w8a8_large_m_kernel<%d, %d, %d> S=%d", p.nb == 1 ? QG_F8_NS1 : QG_F8_NS,
+                 p.nb, p.bm, p.S);
+    }
+    return buf;
 }
 
 size_t w8a8_workspace_bytes(int M, int N, int K) {
@@ -729,8 +726,7 @@ static void launch_small(const uint8_t* a, const float* sa, const uint8_t* w, co
 template <class Fmt, int MT>
 static void launch_small_ct(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                             uint16_t* y, int M, int N, int K, hipStream_t st) {
-    const int NT = N / 16;
-    if (NT % 2 == 0 && NT >= 1024)
+    if (f8_small_ct(N / 16) == 2)
         launch_small<Fmt, MT, 2>(a, sa, w, sw, y, M, N, K, st);
     else
         launch_small<Fmt, MT, 1>(a, sa, w, sw, y, M, N, K, st);
@@ -750,8 +746,8 @@ static void launch_w8a8(const uint8_t* a, const float* sa, const uint8_t* w, con
         static_assert(sizeof(elem_t) == sizeof(float), "slot size of the workspace plan");
         const F8Plan p = f8_plan(M, N, K);
         char* wsb = static_cast<char*>(ws);
-        elem_t* part = p.S > 1 ? reinterpret_cast<elem_t*>(wsb) : nullptr;
-        unsigned* cnt = p.S > 1 ? reinterpret_cast<unsigned*>(wsb + p.cnt_off) : nullptr;
+        elem_t* part = p.S > 1 ? reinterpret_cast<elem_t*>(wsb + p.part_off) : nullptr;
+        unsigned* cnt = p.S > 1 ? reinterpret_cast<unsigned*>(wsb) : nullptr;
         const dim3 grid((unsigned)(p.tiles * p.S));
         if (p.bm == 64) {
             if (p.nb == 1)

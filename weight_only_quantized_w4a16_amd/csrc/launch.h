@@ -6,7 +6,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qg {
+
+// Workspace of the K-split GEMMs (qgemm_w4a16, qgemm_w8a8_fp8 / _int8): the
+// first kCounterBytes hold the completion counters (one 32-bit word per output
+// tile or column strip, at most kMaxCounters of them), which every call that
+// uses them leaves at zero; the offset terms and fp32 / int32 partial sums of
+// the call follow.  The counters sit at the same offset for every shape, so a
+// workspace that was zero-filled once serves calls of any shape in any order.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned));
+
+// Compute units of the current device (queried once per device).  The kernel
+// plans, and with them the workspace sizes, depend on it: a size query and the
+// call it is made for must run with the same device current.
+int device_cu_count();
+
+// Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device, once per
+// device (`done` is the kernel's own record of the devices already set up).
+void allow_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done);
 
 // W4A16 path (w4a16.hip)
 void launch_pack_int4_g128(const uint16_t* w, int K, int N, uint32_t* packed,
@@ -37,32 +57,6 @@ void launch_qgemm_w4a8_fp8(const uint8_t* qa, const float* sa, const uint32_t* w
 void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int* offsets,
                                    const uint32_t* wq, const uint16_t* sc, uint16_t* y, int E, int T,
                                    int N, int K, void* ws, hipStream_t s);
-
-// Chained decode (chain.hip)
-struct ChainDesc {          // one GEMM of a chain as the kernel reads it (64 bytes)
-    const uint16_t* a;
-    const uint32_t* wq;
-    const uint16_t* sc;
-    uint16_t* y;
-    int N, K;
-    int units;              // column strips (one per workgroup)
-    int kw;                 // waves per column tile (K split inside the workgroup)
-    int u;                  // groups per pipelined item
-    int nchunks;            // K processed in this many LDS-sized chunks
-    int after_prev;         // wait for the previous GEMM to complete
-    int pad;
-};
-struct ChainHeader {        // first 64 bytes of a plan
-    uint32_t magic;
-    int32_t count, M, grid;
-    uint64_t lds;
-    uint64_t reserved[5];
-};
-constexpr uint32_t kChainMagic = 0x51474331u;   // "QGC1"
-int chain_grid();
-bool chain_plan_one(int M, int N, int K, int P, ChainDesc* d, size_t* lds);
-hipError_t launch_chain(const ChainDesc* plan, int count, int M, size_t lds, unsigned* ws,
-                        hipStream_t s);
 
 // W8A8-FP8 path (fp8.hip)
 void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, float* s,

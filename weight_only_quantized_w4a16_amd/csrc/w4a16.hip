@@ -15,6 +15,10 @@
 // weight, at 7 VALU instructions per 8 weights for the unpack plus one FMA per
 // accumulator per group for the scale.
 
+#include <stdio.h>
+
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -469,13 +473,13 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_grouped_kernel(
 //     whole tiles and stores bf16 directly;
 //   - KW > 1: the KW partial sums of a tile are added in LDS in a fixed order;
 //   - S > 1 slices: each workgroup writes its fp32 partial tile sums to its own
-//     workspace slot, then increments the strip's counter; the workgroup that
-//     arrives last adds the S slots in slice order (deterministic), stores
-//     bf16 and resets the counter to 0.  The slots are written and read with
-//     agent-scope relaxed atomic accesses (coherent across the XCDs without
-//     cache maintenance); a device-wide fence would instead write back and
-//     invalidate every XCD's whole L2 on each call, which costs more than the
-//     GEMM.
+//     workspace slot, then counts its arrival on the strip's counter
+//     (arrive_and_check_last: every wave's slot stores complete before the
+//     increment); the workgroup that arrives last adds the S slots in slice
+//     order (deterministic), stores bf16 and resets the counter to 0.  The
+//     slots are written and read with agent-scope atomic accesses (coherent
+//     across the XCDs without cache maintenance); an agent-scope release fence
+//     would also write back the XCD's L2 in every wave.
 // ---------------------------------------------------------------------------
 constexpr int DK_NWAVE = 8;
 
@@ -644,14 +648,7 @@ __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
         }
     }
     if (S == 1) return;
-    // every thread's slot stores are complete before the counter moves
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (tid == 0)
-        last_flag = (__hip_atomic_fetch_add(&cnt[strip], 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1));
-    __syncthreads();
-    if (!last_flag) return;
+    if (!arrive_and_check_last(&cnt[strip], (unsigned)S, &last_flag)) return;
     // each thread reduces EB elements at once: the loads of all of them (8 slots
     // each) are in flight together, so the tail pays one memory round trip per
     // EB elements; every element still adds its slots in slice order
@@ -799,8 +796,6 @@ __device__ __forceinline__ void large_m_tile(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2;                    // 0..1: row half (BM / 2 rows)
     const int wn = wave & 3;                     // 0..3: column quarter (32 * NB columns)
-    const int col = lane & 15;
-    const int kq = lane >> 4;
     const int mb = (M + BM - 1) / BM;
     // slice `split` holds groups [split*G/S, (split+1)*G/S)
     (void)tiles;
@@ -977,7 +972,8 @@ __device__ __forceinline__ void large_m_tile(
     }
     // K split: this slice's fp32 sums go to its own slot (agent-scope stores:
     // coherent across the XCDs' L2s without cache maintenance); the workgroup
-    // that completes a tile's count adds the S slots in slice order
+    // that completes a tile's count (arrive_and_check_last orders every slot
+    // store before the increment) adds the S slots in slice order
     // (deterministic), stores bf16 and leaves the counter at zero
     __shared__ int last_flag;
 #pragma unroll
@@ -996,13 +992,7 @@ __device__ __forceinline__ void large_m_tile(
             }
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (tid == 0)
-        last_flag = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    (unsigned)(S - 1);
-    __syncthreads();
-    if (!last_flag) return;
+    if (!arrive_and_check_last(&cnt[tile], (unsigned)S, &last_flag)) return;
     constexpr int BN = 128 * NB;
     const int n0 = nt0 * 16;
     // EB elements per thread at once, all their slot loads in flight together
@@ -1341,17 +1331,38 @@ static int ring_umax(int D) {
     return u < QG_DK_MAX_U ? (u < 1 ? 1 : u) : QG_DK_MAX_U;
 }
 
-// compute units of the current device, read once per process (the grid shapes
-// of a plan must not change between its workspace query and its launch)
-static int device_cu_count() {
-    static const int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return 256;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return 256;
-        return n;
-    }();
-    return cus;
+// Per-device host state: the CU count and which devices have a kernel's
+// dynamic-LDS limit raised.  Both are set idempotently (concurrent first calls
+// store the same value), so calls from several threads and devices need no lock.
+constexpr int kMaxDevices = 64;
+
+static int query_cu_count(int dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
+int device_cu_count() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev < 0 || dev >= kMaxDevices) return query_cu_count(dev);
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        n = query_cu_count(dev);
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+void allow_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return;
+    (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    done.fetch_or(bit, std::memory_order_relaxed);
 }
 
 static DecodeCfg decode_cfg(int M, int N, int K) {
@@ -1411,7 +1422,8 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
     // up to 8 rows the small-M kernel, which reads a from L2, is faster (measured:
     // 8B down at B = 8 12.1 -> 11.2 us, 70B down at B = 4 / 8 -5 / -7 %)
     if (M < QG_DK_SPLIT_MIN_M) return c;
-    const int NS = NT / QG_DK_SPLIT_TPS > 0 ? NT / QG_DK_SPLIT_TPS : 1;
+    // one completion counter per strip: at most kMaxCounters strips (more tiles per strip beyond)
+    const int NS = std::min(std::max(NT / QG_DK_SPLIT_TPS, 1), kMaxCounters);
     const int tmax = (NT + NS - 1) / NS;
     int kw1 = 1;
     while (kw1 * 2 <= QG_DK_SPLIT_KW && kw1 * 2 * tmax <= DK_NWAVE) kw1 *= 2;
@@ -1433,24 +1445,22 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
     return c;
 }
 
+// workspace: the counter region (one counter per strip), then S slots of
+// N/16 fp32 tiles
 static size_t decode_ws_bytes(const DecodeCfg& c, int N) {
     if (!c.ok || c.S == 1) return 0;
-    const size_t part = (size_t)c.S * (N / 16) * 256 * sizeof(float);
-    return part + (size_t)c.NS * sizeof(unsigned);
+    return kCounterBytes + (size_t)c.S * (N / 16) * 256 * sizeof(float);
 }
 
 template <int KW, int U, int D>
 static void launch_decode_t(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
                             int M, int N, int K, const DecodeCfg& c, int NS, void* ws,
                             hipStream_t s) {
-    static bool attr_set = false;   // allow up to the LDS budget (the default limit is 64 KiB)
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_decode_kernel<KW, U, D>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, QG_DK_LDS_BUDGET);
-        attr_set = true;
-    }
-    float* part = static_cast<float*>(ws);
-    unsigned* cnt = ws ? reinterpret_cast<unsigned*>(part + (size_t)c.S * (N / 16) * 256) : nullptr;
+    static std::atomic<uint64_t> lds_set{0};   // up to the LDS budget (the default limit is 64 KiB)
+    allow_dynamic_lds(reinterpret_cast<const void*>(&w4a16_decode_kernel<KW, U, D>), QG_DK_LDS_BUDGET,
+                      lds_set);
+    unsigned* cnt = ws ? static_cast<unsigned*>(ws) : nullptr;
+    float* part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes) : nullptr;
     hipLaunchKernelGGL((w4a16_decode_kernel<KW, U, D>), dim3(c.S * NS), dim3(DK_NWAVE * 64), c.lds, s,
                        a, wq, sc, y, M, N, K, c.S, NS, part, cnt);
 }
@@ -1510,8 +1520,8 @@ static int large_m_nb(int M, int N, int bm) {
     return 8 * rounds128 < 14 * rounds256 ? 1 : 2;
 }
 
-// Large-M plan: tile width, K split and workspace layout (corr | slots | counters),
-// a function of the shape and the device's CU count only.
+// Large-M plan: tile width, K split and workspace layout (counters | corr |
+// slots), a function of the shape and the device's CU count only.
 struct LargePlan {
     int bm, nb, S, tiles, Mp;
     size_t corr_off, part_off, cnt_off, bytes;
@@ -1557,11 +1567,13 @@ static LargePlan large_plan(int M, int N, int K) {
         }
         p.S = best;
     }
+    // a split runs only while the tiles do not fill the CUs: one counter per tile
+    if (p.S > 1 && p.tiles > kMaxCounters) p.S = 1;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-    p.corr_off = 0;
-    p.part_off = al((size_t)G * p.Mp * sizeof(float));
-    p.cnt_off = al(p.part_off + (p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0));
-    p.bytes = p.cnt_off + (p.S > 1 ? (size_t)p.tiles * sizeof(unsigned) : 0);
+    p.cnt_off = 0;
+    p.corr_off = kCounterBytes;
+    p.part_off = al(p.corr_off + (size_t)G * p.Mp * sizeof(float));
+    p.bytes = p.part_off + (p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0);
     return p;
 }
 
@@ -1596,22 +1608,29 @@ static void launch_large(const uint16_t* a, const uint32_t* wq, const uint16_t* 
     }
 }
 
+// The kernel and its compile-time configuration for a shape on the current
+// device, in a per-thread buffer: "w4a16_decode_kernel<KW, U, D> S=s",
+// "w4a16_small_m_kernel<MT, CT>" or "w4a16_large_m_kernel<NS, NB, BM> S=s".
 const char* w4a16_kernel_for(int M, int N, int K) {
+    static thread_local char buf[96];
     if (M == 0) return "none";
-    if (decode_cfg(M, N, K).ok) return "w4a16_decode_kernel";
-    if (M <= 64 && !use_large_m(M, N, K)) {
-        const int NT = N / 16;
-        const int ct = small_ct(NT);
-        static const char* names[3][3] = {
-            {"w4a16_small_m_kernel<1, 1>", "w4a16_small_m_kernel<1, 2>", "w4a16_small_m_kernel<1, 4>"},
-            {"w4a16_small_m_kernel<2, 1>", "w4a16_small_m_kernel<2, 2>", "w4a16_small_m_kernel<2, 4>"},
-            {"w4a16_small_m_kernel<4, 1>", "w4a16_small_m_kernel<4, 2>", "w4a16_small_m_kernel<4, 4>"}};
-        return names[M <= 16 ? 0 : M <= 32 ? 1 : 2][ct == 1 ? 0 : ct == 2 ? 1 : 2];
+    const DecodeCfg dc = decode_cfg(M, N, K);
+    if (dc.ok) {
+        const int u = dc.U > 16 / dc.D ? 1 : dc.U;   // the instantiation launch_decode_u picks
+        snprintf(buf, sizeof buf, "w4a16_decode_kernel<%d, %d, %d> S=%d", dc.KW, u,
+                 dc.KW == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D, dc.S);
+    } else if (M <= 64 && !use_large_m(M, N, K)) {
+        snprintf(buf, sizeof buf, "w4a16_small_m_kernel<%d, %d>", M <= 16 ? 1 : M <= 32 ? 2 : 4,
+                 small_ct(N / 16));
+    } else {
+        const LargePlan p = large_plan(M, N, K);
+        snprintf(buf, sizeof buf, "w4a16_large_m_kernel<%d, %d, %d> S=%d", QG_LM_NS, p.nb, p.bm, p.S);
     }
-    return "w4a16_large_m_kernel";
+    return buf;
 }
 
 size_t w4a16_workspace_bytes(int M, int N, int K) {
+    if (M == 0) return 0;
     if (M <= 16) return decode_ws_bytes(decode_cfg(M, N, K), N);
     if (!use_large_m(M, N, K)) return 0;
     return large_plan(M, N, K).bytes;
@@ -1629,12 +1648,11 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
     } else if (!use_large_m(M, N, K)) {
         launch_small_ct<4>(a, packed, scales, y, M, N, K, s);
     } else {
-        const int Mp = round_up(M, LM_MAX_BM);
-        const int G = K / 128;
-        float* corr = static_cast<float*>(ws);
-        const size_t n = (size_t)G * Mp * 16;      // 16 lanes per (group, row)
+        const LargePlan p = large_plan(M, N, K);
+        float* corr = reinterpret_cast<float*>(static_cast<char*>(ws) + p.corr_off);
+        const size_t n = (size_t)(K / 128) * p.Mp * 16;      // 16 lanes per (group, row)
         hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
-                           0, s, a, M, Mp, K, corr);
+                           0, s, a, M, p.Mp, K, corr);
         launch_large(a, packed, scales, ws, y, M, N, K, s);
     }
 }

@@ -14,8 +14,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# QGEMM_LIBRARY selects another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("QGEMM_LIBRARY") or os.path.join(_PKG, "libqgemm.so")
+LIB_PATH = os.path.join(_PKG, "libqgemm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -42,10 +41,6 @@ _SIGS = {
     "pack_int4_g128_mse": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "dequant_int4_g128": (_I, [_P, _P, _I, _I, _P, _P, _P]),
     "qgemm_w4a16": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
-    "qg_w4a16_chain_plan_bytes": (_SZ, [_I]),
-    "qg_w4a16_chain_workspace_bytes": (_SZ, [_I]),
-    "qg_w4a16_chain_plan": (_I, [_P, _I, _I, _P, _SZ]),
-    "qgemm_w4a16_chain": (_I, [_P, _P, _P, _SZ, _P]),
     "qg_w4a16_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "qgemm_w4a16_grouped": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
     "quant_act_per_token": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -439,53 +434,3 @@ class W8A8Int8Linear:
         ws, need = self.workspace(M)
         qgemm_w8a8_int8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
         return y
-
-
-# ---- chained decode -----------------------------------------------------------
-
-class ChainGemm(ctypes.Structure):
-    """qg_w4a16_chain_gemm of include/qgemm.h."""
-    _fields_ = [("a_bf16", ctypes.c_void_p), ("packed", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p), ("y_bf16", ctypes.c_void_p),
-                ("N", ctypes.c_int32), ("K", ctypes.c_int32),
-                ("after_previous", ctypes.c_int32), ("reserved", ctypes.c_int32)]
-
-
-def chain_plan(gemms, M):
-    """Plan a chain on the host.  gemms: list of (a, Int4G128Weight, y, after_previous).
-    Returns the plan bytes (ctypes buffer)."""
-    arr = (ChainGemm * len(gemms))()
-    for i, (a, w, y, dep) in enumerate(gemms):
-        arr[i] = ChainGemm(_ptr(a), _ptr(w.packed), _ptr(w.scales), _ptr(y), w.N, w.K, int(dep), 0)
-    nbytes = _lib.qg_w4a16_chain_plan_bytes(len(gemms))
-    plan = ctypes.create_string_buffer(nbytes)
-    _check("qg_w4a16_chain_plan", _lib.qg_w4a16_chain_plan(ctypes.addressof(arr), len(gemms), M,
-                                                           ctypes.addressof(plan), nbytes))
-    return plan
-
-
-class W4A16Chain:
-    """The W4A16 GEMMs of one decode step in one persistent launch.
-
-    gemms: list of (a [M, K], Int4G128Weight, y [M, N], after_previous).  The
-    tensors must stay alive and in place as long as the chain is used."""
-
-    def __init__(self, gemms, M):
-        self.M = M
-        self.count = len(gemms)
-        self._keep = gemms
-        self.plan_host = chain_plan(gemms, M)
-        dev = gemms[0][0].device
-        host = torch.frombuffer(bytearray(self.plan_host.raw), dtype=torch.uint8)
-        self.plan_dev = host.to(dev)
-        self.ws_bytes = _lib.qg_w4a16_chain_workspace_bytes(self.count)
-        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
-
-    def __call__(self, stream=None):
-        _check("qgemm_w4a16_chain",
-               _lib.qgemm_w4a16_chain(ctypes.addressof(self.plan_host), _ptr(self.plan_dev),
-                                      _ptr(self.ws), self.ws_bytes, _stream(stream)))
-
-    def error_word(self):
-        """Nonzero if a dependency wait of a past call exceeded its bound."""
-        return int(self.ws[4:8].view(torch.int32).item())

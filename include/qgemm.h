@@ -197,6 +197,28 @@ qg_status qgemm_w4a16(const uint16_t *a_bf16, const uint32_t *packed,
                       qg_stream stream);
 
 /*
+ * qgemm_w4a16_noalloc -- qgemm_w4a16 without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops and harnesses that forbid hipMalloc.  It allocates nothing and
+ * calls no allocating routine.
+ *
+ * Same arguments (minus the workspace), kernels, arithmetic and results as
+ * qgemm_w4a16.  Its workspace is a library-owned device array of
+ * QG_NOALLOC_SCRATCH_BYTES per device (held from the library's load until the
+ * process ends): shapes whose qg_w4a16_workspace_bytes exceeds it are rejected
+ * with QG_ERR_WORKSPACE before any launch; the array's address on the current
+ * device is looked up on the first call there (QG_ERR_HIP if that fails).
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (other streams, other threads) race and give undefined
+ * results; calls in one stream's order are safe.  The array's completion
+ * counters are zero at load and every call leaves them zero.
+ */
+#define QG_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+qg_status qgemm_w4a16_noalloc(const uint16_t *a_bf16, const uint32_t *packed,
+                              const uint16_t *scales, uint16_t *y_bf16,
+                              int M, int N, int K, qg_stream stream);
+
+/*
  * qgemm_w4a16_grouped -- the W4A16 product of a mixture-of-experts layer: each
  * routed row times its own expert's INT4 g128 weight, bf16 in and out.
  * [P1, the mixture-of-experts section: a batch of B tokens sends about B k / E

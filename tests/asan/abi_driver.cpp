@@ -70,6 +70,15 @@ int main() {
     EXPECT_LAUNCH(qgemm_w4a16(a16, w32, s16, y16, 100, 32, 256, ws, 4096, nullptr));
     EXPECT(qg_w4a16_workspace_bytes(100, 32, 256) == 4096);
     EXPECT(qg_w4a16_workspace_bytes(100, 30, 256) == 0);
+    // allocation-free variant: the library's scratch serves the workspace
+    EXPECT_LAUNCH(qgemm_w4a16_noalloc(a16, w32, s16, y16, 4, 32, 256, nullptr));
+    EXPECT_LAUNCH(qgemm_w4a16_noalloc(a16, w32, s16, y16, 100, 32, 256, nullptr));
+    EXPECT_STATUS(qgemm_w4a16_noalloc(a16, w32, s16, y16, 0, 32, 256, nullptr), QG_OK);
+    EXPECT_STATUS(qgemm_w4a16_noalloc(nullptr, w32, s16, y16, 4, 32, 256, nullptr), QG_ERR_NULL);
+    EXPECT_STATUS(qgemm_w4a16_noalloc(a16, w32, s16, y16, 4, 30, 256, nullptr), QG_ERR_SHAPE);
+    EXPECT_STATUS(qgemm_w4a16_noalloc(a16 + 1, w32, s16, y16, 4, 32, 256, nullptr), QG_ERR_ALIGN);
+    // a shape whose workspace exceeds the scratch (the stub's size query says 64 MiB)
+    EXPECT_STATUS(qgemm_w4a16_noalloc(a16, w32, s16, y16, 100, 128000, 256, nullptr), QG_ERR_WORKSPACE);
 
     // grouped W4A16 and W4A8
     const int32_t off_ok[4] = {0, 3, 3, 8};

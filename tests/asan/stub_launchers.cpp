@@ -15,7 +15,9 @@ namespace qg {
 void launch_pack_int4_g128(const uint16_t*, int, int, uint32_t*, uint16_t*, hipStream_t) { ++g_launches; }
 void launch_pack_int4_g128_mse(const uint16_t*, int, int, int, uint32_t*, uint16_t*, hipStream_t) { ++g_launches; }
 void launch_dequant_int4_g128(const uint32_t*, const uint16_t*, int, int, uint16_t*, uint8_t*, hipStream_t) { ++g_launches; }
-size_t w4a16_workspace_bytes(int M, int, int) { return M > 64 ? 4096 : 0; }
+size_t w4a16_workspace_bytes(int M, int N, int) { return M > 64 ? (N > 100000 ? (size_t(64) << 20) : 4096) : 0; }
+static unsigned char g_scratch[256];
+void* noalloc_scratch() { return g_scratch; }
 const char* w4a16_kernel_for(int, int, int) { return "stub"; }
 void launch_qgemm_w4a16(const uint16_t*, const uint32_t*, const uint16_t*, uint16_t*, int, int, int, void*,
                         hipStream_t) { ++g_launches; }

@@ -139,6 +139,22 @@ qg_status qgemm_w4a16(const uint16_t* a_bf16, const uint32_t* packed, const uint
     return launched();
 }
 
+qg_status qgemm_w4a16_noalloc(const uint16_t* a_bf16, const uint32_t* packed, const uint16_t* scales,
+                              uint16_t* y_bf16, int M, int N, int K, qg_stream stream) {
+    static_assert(qg::kNoAllocScratchBytes == QG_NOALLOC_SCRATCH_BYTES, "scratch limit of the header");
+    if (!shape_ok(M, N, K)) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    if (!a_bf16 || !packed || !scales || !y_bf16) return QG_ERR_NULL;
+    if (!aligned(a_bf16, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y_bf16, 16))
+        return QG_ERR_ALIGN;
+    const size_t need = qg::w4a16_workspace_bytes(M, N, K);
+    if (need > qg::kNoAllocScratchBytes) return QG_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0 && (ws = qg::noalloc_scratch()) == nullptr) return QG_ERR_HIP;
+    qg::launch_qgemm_w4a16(a_bf16, packed, scales, y_bf16, M, N, K, ws, as_stream(stream));
+    return launched();
+}
+
 qg_status qgemm_w4a16_grouped(const uint16_t* a_bf16, const int32_t* offsets,
                               const uint32_t* packed, const uint16_t* scales, uint16_t* y_bf16,
                               int E, int T, int N, int K, void* workspace, size_t workspace_bytes,

@@ -19,6 +19,16 @@ namespace qg {
 constexpr size_t kCounterBytes = 64 * 1024;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned));
 
+// Devices whose host state (CU count, scratch address) is cached.
+constexpr int kMaxDevices = 64;
+
+// Library-owned scratch of qgemm_w4a16_noalloc: one array per device, the
+// size limit of the workspace that entry point can serve.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+// Device address of the current device's copy of that array (looked up once
+// per device), or nullptr if the lookup fails.
+void* noalloc_scratch();
+
 // Compute units of the current device (queried once per device).  The kernel
 // plans, and with them the workspace sizes, depend on it: a size query and the
 // call it is made for must run with the same device current.

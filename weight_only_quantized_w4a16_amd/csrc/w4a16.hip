@@ -1258,6 +1258,31 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
     else go(ic<4>{});
 }
 
+// ---- library-owned scratch for callers that cannot allocate -------------------
+// qgemm_w4a16_noalloc uses this array as its workspace.  Each device holds its
+// own copy at its own address: host code reads that address once per device
+// with hipGetSymbolAddress (with the device current) and passes it to the
+// kernels; the array's name itself is not a device address on the host.  The
+// array is zero when the code object is loaded, and every call leaves its
+// counter region at zero again (the offset terms and partial sums are written
+// before they are read), so no call needs to clear it first.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch() {
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    addr[dev].store(q, std::memory_order_release);
+    return q;
+}
+
 // ---- decode-kernel configuration (M <= 16), a function of the shape only ----
 #ifndef QG_DK_WIDE_TILES          // one workgroup strip per CU from this many column tiles
 #define QG_DK_WIDE_TILES 512
@@ -1334,7 +1359,6 @@ static int ring_umax(int D) {
 // Per-device host state: the CU count and which devices have a kernel's
 // dynamic-LDS limit raised.  Both are set idempotently (concurrent first calls
 // store the same value), so calls from several threads and devices need no lock.
-constexpr int kMaxDevices = 64;
 
 static int query_cu_count(int dev) {
     int n = 0;

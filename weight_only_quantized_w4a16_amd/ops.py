@@ -41,6 +41,7 @@ _SIGS = {
     "pack_int4_g128_mse": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "dequant_int4_g128": (_I, [_P, _P, _I, _I, _P, _P, _P]),
     "qgemm_w4a16": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "qgemm_w4a16_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "qg_w4a16_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "qgemm_w4a16_grouped": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
     "quant_act_per_token": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -143,6 +144,14 @@ def qgemm_w4a16(a_bf16, packed, scales, y_bf16, M, N, K, workspace=None, workspa
     _check("qgemm_w4a16", _lib.qgemm_w4a16(_ptr(a_bf16), _ptr(packed), _ptr(scales), _ptr(y_bf16),
                                            M, N, K, _ptr(workspace), workspace_bytes,
                                            _stream(stream)))
+
+
+def qgemm_w4a16_noalloc(a_bf16, packed, scales, y_bf16, M, N, K, stream=None):
+    _check("qgemm_w4a16_noalloc", _lib.qgemm_w4a16_noalloc(_ptr(a_bf16), _ptr(packed), _ptr(scales),
+                                                           _ptr(y_bf16), M, N, K, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20    # QG_NOALLOC_SCRATCH_BYTES of include/qgemm.h
 
 
 def quant_act_per_token(a_bf16, M, K, a_e4m3, a_scale, stream=None):

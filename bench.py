@@ -13,9 +13,13 @@ bracket exactly `--steps` replays after `--warmup` untimed ones.
 
 Default workload "decode": B in {1, 2, 4, 8, 16}; the JSON line's value is
 the algorithmic HBM throughput at --batch (default 16), the other batches are
-listed under "by_batch".  Other workloads (one line each):
-  large-batch  the same stack at B in {32 .. 1024} against a dense bf16 stack
-               (hipBLASLt through torch.matmul), MFMA utilisation and crossover
+listed under "by_batch".  The same line carries "single_gemm" (a[4, 4096] x
+W[4096, 4096] over 64 rotating weight copies) and "large_batch" (the stack at
+B in {32 .. 1024} against the dense bf16 stack in both weight layouts: MFMA
+utilisation with its roofline at B = 512, the crossover, the oracle's CPU
+baseline); --no-large-batch leaves the latter out.  Other workloads (one line
+each):
+  large-batch  only the large-batch half
   fp8          the W8A8-FP8 stack (per-token activation quantization + fp8 GEMM)
   int8         the W8A8-INT8 stack (per-token activation quantization + int8 GEMM)
   70b          the Llama-3-70B W4A16 stack on one GPU
@@ -80,6 +84,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--batches", default="",
                    help="large-batch workload: extra batch sizes to time, comma separated")
+    p.add_argument("--no-large-batch", action="store_true",
+                   help="decode workload: skip the large-batch half (B = 32 .. 1024 against dense bf16)")
+    p.add_argument("--lb-steps", type=int, default=20,
+                   help="timed replays per large-batch step (B = 32 .. 1024)")
     p.add_argument("--only-batch", action="store_true",
                    help="decode workload: time only --batch (short profiled runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -248,7 +256,7 @@ def cpu_baseline(B):
     """The oracle (numpy fp32 dequant + fp64 matmul) on the host cores, on a bounded
     sample of the decode step: one decoder layer's four GEMMs plus 1/8 of the LM
     head's columns, each timed REPS times, scaled to the full 129-GEMM step."""
-    REPS = 8
+    REPS = 24
     from oracle import int4_g128 as q4
     from weight_only_quantized_w4a16_amd import synth
     try:
@@ -455,39 +463,30 @@ def main():
         run_70b(args, torch, ops, synth)
 
 
-def time_launches(torch, fn, steps, warmup):
-    """`warmup` untimed calls, then exactly `steps` calls bracketed by HIP events on
-    the launch stream; returns ms per call."""
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        fn()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+LARGE_BATCHES = [32, 64, 128, 256, 384, 512, 576, 640, 768, 1024]
+LARGE_ROOFLINE_B = 512         # the large-batch roofline and CPU baseline are quoted here
 
 
 def run_decode(args, torch, ops, synth):
-    batches = [args.batch] if args.only_batch else sorted({1, 2, 4, 8, 16, args.batch})
-    stack = Stack(ops, synth, torch, "8b", batches)
+    """The default run: the decode step at B in {1, 2, 4, 8, 16} (the headline
+    value, at --batch), the single-GEMM configuration, and the large-batch half
+    of the metric (MFMA utilisation at B >= 512, the crossover against dense
+    bf16), all in one JSON line."""
+    decode_batches = [args.batch] if args.only_batch else sorted({1, 2, 4, 8, 16, args.batch})
+    large = [] if (args.only_batch or args.no_large_batch) else LARGE_BATCHES
+    stack = Stack(ops, synth, torch, "8b", decode_batches)
     print(f"[bench] packed {len(stack.layers)} GEMMs, {stack.bytes(0) / 1e9:.3f} GB of weights+scales",
           file=sys.stderr, flush=True)
     by_batch = {}
-    for B in batches:
+    for B in decode_batches:
         nbytes = stack.bytes(B)
         rec = {}
         g = graph_of(torch, lambda: stack.step(B))
         ms_g = time_graph(torch, g, args.steps, args.warmup)
         rec["step_ms_p10_p50_p90"] = replay_percentiles(torch, g)
         del g
-        rec["graph_ms"] = round(ms_g, 4)
         ms = ms_g
-        rec.update({"ms_per_step": ms, "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3),
+        rec.update({"ms_per_step": round(ms, 5), "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3),
                     "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)})
         by_batch[str(B)] = rec
         print(f"[bench] B={B}: {rec}", file=sys.stderr, flush=True)
@@ -542,58 +541,213 @@ def run_decode(args, torch, ops, synth):
             "value": round(nbytes / sec / 1e12, 6), "unit": "TB/s", "cores": threads,
             "kind": "oracle", "seconds_per_step": round(sec, 2),
             "sample": (f"B={B}: layer-0 qkv/o/gate_up/down (each x32) + LM head columns "
-                       f"[0, 16032) (x8), mean of 8 timed runs each; numpy fp32 dequant + fp64 matmul; "
+                       f"[0, 16032) (x8), mean of 24 timed runs each; numpy fp32 dequant + fp64 matmul; "
                        + ", ".join(parts))}
+    if not args.only_batch:
+        del stack
+        torch.cuda.empty_cache()
+        out["single_gemm"] = single_gemm_part(args, torch, ops, synth)
+    if large:
+        out["large_batch"] = large_batch_part(args, torch, ops, synth, large)
     print(json.dumps(out), flush=True)
 
 
-def run_large_batch(args, torch, ops, synth):
-    batches = [32, 64, 128, 256, 384, 512, 1024]
-    if args.batches:
-        # extra batches (e.g. a finer sweep around the crossover), timed alongside;
-        # with --only-batch only these (short profiled runs)
-        extra = {int(x) for x in args.batches.split(",")}
-        batches = sorted(extra if args.only_batch else set(batches) | extra)
+def single_gemm_part(args, torch, ops, synth):
+    """The single-GEMM configuration: a[4, 4096] x W[4096, 4096] (weight seed 0,
+    activation seed 1), timed over 64 copies of the packed weight (each copy
+    quantized from its own draw), called in turn inside one HIP graph, so every
+    call streams its weight from HBM (64 x 8.65 MB = 554 MB, beyond the 256 MB
+    memory-side cache)."""
+    M, K, N, COPIES = 4, 4096, 4096, 64
+    dev = torch.device("cuda:0")
+    ws = []
+    for c in range(COPIES):
+        w = synth.normal_bf16_device((K, N), 7000 + c, synth.WEIGHT_STD, dev)
+        ws.append(ops.Int4G128Weight.from_bf16(w))
+        del w
+    w0 = synth.weights(K, N, seed=0)                       # copy 0 is the configuration's own draw
+    ws[0] = ops.Int4G128Weight.from_bf16(torch.from_numpy(w0.view(np.int16)).view(torch.bfloat16).to(dev))
+    a = torch.from_numpy(synth.activations(M, K, seed=1).view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert ops.w4a16_workspace_bytes(M, N, K) == 0
+
+    def calls():
+        for wt in ws:
+            ops.qgemm_w4a16(a, wt.packed, wt.scales, y, M, N, K)
+    g = graph_of(torch, calls)
+    ms = time_graph(torch, g, args.steps, args.warmup)
+    del g
+    us = ms * 1e3 / COPIES
+    nbytes = w4a16_bytes(M, K, N)
+    rec = {"workload": "single W4A16 GEMM a[4, 4096] x W[4096, 4096], 64 rotating weight copies in one "
+                       "HIP graph (HBM-resident weights)",
+           "kernel": ops.w4a16_kernel_for(M, N, K), "us_per_gemm": round(us, 3),
+           "algorithmic_bytes": nbytes, "TB_s": round(nbytes / (us * 1e-6) / 1e12, 3),
+           "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_single_gemm()
+    print(f"[bench] single GEMM: {rec}", file=sys.stderr, flush=True)
+    return rec
+
+
+def cpu_baseline_single_gemm(reps=5):
+    """The oracle on the single-GEMM configuration, the fp32 dequantization and the
+    fp64 product timed separately, on every host core and on one core."""
+    from oracle import int4_g128 as q4
+    from oracle.bf16 import bf16_bits_to_f32
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from weight_only_quantized_w4a16_amd import synth
+    w = synth.weights(4096, 4096, seed=0)
+    a = synth.activations(4, 4096, seed=1)
+    codes, s = q4.quantize(w)                     # offline: not timed
+    out = {"unit": "us per GEMM", "kind": "oracle"}
+    for label, limit in (("all_cores", None), ("one_core", 1)):
+        with threadpool_limits(limits=limit):
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            t_deq = t_mm = 0.0
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                wd = q4.dequant_f32(codes, s).astype(np.float64)
+                t1 = time.perf_counter()
+                bf16_bits_to_f32(a).astype(np.float64) @ wd
+                t2 = time.perf_counter()
+                t_deq += t1 - t0
+                t_mm += t2 - t1
+        out[label] = {"cores": threads, "dequant_us": round(t_deq / reps * 1e6, 1),
+                      "matmul_us": round(t_mm / reps * 1e6, 1),
+                      "value": round((t_deq + t_mm) / reps * 1e6, 1)}
+    out["value"] = out["all_cores"]["value"]
+    out["cores"] = out["all_cores"]["cores"]
+    out["sample"] = f"the whole GEMM, mean of {reps} runs (dequant and fp64 matmul timed separately)"
+    return out
+
+
+def cpu_baseline_large(B):
+    """The oracle on a bounded sample of the large-batch step: layer 0's four
+    GEMMs at B rows and 1/16 of the LM head's columns, each timed 8 times,
+    scaled to the 129-GEMM step (x32 and x16)."""
+    from oracle import int4_g128 as q4
+    from threadpoolctl import threadpool_info
+    from weight_only_quantized_w4a16_amd import synth
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    total, parts = 0.0, []
+    shapes = [(name, K, N, 32, j) for j, (name, K, N) in enumerate(synth.LLAMA3_8B_LAYER)]
+    shapes.append(("lm_head/16", synth.LLAMA3_8B_HEAD[1], synth.LLAMA3_8B_HEAD[2] // 16, 16, None))
+    REPS = 8
+    for name, K, N, mult, j in shapes:
+        seed = synth.weight_seed(0, j) if j is not None else synth.weight_seed(32, 0)
+        w = synth.weights(K, N, seed=seed)
+        a = synth.activations(B, K, seed=seed + 1000)
+        codes, s = q4.quantize(w)                 # offline: not timed
+        del w
+        t0 = time.perf_counter()
+        for _ in range(REPS):
+            q4.gemm_ref(a, codes, s)
+        dt = (time.perf_counter() - t0) / REPS
+        total += mult * dt
+        parts.append(f"{name} {dt:.2f}s")
+        del codes, s
+    return total, threads, parts
+
+
+def large_batch_part(args, torch, ops, synth, batches):
+    """The same W4A16 stack at large batches against the dense bf16 stack of the
+    same weights, stored both as [K, N] (torch.matmul(a, w)) and in the
+    checkpoint layout [N, K] (a @ w.T, what a linear layer computes);
+    the crossover is located against the faster dense layout at each batch.
+    Each step is a HIP graph, `steps` replays timed with HIP events."""
+    steps, warmup = args.lb_steps, max(2, min(args.warmup, 5))
     stack = Stack(ops, synth, torch, "8b", batches)
     dev = torch.device("cuda:0")
-    # the dense bf16 baseline: the same shapes, fresh bf16 weights (15.0 GB)
-    dense = []
+    dense_kn, dense_nk = [], []
     for idx, (name, K, N) in enumerate(stack.shapes):
         layer, j = divmod(idx, 4)
-        dense.append(synth.normal_bf16_device((K, N), synth.weight_seed(layer, j), synth.WEIGHT_STD, dev))
+        w = synth.normal_bf16_device((K, N), synth.weight_seed(layer, j), synth.WEIGHT_STD, dev)
+        dense_kn.append(w)
+        dense_nk.append(w.t().contiguous())
+    torch.cuda.synchronize()
     res = {}
     for B in batches:
         g = graph_of(torch, lambda: stack.step(B))
-        ms4 = time_graph(torch, g, args.steps, args.warmup)
+        ms4 = time_graph(torch, g, steps, warmup)
         del g
 
-        def dense_step():
-            for r, w in zip(stack.layers, dense):
+        def kn_step():
+            for r, w in zip(stack.layers, dense_kn):
                 torch.matmul(r["a"][:B], w, out=r["y"][:B])
-        g = graph_of(torch, dense_step)
-        ms16 = time_graph(torch, g, args.steps, args.warmup)
+
+        def nk_step():
+            for r, w in zip(stack.layers, dense_nk):
+                torch.matmul(r["a"][:B], w.t(), out=r["y"][:B])      # a @ w.T, as a linear layer runs
+        g = graph_of(torch, kn_step)
+        ms_kn = time_graph(torch, g, steps, warmup)
+        del g
+        g = graph_of(torch, nk_step)
+        ms_nk = time_graph(torch, g, steps, warmup)
         del g
         fl = stack.flops(B)
-        res[str(B)] = {"w4a16_ms": round(ms4, 4), "bf16_ms": round(ms16, 4),
-                       "w4a16_mfma_frac": round(fl / (ms4 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
-                       "bf16_mfma_frac": round(fl / (ms16 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+        frac = lambda t: round(fl / (t * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)
+        res[str(B)] = {"w4a16_ms": round(ms4, 4), "bf16_kn_ms": round(ms_kn, 4), "bf16_nk_ms": round(ms_nk, 4),
+                       "w4a16_mfma_frac": frac(ms4), "bf16_kn_mfma_frac": frac(ms_kn),
+                       "bf16_nk_mfma_frac": frac(ms_nk),
                        "w4a16_TB_s": round(stack.bytes(B) / (ms4 * 1e-3) / 1e12, 3)}
-        print(f"[bench] B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
-    # the smallest measured batch from which W4A16 is not faster at every larger one
+        print(f"[bench] large B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
+    # the smallest measured batch from which W4A16 is not faster than the faster
+    # dense layout at every larger measured batch
     cross = None
     for b in sorted(res, key=int, reverse=True):
-        if res[b]["w4a16_ms"] < res[b]["bf16_ms"]:
+        r = res[b]
+        if r["w4a16_ms"] < min(r["bf16_kn_ms"], r["bf16_nk_ms"]):
             break
         cross = int(b)
-    B = 512 if "512" in res else batches[-1]
+    B = LARGE_ROOFLINE_B
+    fl = stack.flops(B)
+    ms4 = res[str(B)]["w4a16_ms"]
+    launches = len(stack.layers)
+    avg_us = ms4 * 1e3 / launches
+    achieved = fl / launches / (avg_us * 1e-6) / 1e12
+    kernels = sorted({ops.w4a16_kernel_for(B, r["N"], r["K"]) for r in stack.layers})
+    out = {"batches": batches, "steps": steps, "warmup": warmup, "by_batch": res,
+           "crossover_batch_w4a16_not_faster": cross,
+           "crossover_rule": "smallest measured B from which W4A16 is not faster than the faster dense "
+                             "bf16 layout at every larger measured B",
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": f"w4a16_large_m_kernel with its offset-term pre-pass "
+                                  f"(w4a16_group_rowsum_kernel), one GEMM call = both launches; "
+                                  f"{launches} calls per step at B={B}: " + "; ".join(kernels),
+                        "batch": B, "calls_per_step": launches,
+                        "algorithmic_flops_per_call": round(fl / launches),
+                        "avg_call_us": round(avg_us, 3)}}
+    if not args.no_cpu_baseline:
+        sec, threads, parts = cpu_baseline_large(B)
+        out["cpu_baseline"] = {
+            "value": round(fl / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds_per_step": round(sec, 2),
+            "sample": f"B={B}: layer-0 qkv/o/gate_up/down (x32) + LM head columns [0, 8016) (x16), "
+                      f"mean of 8 timed runs each; numpy fp32 dequant + fp64 matmul; " + ", ".join(parts)}
+    del dense_kn, dense_nk, stack
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_large_batch(args, torch, ops, synth):
+    """Only the large-batch half (with --batches: extra batch sizes)."""
+    batches = LARGE_BATCHES
+    if args.batches:
+        extra = {int(x) for x in args.batches.split(",")}
+        batches = sorted(extra if args.only_batch else set(batches) | extra)
+    lb = large_batch_part(args, torch, ops, synth, batches)
+    B = LARGE_ROOFLINE_B if str(LARGE_ROOFLINE_B) in lb["by_batch"] else batches[-1]
     out = {"metric": "Llama-3-8B W4A16 decode-step ms & HBM TB/s vs batch; MFMA util at B>=512",
-           "value": res[str(B)]["w4a16_mfma_frac"], "unit": f"fraction of bf16 MFMA peak at B={B}",
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": res[str(B)]["w4a16_ms"], "higher_is_better": True, "scaling": "weak",
+           "value": lb["by_batch"][str(B)]["w4a16_mfma_frac"], "unit": f"fraction of bf16 MFMA peak at B={B}",
+           "n_gpus": 1, "steps": lb["steps"], "warmup": lb["warmup"],
+           "ms_per_step": lb["by_batch"][str(B)]["w4a16_ms"], "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "int4-g128 x bf16 -> fp32 acc (bf16 MFMA)",
-           "data": "synthetic", "config": {"workload": "Llama-3-8B W4A16 stack vs dense bf16 stack (torch.matmul)",
+           "data": "synthetic", "config": {"workload": "Llama-3-8B W4A16 stack vs dense bf16 stack "
+                                                       "([K, N] and [N, K] weights, hipBLASLt via torch)",
                                            "batch": B},
-           "by_batch": res, "crossover_batch_w4a16_not_faster": cross}
+           "large_batch": lb}
     print(json.dumps(out), flush=True)
 
 

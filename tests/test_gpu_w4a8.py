@@ -77,10 +77,13 @@ def test_w4a8_llama3_shapes_sampled(ops, B, j, name, K, N):
 
 
 # means of 23, 2.5 and 61 rows per non-empty expert: 16-, 32- and 64-row items;
-# 64-row items split the columns over the waves (N a multiple of 128)
+# from a mean of 33 rows and N >= 256 the 64-row items run on the large tile
+# (64 x 256, K through LDS stages): N = 272 leaves a last workgroup with one
+# 16-column tile, K = 640 five groups (not a multiple of the three stages)
 @pytest.mark.parametrize("sizes,K,N", [([0, 1, 17, 0, 40, 3, 70, 5], 256, 64),
                                        ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48),
-                                       ([0, 65, 33, 0, 128, 7, 70], 384, 256)])
+                                       ([0, 65, 33, 0, 128, 7, 70], 384, 256),
+                                       ([0, 65, 33, 0, 128, 7, 70], 640, 272)])
 def test_w4a8_grouped_ragged(ops, sizes, K, N):
     announce(f"qgemm_w4a8_fp8_grouped sizes={sizes} K={K} N={N}")
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -98,14 +101,15 @@ def test_w4a8_grouped_ragged(ops, sizes, K, N):
             assert_close_rms(y[r0:r1], ref, what=f"w4a8 expert {e}")
 
 
+@pytest.mark.parametrize("j", [0, 1])
 @pytest.mark.parametrize("B", [1, 16, 64, 1024])
-def test_w4a8_grouped_qwen3_shapes(ops, B):
+def test_w4a8_grouped_qwen3_shapes(ops, B, j):
     E, k = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK
-    name, K, N = synth.QWEN3_MOE_SHAPES[0]
+    name, K, N = synth.QWEN3_MOE_SHAPES[j]
     announce(f"qgemm_w4a8_fp8_grouped qwen3 {name} B={B}")
     token, offsets = synth.moe_routing(B, E, k, seed=B)
     a = synth.activations(B, K, seed=11 + B)[token]
-    w = synth.normal_bf16_device((E, K, N), seed=77, std=synth.WEIGHT_STD, device="cuda")
+    w = synth.normal_bf16_device((E, K, N), seed=77 + j, std=synth.WEIGHT_STD, device="cuda")
     gw = ops.GroupedInt4Weight.from_bf16(w)
     qa_d, sa_d = ops.quantize_activations(dev_bf16(a))
     y = host_bits16(gw.w4a8(qa_d, sa_d, torch.from_numpy(offsets).cuda()))

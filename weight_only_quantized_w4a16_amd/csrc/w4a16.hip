@@ -481,7 +481,10 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_grouped_kernel(
 //     across the XCDs without cache maintenance); an agent-scope release fence
 //     would also write back the XCD's L2 in every wave.
 // ---------------------------------------------------------------------------
-constexpr int DK_NWAVE = 8;
+#ifndef QG_DK_NWAVE               // waves per decode workgroup
+#define QG_DK_NWAVE 8
+#endif
+constexpr int DK_NWAVE = QG_DK_NWAVE;
 
 template <int KW, int U, int D>
 __global__ __launch_bounds__(DK_NWAVE * 64) void w4a16_decode_kernel(
@@ -762,14 +765,20 @@ constexpr int LM_BM = 128;
 // BM = 128 rows (two 32-row blocks per wave) or 64 (one block per wave: half
 // the MFMA work per weight unpacked, for M <= 64 and grids too small to fill
 // the CUs with 128-row tiles).
-template <int NS, int NB, int BM = 128>
+template <int NS, int NB, int BM = 128, int WR = 2>
 __device__ __forceinline__ void large_m_tile(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
     int M, int Mp, int N, int K, int S, float* __restrict__ part, unsigned* __restrict__ cnt,
     int tiles, int split, int tile) {
-    constexpr int NTB = 8 * NB;                  // column tiles per workgroup (NB 32-column blocks per wave)
-    constexpr int MI = BM / 64;                  // 32-row blocks per wave
+    constexpr int NTB = 8 * NB;                  // column tiles per workgroup
+    // wave grid: WR = 2 rows x 4 columns of waves (BM/2 rows x 32·NB columns
+    // each), or WR = 1 row of 8 waves (BM rows x 32 columns each: every weight
+    // fragment a wave unpacks then feeds BM/32 MFMAs instead of BM/64)
+    static_assert(WR == 2 || (WR == 1 && NB == 2), "wave grid");
+    constexpr int WROWS = BM / WR;               // rows per wave
+    constexpr int MI = WROWS / 32;               // 32-row blocks per wave
+    constexpr int NBW = WR == 2 ? NB : 1;        // 32-column blocks per wave
     constexpr int ACP = BM / 32;                 // activation copies per thread per stage
     constexpr int NCOPY = ACP + NB;              // copies per thread per stage (wave 0: one more)
     static_assert(NS >= 2 && NS <= 3, "stages");
@@ -794,8 +803,8 @@ __device__ __forceinline__ void large_m_tile(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2;                    // 0..1: row half (BM / 2 rows)
-    const int wn = wave & 3;                     // 0..3: column quarter (32 * NB columns)
+    const int wm = WR == 2 ? wave >> 2 : 0;      // row block of the wave grid (WROWS rows)
+    const int wn = WR == 2 ? wave & 3 : wave;    // column block of the wave grid (32 * NBW columns)
     const int mb = (M + BM - 1) / BM;
     // slice `split` holds groups [split*G/S, (split+1)*G/S)
     (void)tiles;
@@ -854,11 +863,11 @@ __device__ __forceinline__ void large_m_tile(
         ++ld_g;
     };
 
-    f32x16 total[MI][NB];                        // [m-block][32-column block]
+    f32x16 total[MI][NBW];                       // [m-block][32-column block]
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb)
+        for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) total[mi][bb][i] = 0.f;
 
@@ -891,11 +900,11 @@ __device__ __forceinline__ void large_m_tile(
         // tile: slot (l%16) + 16h holds rows 32t + 8h + 0..7 (k-step 2t), slot
         // (l%16) + 16(2+h) rows 32t + 16 + 8h + 0..7 (k-step 2t+1), word t each
         const int h = lane >> 5;
-        u32x4 wlo[NB], whi[NB];
-        float scur[NB];
+        u32x4 wlo[NBW], whi[NBW];
+        float scur[NBW];
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            const int tl = wn * 2 * NB + 2 * bb + ((lane & 31) >> 4);
+        for (int bb = 0; bb < NBW; ++bb) {
+            const int tl = wn * 2 * NBW + 2 * bb + ((lane & 31) >> 4);
             wlo[bb] = S.w[tl * 64 + (lane & 15) + 16 * h];
             whi[bb] = S.w[tl * 64 + (lane & 15) + 16 * h + 32];
             scur[bb] = bf16_to_f32(S.s[tl * 16 + (lane & 15)]);
@@ -906,7 +915,7 @@ __device__ __forceinline__ void large_m_tile(
         f32x16 cinit[MI];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-            const float* cb = S.c + wm * (BM / 2) + mi * 32 + 4 * h;
+            const float* cb = S.c + wm * WROWS + mi * 32 + 4 * h;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 c4 = *reinterpret_cast<const f32x4*>(cb + 8 * q);
@@ -914,34 +923,34 @@ __device__ __forceinline__ void large_m_tile(
                 for (int e = 0; e < 4; ++e) cinit[mi][4 * q + e] = c4[e];
             }
         }
-        f32x16 acc[MI][NB];
+        f32x16 acc[MI][NBW];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {            // 16-k steps of the group
             // the next stage's copies go out one per k-step, between the MFMAs,
             // so a wave does not stall on the copy queue before its math
             if (j <= NCOPY) copy(Dst, gnext, j);
-            bf16x8 bfr[NB], af[MI];
+            bf16x8 bfr[NBW], af[MI];
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
+            for (int bb = 0; bb < NBW; ++bb) {
                 const u32x4 wv = (j & 1) ? whi[bb] : wlo[bb];
                 const int t = j >> 1;
                 bfr[bb] = unpack(t == 0 ? wv.x : t == 1 ? wv.y : t == 2 ? wv.z : wv.w);
             }
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const int r = wm * (BM / 2) + mi * 32 + (lane & 31);
+                const int r = wm * WROWS + mi * 32 + (lane & 31);
                 af[mi] = as_bf16x8(S.a[r * 16 + ((2 * j + h) ^ (r & 15))]);
             }
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int bb = 0; bb < NB; ++bb)
+                for (int bb = 0; bb < NBW; ++bb)
                     acc[mi][bb] = mfma_bf16_32x32x16(af[mi], bfr[bb], j == 0 ? cinit[mi] : acc[mi][bb]);
         }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb)
+            for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) total[mi][bb][i] = fmaf(scur[bb], acc[mi][bb][i], total[mi][bb][i]);
     };
@@ -955,15 +964,15 @@ __device__ __forceinline__ void large_m_tile(
 
     if (S == 1) {
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            const int nt = nt0 + wn * 2 * NB + 2 * bb + ((lane & 31) >> 4);
+        for (int bb = 0; bb < NBW; ++bb) {
+            const int nt = nt0 + wn * 2 * NBW + 2 * bb + ((lane & 31) >> 4);
             if (nt >= NT) continue;
             const int n = nt * 16 + (lane & 15);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int m = m0 + wm * (BM / 2) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    const int m = m0 + wm * WROWS + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                     if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(total[mi][bb][i]);
                 }
             }
@@ -977,15 +986,15 @@ __device__ __forceinline__ void large_m_tile(
     // (deterministic), stores bf16 and leaves the counter at zero
     __shared__ int last_flag;
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-        const int nt = nt0 + wn * 2 * NB + 2 * bb + ((lane & 31) >> 4);
+    for (int bb = 0; bb < NBW; ++bb) {
+        const int nt = nt0 + wn * 2 * NBW + 2 * bb + ((lane & 31) >> 4);
         if (nt >= NT) continue;
         const int n = nt * 16 + (lane & 15);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int m = m0 + wm * (BM / 2) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                const int m = m0 + wm * WROWS + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                 if (m < M)
                     __hip_atomic_store(part + ((size_t)split * M + m) * N + n, total[mi][bb][i],
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1035,7 +1044,7 @@ __device__ __forceinline__ void large_m_tile(
 }
 
 // grid = tiles x S K-slices
-template <int NS, int NB, int BM>
+template <int NS, int NB, int BM, int WR>
 __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
     const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
@@ -1043,7 +1052,7 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     const int tiles = gridDim.x / S;
     const int split = blockIdx.x / tiles;
     const int tile = xcd_tile(blockIdx.x - split * tiles, tiles);
-    large_m_tile<NS, NB, BM>(a, wq, sc, corr, y, M, Mp, N, K, S, part, cnt, tiles, split, tile);
+    large_m_tile<NS, NB, BM, WR>(a, wq, sc, corr, y, M, Mp, N, K, S, part, cnt, tiles, split, tile);
 }
 
 // Expert-grouped, many rows per expert: one work item (expert, up to BM rows)
@@ -1075,6 +1084,9 @@ static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple of this
 #ifndef QG_LM_NS                   // pipeline stages of the large-M kernel
 #define QG_LM_NS 3
+#endif
+#ifndef QG_LM_WR1                  // 1: 256-column tiles use the one-row wave grid
+#define QG_LM_WR1 0
 #endif
 
 
@@ -1113,16 +1125,34 @@ constexpr int LM_MAX_BM = 256;     // offset-term rows are padded to a multiple 
 #define QG_SM_CT4_MIN_TILES (1 << 30)
 #endif
 
-template <int MT, int CT>
-static void launch_small(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
-                         int M, int N, int K, hipStream_t s) {
+// groups per pipelined item of the small-M kernel: QG_SM_U for one 16-row
+// m-tile, except one group for short K (at most 32 groups) and at most 8 rows,
+// where each wave streams only a few groups and the shorter first item starts
+// the math sooner (measured: qkv / o at B = 1 6.2 / 4.7 -> 5.7 / 4.2 us, at
+// B = 8 -3 / -4 %; long-K down loses 1-2 % with it)
+static int small_u(int M, int MT, int K) {
+    if (MT != 1) return 1;
+    return (K / 128 <= 32 && M <= 8) ? 1 : QG_SM_U;
+}
+
+template <int MT, int CT, int U>
+static void launch_small_u(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
+                           int M, int N, int K, hipStream_t s) {
     constexpr int NWAVE = QG_SM_NWAVE;
-    constexpr int U = MT == 1 ? QG_SM_U : 1;
     // two items in flight need 2*U*(5*CT + 16*MT) VGPRs of buffers
     constexpr bool PIPE = MT <= 2 && CT <= 2;
     const int NT = N / 16;
     hipLaunchKernelGGL((w4a16_small_m_kernel<MT, CT, NWAVE, U, PIPE>), dim3(NT / CT), dim3(NWAVE * 64),
                        0, s, a, wq, sc, y, M, N, K);
+}
+
+template <int MT, int CT>
+static void launch_small(const uint16_t* a, const uint32_t* wq, const uint16_t* sc, uint16_t* y,
+                         int M, int N, int K, hipStream_t s) {
+    if (MT == 1 && small_u(M, MT, K) == QG_SM_U)
+        launch_small_u<MT, CT, MT == 1 ? QG_SM_U : 1>(a, wq, sc, y, M, N, K, s);
+    else
+        launch_small_u<MT, CT, 1>(a, wq, sc, y, M, N, K, s);
 }
 
 // column tiles per workgroup of the small-M kernel: more tiles share each
@@ -1293,8 +1323,8 @@ void* noalloc_scratch() {
 #ifndef QG_DK_WIDE_PER_CU         // workgroup strips per CU, wide outputs
 #define QG_DK_WIDE_PER_CU 2
 #endif
-#ifndef QG_DK_WIDE_D              // ring depth, wide outputs
-#define QG_DK_WIDE_D 4
+#ifndef QG_DK_WIDE_D              // ring depth, wide outputs (measured: 3 beats 4 by 0-5 %, 70B most)
+#define QG_DK_WIDE_D 3
 #endif
 #ifndef QG_DK_NARROW_D            // ring depth, narrow outputs
 #define QG_DK_NARROW_D 4
@@ -1547,7 +1577,7 @@ static int large_m_nb(int M, int N, int bm) {
 // Large-M plan: tile width, K split and workspace layout (counters | corr |
 // slots), a function of the shape and the device's CU count only.
 struct LargePlan {
-    int bm, nb, S, tiles, Mp;
+    int bm, nb, wr, S, tiles, Mp;
     size_t corr_off, part_off, cnt_off, bytes;
 };
 
@@ -1573,6 +1603,9 @@ static LargePlan large_plan(int M, int N, int K) {
     }
     p.tiles = ((N + 128 * p.nb - 1) / (128 * p.nb)) * ((M + p.bm - 1) / p.bm);
     p.Mp = round_up(M, LM_MAX_BM);
+    // 256-column tiles: one row of 8 waves, each unpacking its weight
+    // fragments once for all BM rows
+    p.wr = (p.nb == 2 && QG_LM_WR1) ? 1 : 2;
     p.S = 1;
     // split long K until the grid fills the CUs, keeping at least
     // QG_LM_SPLIT_MIN_GPS groups per slice.  Short K (32 groups) only when the
@@ -1619,22 +1652,26 @@ static void launch_large(const uint16_t* a, const uint32_t* wq, const uint16_t* 
     float* part = p.S > 1 ? reinterpret_cast<float*>(w + p.part_off) : nullptr;
     unsigned* cnt = p.S > 1 ? reinterpret_cast<unsigned*>(w + p.cnt_off) : nullptr;
     const dim3 grid((unsigned)(p.tiles * p.S));
-    auto go = [&](auto nb, auto bm) {
-        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, decltype(nb)::value, decltype(bm)::value>), grid,
-                           dim3(512), 0, s, a, wq, sc, corr, y, M, p.Mp, N, K, p.S, part, cnt);
+    auto go = [&](auto nb, auto bm, auto wr) {
+        hipLaunchKernelGGL((w4a16_large_m_kernel<QG_LM_NS, decltype(nb)::value, decltype(bm)::value,
+                                                 decltype(wr)::value>),
+                           grid, dim3(512), 0, s, a, wq, sc, corr, y, M, p.Mp, N, K, p.S, part, cnt);
     };
-    if (p.bm == 64) {
-        if (p.nb == 1) go(ic<1>{}, ic<64>{});
-        else go(ic<2>{}, ic<64>{});
+    if (p.nb == 1) {
+        if (p.bm == 64) go(ic<1>{}, ic<64>{}, ic<2>{});
+        else go(ic<1>{}, ic<LM_BM>{}, ic<2>{});
+    } else if (p.wr == 1) {
+        if (p.bm == 64) go(ic<2>{}, ic<64>{}, ic<1>{});
+        else go(ic<2>{}, ic<LM_BM>{}, ic<1>{});
     } else {
-        if (p.nb == 1) go(ic<1>{}, ic<LM_BM>{});
-        else go(ic<2>{}, ic<LM_BM>{});
+        if (p.bm == 64) go(ic<2>{}, ic<64>{}, ic<2>{});
+        else go(ic<2>{}, ic<LM_BM>{}, ic<2>{});
     }
 }
 
 // The kernel and its compile-time configuration for a shape on the current
 // device, in a per-thread buffer: "w4a16_decode_kernel<KW, U, D> S=s",
-// "w4a16_small_m_kernel<MT, CT>" or "w4a16_large_m_kernel<NS, NB, BM> S=s".
+// "w4a16_small_m_kernel<MT, CT>" or "w4a16_large_m_kernel<NS, NB, BM, WR> S=s".
 const char* w4a16_kernel_for(int M, int N, int K) {
     static thread_local char buf[96];
     if (M == 0) return "none";
@@ -1648,7 +1685,8 @@ const char* w4a16_kernel_for(int M, int N, int K) {
                  small_ct(N / 16));
     } else {
         const LargePlan p = large_plan(M, N, K);
-        snprintf(buf, sizeof buf, "w4a16_large_m_kernel<%d, %d, %d> S=%d", QG_LM_NS, p.nb, p.bm, p.S);
+        snprintf(buf, sizeof buf, "w4a16_large_m_kernel<%d, %d, %d, %d> S=%d", QG_LM_NS, p.nb, p.bm, p.wr,
+                 p.S);
     }
     return buf;
 }

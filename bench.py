@@ -61,7 +61,11 @@ MSE_FP32_OPS_PER_POINT = 14.05
 MSE_FP64_OPS_PER_POINT = 5.58
 MSE_GRID = 100
 DOMINANT_SRC = os.path.join(ROOT, "weight_only_quantized_w4a16_amd", "csrc", "w4a16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_decode_kernel_llama3_8b_decode_B16_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_file(B):
+    return os.path.join(PROFILES, f"w4a16_decode_kernel_llama3_8b_decode_B{B}_traffic.txt")
 
 
 def w4a16_bytes(M, K, N):
@@ -94,13 +98,15 @@ def parse():
                    help="run only a plain 1 GiB device copy (counter calibration) and exit")
     p.add_argument("--summarize-stats", metavar="CSV",
                    help="print a text summary of a rocprofv3 *_kernel_stats.csv and exit")
-    p.add_argument("--summarize-traffic", nargs=4,
-                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                   help="derive HBM bytes per dominant-kernel launch from four rocprofv3 --pmc "
-                        "runs and write the traffic summary under profiles/, then exit")
     p.add_argument("--summarize-mfma", metavar="DIR",
                    help="print the MFMA busy share per kernel from a rocprofv3 --pmc run of "
                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE and exit")
+    p.add_argument("--profile-step", action="store_true",
+                   help="run --steps eager decode steps at --batch (no graphs, no timing) for counter runs")
+    p.add_argument("--summarize-counters", nargs=5,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "VALU_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="per-GEMM HBM traffic and VALU lane-ops per weight of a --profile-step run at "
+                        "--batch; writes the dominant kernel's traffic summary under profiles/, then exits")
     p.add_argument("--command", default="", help="command line recorded in summaries")
     return p.parse_args()
 
@@ -232,13 +238,14 @@ def dominant_rule(ops, M, K, N):
     return ops.w4a16_kernel_for(M, N, K).startswith(DOMINANT_KERNEL + "<")
 
 
-def read_traffic(kernel_sha):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(kernel_sha, B):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary at this batch, if it was taken on the current kernel source; else None."""
+    path = traffic_file(B)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -319,47 +326,100 @@ def _pmc_rows(d):
     return rows
 
 
-def summarize_traffic(dirs, command):
-    """KiB per dispatch of FETCH_SIZE / WRITE_SIZE for the dominant kernel, scaled
-    by what the same counters read for the calibration copy."""
-    fetch_dir, write_dir, cf_dir, cw_dir = dirs
+def _gemm_dispatches(d, counter):
+    """(kernel name, value) of every GEMM dispatch carrying `counter`, in dispatch order."""
+    rows = [r for r in _pmc_rows(d) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    out = []
+    for r in rows:
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        if any(k in name for k in ("w4a16_decode_kernel", "w4a16_small_m_kernel", "w4a16_large_m_kernel")):
+            out.append((name, float(r["Counter_Value"])))
+    return out
 
-    def per_dispatch(d, counter, match):
-        vals = [float(r["Counter_Value"]) for r in _pmc_rows(d)
-                if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
-        return sum(vals) / len(vals) if vals else None, len(vals)
 
-    is_dom = lambda n: DOMINANT_KERNEL in n
-    is_copy = lambda n: "copy" in n.lower() and "qg::" not in n
-    f_kib, nf = per_dispatch(fetch_dir, "FETCH_SIZE", is_dom)
-    w_kib, nw = per_dispatch(write_dir, "WRITE_SIZE", is_dom)
-    cf_kib, ncf = per_dispatch(cf_dir, "FETCH_SIZE", is_copy)
-    cw_kib, ncw = per_dispatch(cw_dir, "WRITE_SIZE", is_copy)
+def _copy_kib(d, counter):
+    vals = [float(r["Counter_Value"]) for r in _pmc_rows(d)
+            if r["Counter_Name"] == counter and "copy" in r["Kernel_Name"].lower() and "qg::" not in r["Kernel_Name"]]
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_counters(dirs, B, command):
+    """Per-GEMM HBM traffic (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    counter reads for a 1 GiB device copy) and VALU lane-ops per streamed weight
+    (SQ_INSTS_VALU x 64 / K N) of a --profile-step run: its GEMM dispatches come
+    in the step's order, so dispatch i is GEMM i mod 129 of the stack."""
+    from weight_only_quantized_w4a16_amd import synth
+    fetch_dir, write_dir, valu_dir, cf_dir, cw_dir = dirs
+    shapes = synth.stack_shapes("8b")
+    n = len(shapes)
+    fetch = _gemm_dispatches(fetch_dir, "FETCH_SIZE")
+    write = _gemm_dispatches(write_dir, "WRITE_SIZE")
+    valu = _gemm_dispatches(valu_dir, "SQ_INSTS_VALU")
+    mfma = _gemm_dispatches(valu_dir, "SQ_INSTS_MFMA")
+    cf_kib, ncf = _copy_kib(cf_dir, "FETCH_SIZE")
+    cw_kib, ncw = _copy_kib(cw_dir, "WRITE_SIZE")
     f_scale = (COPY_BYTES / 1024) / cf_kib
     w_scale = (COPY_BYTES / 1024) / cw_kib
-    hbm = f_kib * 1024 * f_scale + w_kib * 1024 * w_scale
+    for lst in (fetch, write, valu, mfma):
+        assert len(lst) % n == 0 and len(lst) > 0, f"{len(lst)} GEMM dispatches is not a whole number of steps"
+    groups = {}                                  # (layer-shape name, kernel) -> accumulators
+    for i, (name, K, N) in enumerate(shapes):
+        base = name.split(".")[-1]
+        kern = fetch[i][0]
+        key = (base, kern)
+        g = groups.setdefault(key, {"K": K, "N": N, "n": 0, "f": 0.0, "w": 0.0, "v": 0.0, "m": 0.0})
+        steps = len(fetch) // n
+        for st in range(steps):
+            j = st * n + i
+            assert fetch[j][0] == kern and write[j][0] == kern and valu[j][0] == kern
+            g["f"] += fetch[j][1] * 1024 * f_scale
+            g["w"] += write[j][1] * 1024 * w_scale
+            g["v"] += valu[j][1]
+            g["m"] += mfma[j][1]
+            g["n"] += 1
     sha = hashlib.sha256(open(DOMINANT_SRC, "rb").read()).hexdigest()
-    lines = [
-        f"# HBM traffic of {DOMINANT_KERNEL}, Llama-3-8B W4A16 decode step, B=16",
-        f"# command: {command}",
-        "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) averaged over the kernel's",
-        "# dispatches, each scaled by copy_bytes / counter of a 1 GiB device copy.",
-        f"kernel: {DOMINANT_KERNEL}",
-        f"dispatches_fetch: {nf}",
-        f"dispatches_write: {nw}",
-        f"fetch_kib_per_dispatch_raw: {f_kib:.1f}",
-        f"write_kib_per_dispatch_raw: {w_kib:.1f}",
-        f"copy_fetch_kib_raw: {cf_kib:.1f}  (dispatches {ncf})",
-        f"copy_write_kib_raw: {cw_kib:.1f}  (dispatches {ncw})",
-        f"fetch_scale: {f_scale:.4f}",
-        f"write_scale: {w_scale:.4f}",
-        f"hbm_bytes_per_launch: {hbm:.0f}",
-        f"kernel_source_sha256: {sha}",
-    ]
-    out = TRAFFIC_FILE
-    with open(out, "w") as fh:
+    lines = [f"# HBM traffic and VALU work per W4A16 GEMM, Llama-3-8B decode step, B={B}",
+             f"# command: {command}",
+             "# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by copy bytes / counter of a 1 GiB device",
+             "# copy; c = SQ_INSTS_VALU x 64 lanes / weights of the GEMM (VALU lane-ops per weight, budget",
+             "# D*b/beta = 2.53 at which vector work takes as long as the weight stream).",
+             f"copy_fetch_kib_raw: {cf_kib:.1f}  (dispatches {ncf})   fetch_scale: {f_scale:.4f}",
+             f"copy_write_kib_raw: {cw_kib:.1f}  (dispatches {ncw})   write_scale: {w_scale:.4f}",
+             f"{'gemm':8s} {'kernel':44s} {'disp':>5s} {'alg_MB':>8s} {'fetch_MB':>9s} {'write_MB':>9s} "
+             f"{'hbm/alg':>8s} {'c':>6s} {'mfma':>8s}"]
+    dom_bytes = dom_hbm = 0.0
+    dom_n = 0
+    for (base, kern), g in groups.items():
+        K, N = g["K"], g["N"]
+        alg = w4a16_bytes(B, K, N)
+        f, w, v, m = (g[k] / g["n"] for k in ("f", "w", "v", "m"))
+        lines.append(f"{base:8s} {kern[:44]:44s} {g['n']:5d} {alg / 1e6:8.2f} {f / 1e6:9.2f} {w / 1e6:9.3f} "
+                     f"{(f + w) / alg:8.3f} {v * 64 / (K * N):6.3f} {m:8.0f}")
+        if DOMINANT_KERNEL in kern:
+            dom_bytes += alg * g["n"]
+            dom_hbm += (f + w) * g["n"]
+            dom_n += g["n"]
+    if dom_n:
+        lines += [f"kernel: {DOMINANT_KERNEL}",
+                  f"dominant_dispatches: {dom_n}",
+                  f"algorithmic_bytes_per_launch: {dom_bytes / dom_n:.0f}",
+                  f"hbm_bytes_per_launch: {dom_hbm / dom_n:.0f}",
+                  f"hbm_over_algorithmic: {dom_hbm / dom_bytes:.4f}"]
+    lines.append(f"kernel_source_sha256: {sha}")
+    with open(traffic_file(B), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def run_profile_step(args, torch, ops, synth):
+    """--steps eager decode steps at --batch, nothing else on the GPU (counter runs)."""
+    stack = Stack(ops, synth, torch, "8b", [args.batch])
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        stack.step(args.batch)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_step": args.batch, "steps": args.steps, "gemms_per_step": len(stack.layers)}))
 
 
 def summarize_mfma(dirname, command):
@@ -419,6 +479,15 @@ def summarize_stats(csv_path, command):
         print(f"{name:70s} {int(r['Calls']):7d} {float(r['AverageNs'])/1e3:9.2f} "
               f"{float(r['MinNs'])/1e3:9.2f} {float(r['MaxNs'])/1e3:9.2f} "
               f"{float(r['TotalDurationNs'])/1e6:9.2f} {float(r['Percentage']):6.2f}")
+    # a large-M GEMM call is two launches (offset-term pre-pass + GEMM kernel):
+    # their summed time per call, the figure bench.py's large-batch roofline times
+    pre = [r for r in rows if "w4a16_group_rowsum_kernel" in r["Name"]]
+    lm = [r for r in rows if "w4a16_large_m_kernel" in r["Name"]]
+    if pre and lm:
+        calls = sum(int(r["Calls"]) for r in pre)
+        ns = sum(float(r["TotalDurationNs"]) for r in pre + lm)
+        print(f"# large-M GEMM calls (pre-pass + w4a16_large_m_kernel): {calls} calls, "
+              f"{ns / calls / 1e3:.2f} us of kernel time per call")
 
 
 def main():
@@ -426,8 +495,8 @@ def main():
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.command)
         return
-    if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic, args.command)
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.batch, args.command)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, args.command)
@@ -447,6 +516,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.profile_step:
+        run_profile_step(args, torch, ops, synth)
         return
 
     if args.workload == "decode":
@@ -506,7 +578,7 @@ def run_decode(args, torch, ops, synth):
     dom_avg_us = dom_ms * 1e3 / launches
     achieved = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9
     sha = hashlib.sha256(open(DOMINANT_SRC, "rb").read()).hexdigest()
-    traffic = read_traffic(sha)
+    traffic = read_traffic(sha, B)
 
     out = {
         "metric": "Llama-3-8B W4A16 decode-step ms & HBM TB/s vs batch; MFMA util at B>=512",

@@ -772,7 +772,7 @@ def large_batch_part(args, torch, ops, synth, batches):
         if r["w4a16_ms"] < min(r["bf16_kn_ms"], r["bf16_nk_ms"]):
             break
         cross = int(b)
-    B = LARGE_ROOFLINE_B
+    B = LARGE_ROOFLINE_B if str(LARGE_ROOFLINE_B) in res else max(batches)
     fl = stack.flops(B)
     ms4 = res[str(B)]["w4a16_ms"]
     launches = len(stack.layers)

@@ -152,17 +152,26 @@ class Stack:
             # allocate the largest workspace up front
             for b in batches:
                 lin.workspace(b)
+                if fp8 or int8:
+                    lin.workspace(b, dynamic=True)
             self.layers.append(rec)
         torch.cuda.synchronize()
 
-    def step(self, B, only=None):
+    def step(self, B, only=None, two_call=False):
+        """One pass over the stack at batch B.  8-bit: the per-token activation
+        quantization inside each GEMM call (qgemm_w8a8_*_dynamic), or with
+        two_call the separate quantization kernel before each GEMM."""
         ops = self.ops
         for r in self.layers:
             if only is not None and not only(r):
                 continue
             a = r["a"][:B]
             y = r["y"][:B]
-            if self.int8:
+            if (self.int8 or self.fp8) and not two_call:
+                ws, nb = r["lin"].workspace(B, dynamic=True)
+                dyn = ops.qgemm_w8a8_int8_dynamic if self.int8 else ops.qgemm_w8a8_fp8_dynamic
+                dyn(a, r["w"].codes, r["w"].scales, y, B, r["N"], r["K"], ws, nb)
+            elif self.int8:
                 ops.quant_act_per_token_int8(a, B, r["K"], r["qa"][:B], r["sa"][:B])
                 ws, nb = r["lin"].workspace(B)
                 ops.qgemm_w8a8_int8(r["qa"][:B], r["sa"][:B], r["w"].codes, r["w"].scales, y,
@@ -836,9 +845,16 @@ def run_fp8(args, torch, ops, synth, int8=False):
         g = graph_of(torch, lambda: stack.step(B))
         ms = time_graph(torch, g, args.steps, args.warmup)
         del g
+        g = graph_of(torch, lambda: stack.step(B, two_call=True))
+        ms_two = time_graph(torch, g, args.steps, args.warmup)
+        del g
         res[str(B)] = {"ms_per_step": round(ms, 4),
                        "TB_s": round(stack.bytes(B) / (ms * 1e-3) / 1e12, 3),
-                       f"{fmt}_mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (peak * 1e12), 4)}
+                       f"{fmt}_mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (peak * 1e12), 4),
+                       "two_call_ms_per_step": round(ms_two, 4),
+                       "gemms_quantizing_inside": sum(
+                           1 for r in stack.layers
+                           if ops.w8a8_dynamic_kernel_for(B, r["N"], r["K"]).startswith("w8a8_small_m_dyn"))}
         print(f"[bench] {fmt} B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
     FMT = fmt.upper()
     out = {"metric": f"Llama-3-8B W8A8-{FMT} decode-step ms vs batch", "value": res["16"]["TB_s"],
@@ -847,7 +863,9 @@ def run_fp8(args, torch, ops, synth, int8=False):
            "vs_baseline": None,
            "dtype": ("int8 x int8 -> int32 acc (int8 MFMA)" if int8 else "e4m3 x e4m3 -> fp32 acc (fp8 MFMA)"),
            "data": "synthetic",
-           "config": {"workload": f"Llama-3-8B W8A8-{FMT} stack incl. per-token activation quantization",
+           "config": {"workload": f"Llama-3-8B W8A8-{FMT} stack incl. per-token activation quantization "
+                                  f"(inside the GEMM call, qgemm_w8a8_{fmt}_dynamic; two_call: the separate "
+                                  f"quantization kernel first)",
                       "batch": 16}, "by_batch": res}
     print(json.dumps(out), flush=True)
 

@@ -363,6 +363,45 @@ qg_status qgemm_w8a8_int8(const int8_t *a_i8, const float *a_scale,
                           void *workspace, size_t workspace_bytes,
                           qg_stream stream);
 
+/*
+ * qgemm_w8a8_fp8_dynamic / qgemm_w8a8_int8_dynamic -- the W8A8 GEMM with the
+ * dynamic per-token activation quantization inside the call: bf16 activations
+ * in, y[m, n] = bf16(s_a[m] * s_w[n] * sum_k qa[m,k] qw[k,n]) out, where qa and
+ * s_a are exactly what quant_act_per_token (_int8) would produce for a.
+ * [P2 3.4 "W8A8-FP" and "W8A8-INT": activation scales computed on the fly per
+ *  token; P1 deployment B.]
+ *
+ *   a_bf16            in  [M, K] activations.
+ *   w_e4m3 / w_i8,    in  from quant_weight_fp8_per_channel /
+ *   w_scale               quant_weight_int8_per_channel.
+ *   y_bf16            out [M, N].
+ *   workspace         qg_w8a8_dynamic_workspace_bytes(M, N, K) bytes (NULL
+ *                     when that is 0), 16-byte aligned, zero-filled before its
+ *                     first use: the GEMM's workspace (counters first, the
+ *                     rules of qgemm_w8a8_fp8) followed by room for the codes
+ *                     and scales.  Calls sharing it must not overlap in time.
+ *
+ * Results equal quant_act_per_token (_int8) followed by qgemm_w8a8_fp8
+ * (_int8) bit for bit.  For a few rows (up to four at K = 4096, one at
+ * K = 14336; qg_w8a8_dynamic_kernel_for names the choice) each workgroup of
+ * the small-M GEMM quantizes the rows itself, into LDS, and no codes reach
+ * memory: one launch instead of two; otherwise the codes and scales are
+ * written to the workspace by the quantization kernel and read by the GEMM.
+ * Errors as qgemm_w8a8_fp8 / qgemm_w8a8_int8.
+ */
+size_t qg_w8a8_dynamic_workspace_bytes(int64_t M, int64_t N, int64_t K);
+const char *qg_w8a8_dynamic_kernel_for(int64_t M, int64_t N, int64_t K);
+qg_status qgemm_w8a8_fp8_dynamic(const uint16_t *a_bf16, const uint8_t *w_e4m3,
+                                 const float *w_scale, uint16_t *y_bf16,
+                                 int M, int N, int K,
+                                 void *workspace, size_t workspace_bytes,
+                                 qg_stream stream);
+qg_status qgemm_w8a8_int8_dynamic(const uint16_t *a_bf16, const int8_t *w_i8,
+                                  const float *w_scale, uint16_t *y_bf16,
+                                  int M, int N, int K,
+                                  void *workspace, size_t workspace_bytes,
+                                  qg_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -110,6 +110,22 @@ int main() {
     EXPECT_STATUS(qgemm_w8a8_int8(i8, f32, i8, f32, y16, 4, 32, 131072 + 128, nullptr, 0, nullptr),
                   QG_ERR_SHAPE);
 
+    // W8A8 with the activation quantization inside the call (bf16 activations)
+    EXPECT_LAUNCH(qgemm_w8a8_fp8_dynamic(a16, u8, f32, y16, 4, 32, 256, nullptr, 0, nullptr));
+    EXPECT_LAUNCH(qgemm_w8a8_int8_dynamic(a16, i8, f32, y16, 4, 32, 256, nullptr, 0, nullptr));
+    const size_t dneed = qg_w8a8_dynamic_workspace_bytes(40, 32, 256);
+    EXPECT(dneed >= (size_t)40 * 256);
+    EXPECT_LAUNCH(qgemm_w8a8_fp8_dynamic(a16, u8, f32, y16, 40, 32, 256, ws, dneed, nullptr));
+    EXPECT_STATUS(qgemm_w8a8_fp8_dynamic(a16, u8, f32, y16, 40, 32, 256, ws, dneed - 1, nullptr),
+                  QG_ERR_WORKSPACE);
+    EXPECT_STATUS(qgemm_w8a8_fp8_dynamic(a16, u8, f32, y16, 40, 32, 256, nullptr, 0, nullptr), QG_ERR_NULL);
+    EXPECT_STATUS(qgemm_w8a8_fp8_dynamic(nullptr, u8, f32, y16, 4, 32, 256, nullptr, 0, nullptr), QG_ERR_NULL);
+    EXPECT_STATUS(qgemm_w8a8_fp8_dynamic(a16 + 1, u8, f32, y16, 4, 32, 256, nullptr, 0, nullptr), QG_ERR_ALIGN);
+    EXPECT_STATUS(qgemm_w8a8_fp8_dynamic(a16, u8, f32, y16, 4, 30, 256, nullptr, 0, nullptr), QG_ERR_SHAPE);
+    EXPECT_STATUS(qgemm_w8a8_fp8_dynamic(a16, u8, f32, y16, 0, 32, 256, nullptr, 0, nullptr), QG_OK);
+    EXPECT_STATUS(qgemm_w8a8_int8_dynamic(a16, i8, f32, y16, 4, 32, 131072 + 128, nullptr, 0, nullptr),
+                  QG_ERR_SHAPE);
+
     // strings
     EXPECT(qg_status_string(QG_OK) != nullptr && qg_status_string(1234) != nullptr);
     EXPECT(qg_version() != nullptr);

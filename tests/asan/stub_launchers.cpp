@@ -43,5 +43,14 @@ size_t w8a8_workspace_bytes(int M, int, int) { return M > 64 ? 2048 : 0; }
 const char* w8a8_kernel_for(int, int, int) { return "stub"; }
 void launch_qgemm_w8a8_fp8(const uint8_t*, const float*, const uint8_t*, const float*, uint16_t*, int, int,
                            int, void*, hipStream_t) { ++g_launches; }
+// bf16-input W8A8: fused (no workspace) up to 16 rows, else codes in the workspace
+size_t w8a8_dyn_workspace_bytes(int M, int N, int K) {
+    return M <= 16 ? 0 : w8a8_workspace_bytes(M, N, K) + (size_t)M * K + (size_t)M * 4;
+}
+const char* w8a8_dyn_kernel_for(int, int, int) { return "stub"; }
+void launch_qgemm_w8a8_fp8_dyn(const uint16_t*, const uint8_t*, const float*, uint16_t*, int, int, int, void*,
+                               hipStream_t) { ++g_launches; }
+void launch_qgemm_w8a8_i8_dyn(const uint16_t*, const int8_t*, const float*, uint16_t*, int, int, int, void*,
+                              hipStream_t) { ++g_launches; }
 
 }  // namespace qg

@@ -144,6 +144,34 @@ def test_w4a16_validation(lib):
     assert _gemm(raw, 256, 4096, 4096, ws=FAKE + 4, wsb=need) == QG_ERR_ALIGN
 
 
+def test_w8a8_dynamic_validation(lib):
+    raw = ctypes.CDLL(LIB)
+    V, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    for name in ("qgemm_w8a8_fp8_dynamic", "qgemm_w8a8_int8_dynamic"):
+        f = getattr(raw, name)
+        f.restype = I
+        f.argtypes = [V, V, V, V, I, I, I, V, S, V]
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 4096, 4000, None, 0, None) == QG_ERR_SHAPE     # K % 128
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 4100, 4096, None, 0, None) == QG_ERR_SHAPE     # N % 16
+        assert f(None, FAKE, FAKE, FAKE, 0, 4096, 4096, None, 0, None) == QG_OK            # M == 0
+        assert f(None, FAKE, FAKE, FAKE, 4, 4096, 4096, None, 0, None) == QG_ERR_NULL
+        assert f(FAKE, FAKE, None, FAKE, 4, 4096, 4096, None, 0, None) == QG_ERR_NULL
+        assert f(FAKE + 2, FAKE, FAKE, FAKE, 4, 4096, 4096, None, 0, None) == QG_ERR_ALIGN
+        assert f(FAKE, FAKE + 8, FAKE, FAKE, 4, 4096, 4096, None, 0, None) == QG_ERR_ALIGN
+        # beyond 16 rows the codes go through the workspace
+        need = lib.w8a8_dynamic_workspace_bytes(40, 4096, 4096)
+        assert need >= 40 * 4096
+        assert f(FAKE, FAKE, FAKE, FAKE, 40, 4096, 4096, None, 0, None) == QG_ERR_NULL
+        assert f(FAKE, FAKE, FAKE, FAKE, 40, 4096, 4096, FAKE, need - 1, None) == QG_ERR_WORKSPACE
+        assert f(FAKE, FAKE, FAKE, FAKE, 40, 4096, 4096, FAKE + 4, need, None) == QG_ERR_ALIGN
+    int8 = raw.qgemm_w8a8_int8_dynamic
+    assert int8(FAKE, FAKE, FAKE, FAKE, 4, 4096, 131072 + 128, None, 0, None) == QG_ERR_SHAPE
+    # fused for a few rows: no workspace, one kernel
+    assert lib.w8a8_dynamic_workspace_bytes(1, 4096, 4096) == 0
+    assert lib.w8a8_dynamic_kernel_for(1, 4096, 4096).startswith("w8a8_small_m_dyn_kernel<")
+    assert lib.w8a8_dynamic_kernel_for(40, 4096, 4096).startswith("quant_act_per_token + ")
+
+
 def test_other_entry_points_validate(lib):
     raw = ctypes.CDLL(LIB)
     V, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t

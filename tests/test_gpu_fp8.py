@@ -89,10 +89,16 @@ def test_weight_quant_bit_exact(ops, K, N):
         assert np.array_equal(got[idx], qw_ref[k, n])
 
 
+def _two_step(ops, lin, a_dev):
+    """quant_act_per_token, then qgemm_w8a8_fp8 on its codes (the unfused path)."""
+    qa, sa = ops.quantize_activations(a_dev)
+    return lin(a_dev, qa=qa, sa=sa)
+
+
 def _fp8_gemm(ops, a_bits, w_bits):
     fw = ops.Fp8Weight.from_bf16(dev_bf16(w_bits))
     lin = ops.W8A8Fp8Linear(fw)
-    y = lin(dev_bf16(a_bits))
+    y = _two_step(ops, lin, dev_bf16(a_bits))
     torch.cuda.synchronize()
     return host_bits16(y)
 
@@ -174,7 +180,7 @@ def test_fp8_large_m_split_counters_reset(ops, M, K, N, tiles, S):
     ad = dev_bf16(a)
     first = None
     for _ in range(3):
-        y = host_bits16(lin(ad))
+        y = host_bits16(_two_step(ops, lin, ad))
         torch.cuda.synchronize()
         assert int(torch.count_nonzero(lin._ws[:65536])) == 0      # counters (first 4 * tiles bytes)
         assert_close_rms(y, ref, what=f"fp8 split M={M} K={K} N={N}")
@@ -213,7 +219,7 @@ def test_fp8_gemm_wide_shapes_sampled(ops, name, K, N, seed, B):
     announce(f"qgemm_w8a8_fp8 8B {name} B={B} ({kern})")
     wt, cols, (qw, sw) = _wide(ops, name, K, N, seed)
     a = synth.activations(B, K, seed=seed + B)
-    y = host_bits16(ops.W8A8Fp8Linear(wt)(dev_bf16(a)))
+    y = host_bits16(_two_step(ops, ops.W8A8Fp8Linear(wt), dev_bf16(a)))
     torch.cuda.synchronize()
     rows = np.unique(np.random.default_rng(B).integers(0, B, 32))
     qa, sa = f8.quant_act_per_token(a[rows])

@@ -64,9 +64,15 @@ def test_weight_quant_bit_exact(ops, K, N):
     assert np.array_equal(host_u8(iw.codes), f8.pack_native(qw_ref.view(np.uint8)))
 
 
+def _two_step(ops, lin, a_dev):
+    """quant_act_per_token_int8, then qgemm_w8a8_int8 on its codes (the unfused path)."""
+    qa, sa = ops.quantize_activations_int8(a_dev)
+    return lin(a_dev, qa=qa, sa=sa)
+
+
 def _int8_gemm(ops, a_bits, w_bits):
     lin = ops.W8A8Int8Linear(ops.Int8Weight.from_bf16(dev_bf16(w_bits)))
-    y = lin(dev_bf16(a_bits))
+    y = _two_step(ops, lin, dev_bf16(a_bits))
     torch.cuda.synchronize()
     return host_bits16(y)
 
@@ -129,7 +135,7 @@ def test_int8_large_m_split_counters_reset(ops, M, K, N, tiles, S):
     ad = dev_bf16(a)
     first = None
     for _ in range(3):
-        y = host_bits16(lin(ad))
+        y = host_bits16(_two_step(ops, lin, ad))
         torch.cuda.synchronize()
         assert int(torch.count_nonzero(lin._ws[:65536])) == 0      # counters (first 4 * tiles bytes)
         assert_close_rms(y, ref, what=f"int8 split M={M} K={K} N={N}")
@@ -168,7 +174,7 @@ def test_int8_gemm_wide_shapes_sampled(ops, name, K, N, seed, B):
     announce(f"qgemm_w8a8_int8 8B {name} B={B} ({kern})")
     wt, cols, (qw, sw) = _wide(ops, name, K, N, seed)
     a = synth.activations(B, K, seed=seed + B)
-    y = host_bits16(ops.W8A8Int8Linear(wt)(dev_bf16(a)))
+    y = host_bits16(_two_step(ops, ops.W8A8Int8Linear(wt), dev_bf16(a)))
     torch.cuda.synchronize()
     rows = np.unique(np.random.default_rng(B).integers(0, B, 32))
     qa, sa = i8.quant_act_per_token(a[rows])

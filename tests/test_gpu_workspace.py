@@ -126,6 +126,12 @@ def _eight_bit(ops, fmt):
     return (ops.W8A8Int8Linear, ops.Int8Weight, i8, ops.w8a8_int8_workspace_bytes)
 
 
+def _gemm_on_codes(ops, fmt, lin, a_dev):
+    """The GEMM entry point on codes from the separate quantization kernel."""
+    qa, sa = (ops.quantize_activations if fmt == "fp8" else ops.quantize_activations_int8)(a_dev)
+    return lin(a_dev, qa=qa, sa=sa)
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
 @pytest.mark.parametrize("M,K,N", EIGHT_BIT_SPLIT)
 def test_8bit_split_alternating_inputs_nan_slots(ops, fmt, M, K, N):
@@ -148,7 +154,7 @@ def test_8bit_split_alternating_inputs_nan_slots(ops, fmt, M, K, N):
     for rep in range(3):
         for i, a in enumerate(acts):
             _poison_slots(ws, nbytes)
-            y = lin(dev_bf16(a))
+            y = _gemm_on_codes(ops, fmt, lin, dev_bf16(a))
             torch.cuda.synchronize()
             assert bool(torch.isfinite(y).all()), f"{name}: non-finite output (a slot read before its write)"
             assert _counters_zero(ws)
@@ -173,7 +179,7 @@ def test_8bit_one_workspace_across_shapes(ops, fmt):
     a_all = synth.activations(512, K, seed=synth.activation_seed(0, 3))
     for M in (384, 512, 200, 384):
         a = a_all[:M]
-        y = lin(dev_bf16(a))
+        y = _gemm_on_codes(ops, fmt, lin, dev_bf16(a))
         torch.cuda.synchronize()
         assert lin._ws.numel() == need
         assert bool(torch.isfinite(y).all())

@@ -288,4 +288,50 @@ qg_status qgemm_w8a8_int8(const int8_t* a_i8, const float* a_scale, const int8_t
     return launched();
 }
 
+size_t qg_w8a8_dynamic_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!shape_ok(M, N, K)) return 0;
+    return qg::w8a8_dyn_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+const char* qg_w8a8_dynamic_kernel_for(int64_t M, int64_t N, int64_t K) {
+    if (!shape_ok(M, N, K)) return "";
+    return qg::w8a8_dyn_kernel_for((int)M, (int)N, (int)K);
+}
+
+// Shared checks of the two bf16-input W8A8 entry points.
+static qg_status dynamic_args_ok(const uint16_t* a, const void* w, const float* sw, const uint16_t* y, int M,
+                                 int N, int K, void* workspace, size_t workspace_bytes) {
+    if (!a || !w || !sw || !y) return QG_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(sw, 4) || !aligned(y, 16)) return QG_ERR_ALIGN;
+    const size_t need = qg::w8a8_dyn_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace) return QG_ERR_NULL;
+        if (workspace_bytes < need) return QG_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QG_ERR_ALIGN;
+    }
+    return QG_OK;
+}
+
+qg_status qgemm_w8a8_fp8_dynamic(const uint16_t* a_bf16, const uint8_t* w_e4m3, const float* w_scale,
+                                 uint16_t* y_bf16, int M, int N, int K, void* workspace,
+                                 size_t workspace_bytes, qg_stream stream) {
+    if (!shape_ok(M, N, K)) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    const qg_status st = dynamic_args_ok(a_bf16, w_e4m3, w_scale, y_bf16, M, N, K, workspace, workspace_bytes);
+    if (st != QG_OK) return st;
+    qg::launch_qgemm_w8a8_fp8_dyn(a_bf16, w_e4m3, w_scale, y_bf16, M, N, K, workspace, as_stream(stream));
+    return launched();
+}
+
+qg_status qgemm_w8a8_int8_dynamic(const uint16_t* a_bf16, const int8_t* w_i8, const float* w_scale,
+                                  uint16_t* y_bf16, int M, int N, int K, void* workspace,
+                                  size_t workspace_bytes, qg_stream stream) {
+    if (!shape_ok(M, N, K) || K > kMaxKInt8) return QG_ERR_SHAPE;
+    if (M == 0) return QG_OK;
+    const qg_status st = dynamic_args_ok(a_bf16, w_i8, w_scale, y_bf16, M, N, K, workspace, workspace_bytes);
+    if (st != QG_OK) return st;
+    qg::launch_qgemm_w8a8_i8_dyn(a_bf16, w_i8, w_scale, y_bf16, M, N, K, workspace, as_stream(stream));
+    return launched();
+}
+
 }  // extern "C"

@@ -278,16 +278,19 @@ void launch_quant_weight_i8(const uint16_t* w, int K, int N, int8_t* q, float* s
 // pieces of its A row (k = 16q .. +15 and 64 + 16q .. +15 for lane quarter q),
 // so each A load instruction reads 64 contiguous bytes per row.
 // ---------------------------------------------------------------------------
-template <class Fmt, int MT, int CT, int NWAVE, int U>
-__global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
-    const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
-    const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
+// The work of one workgroup: column tiles [nt0, nt0 + CT).  afrag(mt, kt, h)
+// returns the lane's 16-byte A piece h (k = 128 kt + 64 h + 16 kq .. +15) of
+// row 16 mt + col (zero for rows >= M); sa(m) is row m's activation scale.
+// PRE: wfirst already holds the wave's first U k-tiles of weights (requested
+// by the caller ahead of other work).
+template <class Fmt, int MT, int CT, int NWAVE, int U, bool PRE = false, class AFrag, class AScale>
+__device__ __forceinline__ void w8a8_small_m_tile(AFrag afrag, AScale sa, const uint8_t* __restrict__ wq,
+                                                  const float* __restrict__ sw, uint16_t* __restrict__ y,
+                                                  int M, int N, int K, int nt0,
+                                                  const u32x4 (*wfirst)[CT][2] = nullptr) {
     const int KT = K >> 7;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
-    const int col = lane & 15;
-    const int kq = lane >> 4;
-    const int nt0 = blockIdx.x * CT;
     const int k_begin = (KT * wave) / NWAVE;
     const int k_end = (KT * (wave + 1)) / NWAVE;
 
@@ -298,14 +301,6 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) total[ct][mt] = Fmt::zero();
 
-    const u32x4* arow[MT];
-    bool rowok[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + col;
-        rowok[mt] = m < M;
-        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)(rowok[mt] ? m : 0) * K) + kq;
-    }
     const u32x4* wtile = reinterpret_cast<const u32x4*>(wq);
 
     for (int k0 = k_begin; k0 < k_end; k0 += U) {
@@ -317,14 +312,19 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
             if (kt < k_end) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const size_t tile = (size_t)(nt0 + ct) * KT + kt;
-                    wv[u][ct][0] = wtile[tile * 128 + lane * 2];
-                    wv[u][ct][1] = wtile[tile * 128 + lane * 2 + 1];
+                    if (PRE && k0 == k_begin) {
+                        wv[u][ct][0] = wfirst[u][ct][0];
+                        wv[u][ct][1] = wfirst[u][ct][1];
+                    } else {
+                        const size_t tile = (size_t)(nt0 + ct) * KT + kt;
+                        wv[u][ct][0] = wtile[tile * 128 + lane * 2];
+                        wv[u][ct][1] = wtile[tile * 128 + lane * 2 + 1];
+                    }
                 }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    av[u][mt][0] = rowok[mt] ? arow[mt][kt * 8] : u32x4{0u, 0u, 0u, 0u};
-                    av[u][mt][1] = rowok[mt] ? arow[mt][kt * 8 + 4] : u32x4{0u, 0u, 0u, 0u};
+                    av[u][mt][0] = afrag(mt, kt, 0);
+                    av[u][mt][1] = afrag(mt, kt, 1);
                 }
             }
         }
@@ -361,8 +361,174 @@ __global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) sum += red[w][ct][mt][l][i];
         const int n = (nt0 + ct) * 16 + (l & 15);
-        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(Fmt::value(sum) * sa[m] * sw[n]);
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(Fmt::value(sum) * sa(m) * sw[n]);
     }
+}
+
+template <class Fmt, int MT, int CT, int NWAVE, int U>
+__global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ wq,
+    const float* __restrict__ sw, uint16_t* __restrict__ y, int M, int N, int K) {
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const u32x4* arow[MT];
+    bool rowok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + col;
+        rowok[mt] = m < M;
+        arow[mt] = reinterpret_cast<const u32x4*>(a + (size_t)(rowok[mt] ? m : 0) * K) + kq;
+    }
+    auto afrag = [&](int mt, int kt, int h) -> u32x4 {
+        return rowok[mt] ? arow[mt][kt * 8 + 4 * h] : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto ascale = [&](int m) { return sa[m]; };
+    w8a8_small_m_tile<Fmt, MT, CT, NWAVE, U>(afrag, ascale, wq, sw, y, M, N, K, blockIdx.x * CT);
+}
+
+// ---------------------------------------------------------------------------
+// Per-token quantization fused into the small-M GEMM (qgemm_w8a8_*_dynamic,
+// bf16 activations, M <= 16).  A row's scale needs the abs-max over all of K,
+// and a workgroup's waves together read all of K, so every workgroup
+// quantizes the whole [M, K] activation itself: the rows are read once into
+// registers (a wave's 64 consecutive 16-byte chunks lie in one row, as K is a
+// multiple of 512), each row's abs-max is reduced over the workgroup (LDS
+// atomic max on the bit pattern of non-negative floats), and the codes go to
+// LDS with a row stride of K + 16 bytes (the 16 rows one fragment read touches
+// then start on 16 distinct 4-bank offsets).  The GEMM body then reads its A
+// pieces from LDS.  Scales, codes, the waves' k-tiles, the MFMA order and the
+// reduction are those of quant_act_per_token + w8a8_small_m_kernel, so the
+// output is theirs bit for bit, without the separate launch and its round trip
+// through memory.
+//
+// Code quotients: with r = 1/s (IEEE), q0 = a r, e = fma(-q0, s, a) and
+// q = fma(e, r, q0) (one correction step of the reciprocal product, three
+// operations instead of a full division) can differ from the IEEE quotient
+// a / s in its last bit, but not in the code it rounds to, for every pair of
+// bf16 values |a| <= amax with s = amax / q_max >= 2^-100, in both formats (an
+// exhaustive check over all such pairs); rows with a smaller or non-finite
+// scale take the division.
+// ---------------------------------------------------------------------------
+constexpr int DYN_MAX_CPT = 4;           // 16-byte activation chunks per thread at most
+constexpr int DYN_MAX_M = 16;
+
+template <class Fmt>
+__device__ __forceinline__ float dyn_quotient(float x, float s, float r, bool fast) {
+    if (!fast) return x / s;
+    const float q0 = x * r;
+    const float e = fmaf(-q0, s, x);
+    return fmaf(e, r, q0);
+}
+
+// CPT: 16-byte activation chunks per thread (M * K / 8 <= CPT * 64 * NWAVE); the
+// registers that hold them are sized by it, so small rows keep the occupancy of
+// the unfused kernel.
+template <class Fmt, int CT, int NWAVE, int U, int CPT>
+__global__ __launch_bounds__(NWAVE * 64) void w8a8_small_m_dyn_kernel(
+    const uint16_t* __restrict__ a, const uint8_t* __restrict__ wq, const float* __restrict__ sw,
+    uint16_t* __restrict__ y, int M, int N, int K) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char codes[];   // [M][K + 16]
+    __shared__ unsigned amax_bits[DYN_MAX_M];
+    __shared__ float srow[DYN_MAX_M], rrow[DYN_MAX_M];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rowb = K + 16;
+    const int cpr = K >> 3;                      // 16-byte chunks per row (a multiple of 64)
+    const int nchunk = M * cpr;
+    const int nt0 = blockIdx.x * CT;
+
+    // the wave's first U k-tiles of weights go out before the activation work
+    const int KT = K >> 7;
+    const int k_begin = (KT * wave) / NWAVE;
+    const int k_end = (KT * (wave + 1)) / NWAVE;
+    u32x4 wfirst[U][CT][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int kt = k_begin + u;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const size_t tile = (size_t)(nt0 + ct) * KT + (kt < k_end ? kt : k_begin);
+            wfirst[u][ct][0] = reinterpret_cast<const u32x4*>(wq)[tile * 128 + lane * 2];
+            wfirst[u][ct][1] = reinterpret_cast<const u32x4*>(wq)[tile * 128 + lane * 2 + 1];
+        }
+    }
+
+    if (tid < DYN_MAX_M) amax_bits[tid] = 0u;
+    const u32x4* arows = reinterpret_cast<const u32x4*>(a);
+    u32x4 v[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = 64 * (wave + NWAVE * i) + lane;
+        v[i] = c < nchunk ? arows[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    // row and in-row chunk of the wave's block i (wave-uniform; blocks advance
+    // by NWAVE * 64 chunks, at most one row per step when a row has at least
+    // that many chunks, else by whole rows in a short loop)
+    int brow[CPT], bcol[CPT];
+    {
+        int m = 0, cc = 64 * wave;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            while (cc >= cpr) { cc -= cpr; ++m; }
+            brow[i] = m;
+            bcol[i] = cc;
+            cc += 64 * NWAVE;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        if (brow[i] >= M) break;
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mx = fmaxf(mx, fabsf(bf16_to_f32(w4[j] & 0xffffu)));
+            mx = fmaxf(mx, fabsf(bf16_to_f32(w4[j] >> 16)));
+        }
+        mx = wave_max(mx);
+        if (lane == 0) atomicMax(&amax_bits[brow[i]], __float_as_uint(mx));
+    }
+    __syncthreads();
+    if (tid < M) {
+        const float s = __uint_as_float(amax_bits[tid]) / Fmt::qmax;        // IEEE fp32 quotient
+        srow[tid] = s;
+        rrow[tid] = 1.0f / s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int m = brow[i];
+        if (m >= M) break;
+        const float s = srow[m];
+        const float r = rrow[m];
+        const bool fast = s >= 0x1p-100f && s < __builtin_inff();
+        uint2 o = make_uint2(0u, 0u);
+        if (s != 0.0f) {
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            uint32_t b[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = Fmt::encode2(dyn_quotient<Fmt>(bf16_to_f32(w4[j] & 0xffffu), s, r, fast),
+                                    dyn_quotient<Fmt>(bf16_to_f32(w4[j] >> 16), s, r, fast));
+            o.x = b[0] | (b[1] << 16);
+            o.y = b[2] | (b[3] << 16);
+        }
+        *reinterpret_cast<uint2*>(codes + (size_t)m * rowb + (size_t)(bcol[i] + lane) * 8) = o;
+    }
+    __syncthreads();
+
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const bool rowok = col < M;
+    const unsigned char* arow = codes + (size_t)(rowok ? col : 0) * rowb + kq * 16;
+    auto afrag = [&](int, int kt, int h) -> u32x4 {
+        return rowok ? *reinterpret_cast<const u32x4*>(arow + kt * 128 + 64 * h) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto ascale = [&](int m) { return srow[m]; };
+    w8a8_small_m_tile<Fmt, 1, CT, NWAVE, U, true>(afrag, ascale, wq, sw, y, M, N, K, nt0, wfirst);
 }
 
 // ---------------------------------------------------------------------------
@@ -765,6 +931,107 @@ static void launch_w8a8(const uint8_t* a, const float* sa, const uint8_t* w, con
                                    sa, w, sw, y, M, N, K, p.S, part, cnt);
         }
     }
+}
+
+// ---- bf16 activations in (per-token quantization inside the call) ----
+#ifndef QG_F8_DYN_BUDGET           // M * K * launch rounds up to which the GEMM quantizes the rows itself
+#define QG_F8_DYN_BUDGET 65536
+#endif
+
+static size_t dyn_lds(int M, int K) { return (size_t)M * (K + 16); }
+
+// 16-byte activation chunks per thread of the fused kernel (0: more than it holds)
+static int dyn_cpt(int M, int K) {
+    const long long per = ((long long)M * (K / 8) + 8 * 64 - 1) / (8 * 64);
+    static_assert(DYN_MAX_CPT == 4, "instantiated chunk counts");
+    return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 0;
+}
+
+// Fused when the rows fit the registers (at most DYN_MAX_CPT chunks per thread) and
+// the redundant quantization (every workgroup repeats it, a round of
+// workgroups after another) stays small next to the separate launch it saves.
+// Measured per GEMM on the 8B shapes, fp8 (unfused -> fused, us): one row
+// qkv 11.4 -> 8.3, o 9.7 -> 6.7, gate_up 26.5 -> 23.5, down 17.6 -> 16.2, LM
+// head 91.6 -> 87.0; two rows -1.7 .. -2.4 (head -1.7); three rows -0.2 ..
+// -1.7; four rows qkv / o (one round of workgroups) -0.4 / -1.1 but gate_up
+// (two rounds) +0.3 and the head (eight) +3.2.
+static bool w8a8_dyn_fused(int M, int N, int K) {
+    if (M < 1 || M > DYN_MAX_M || K % 512 != 0 || K < 1024) return false;
+    if (dyn_cpt(M, K) == 0) return false;
+    const int wgs = N / 16 / f8_small_ct(N / 16);
+    const int per_round = 2 * device_cu_count();     // two 8-wave workgroups per CU at <= 128 VGPRs
+    const long long rounds = (wgs + per_round - 1) / per_round;
+    if (M > 3 && rounds > 1) return false;
+    return (long long)M * K * rounds <= QG_F8_DYN_BUDGET;
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// unfused: the GEMM's own workspace first (counters at offset 0), then the codes and scales
+size_t w8a8_dyn_workspace_bytes(int M, int N, int K) {
+    if (M == 0 || w8a8_dyn_fused(M, N, K)) return 0;
+    return align256(w8a8_workspace_bytes(M, N, K)) + align256((size_t)M * K) + align256((size_t)M * 4);
+}
+
+const char* w8a8_dyn_kernel_for(int M, int N, int K) {
+    thread_local char buf[128];
+    if (M == 0) return "none";
+    if (w8a8_dyn_fused(M, N, K)) {
+        snprintf(buf, sizeof buf, "w8a8_small_m_dyn_kernel<%d>", f8_small_ct(N / 16));
+        return buf;
+    }
+    snprintf(buf, sizeof buf, "quant_act_per_token + %s", w8a8_kernel_for(M, N, K));
+    return buf;
+}
+
+template <class Fmt, int CT, int CPT>
+static void launch_dyn_cpt(const uint16_t* a, const uint8_t* w, const float* sw, uint16_t* y, int M, int N,
+                           int K, hipStream_t st) {
+    constexpr int NWAVE = 8;
+    constexpr int U = 4;                     // as the small-M launch for one m-tile
+    static std::atomic<uint64_t> lds_set{0};
+    allow_dynamic_lds(reinterpret_cast<const void*>(&w8a8_small_m_dyn_kernel<Fmt, CT, NWAVE, U, CPT>),
+                      CPT * 8 * 64 * 8 + 16 * DYN_MAX_M, lds_set);   // M * K <= CPT * 4096 codes
+    hipLaunchKernelGGL((w8a8_small_m_dyn_kernel<Fmt, CT, NWAVE, U, CPT>), dim3(N / 16 / CT),
+                       dim3(NWAVE * 64), dyn_lds(M, K), st, a, w, sw, y, M, N, K);
+}
+
+template <class Fmt, int CT>
+static void launch_dyn_ct(const uint16_t* a, const uint8_t* w, const float* sw, uint16_t* y, int M, int N,
+                          int K, hipStream_t st) {
+    switch (dyn_cpt(M, K)) {
+        case 1: launch_dyn_cpt<Fmt, CT, 1>(a, w, sw, y, M, N, K, st); break;
+        case 2: launch_dyn_cpt<Fmt, CT, 2>(a, w, sw, y, M, N, K, st); break;
+        default: launch_dyn_cpt<Fmt, CT, 4>(a, w, sw, y, M, N, K, st); break;
+    }
+}
+
+template <class Fmt>
+static void launch_w8a8_dyn(const uint16_t* a, const uint8_t* w, const float* sw, uint16_t* y, int M,
+                            int N, int K, void* ws, hipStream_t st) {
+    if (w8a8_dyn_fused(M, N, K)) {
+        if (f8_small_ct(N / 16) == 2)
+            launch_dyn_ct<Fmt, 2>(a, w, sw, y, M, N, K, st);
+        else
+            launch_dyn_ct<Fmt, 1>(a, w, sw, y, M, N, K, st);
+        return;
+    }
+    char* base = static_cast<char*>(ws);
+    const size_t q_off = align256(w8a8_workspace_bytes(M, N, K));
+    uint8_t* q = reinterpret_cast<uint8_t*>(base + q_off);
+    float* sa = reinterpret_cast<float*>(base + q_off + align256((size_t)M * K));
+    launch_quant_act<Fmt>(a, M, K, q, sa, st);
+    launch_w8a8<Fmt>(q, sa, w, sw, y, M, N, K, base, st);
+}
+
+void launch_qgemm_w8a8_fp8_dyn(const uint16_t* a, const uint8_t* w, const float* sw, uint16_t* y, int M,
+                               int N, int K, void* ws, hipStream_t st) {
+    launch_w8a8_dyn<FmtE4M3>(a, w, sw, y, M, N, K, ws, st);
+}
+
+void launch_qgemm_w8a8_i8_dyn(const uint16_t* a, const int8_t* w, const float* sw, uint16_t* y, int M,
+                              int N, int K, void* ws, hipStream_t st) {
+    launch_w8a8_dyn<FmtI8>(a, reinterpret_cast<const uint8_t*>(w), sw, y, M, N, K, ws, st);
 }
 
 void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,

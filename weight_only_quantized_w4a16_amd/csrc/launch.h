@@ -83,5 +83,13 @@ const char* w8a8_kernel_for(int M, int N, int K);
 void launch_qgemm_w8a8_fp8(const uint8_t* a, const float* sa, const uint8_t* w,
                            const float* sw, uint16_t* y, int M, int N, int K, void* ws,
                            hipStream_t st);
+// bf16 activations in: per-token quantization fused into the small-M GEMM, or
+// quant_act into the workspace followed by the GEMM (both formats)
+size_t w8a8_dyn_workspace_bytes(int M, int N, int K);
+const char* w8a8_dyn_kernel_for(int M, int N, int K);
+void launch_qgemm_w8a8_fp8_dyn(const uint16_t* a, const uint8_t* w, const float* sw, uint16_t* y,
+                               int M, int N, int K, void* ws, hipStream_t st);
+void launch_qgemm_w8a8_i8_dyn(const uint16_t* a, const int8_t* w, const float* sw, uint16_t* y,
+                              int M, int N, int K, void* ws, hipStream_t st);
 
 }  // namespace qg

@@ -53,6 +53,10 @@ _SIGS = {
     "quant_act_per_token_int8": (_I, [_P, _I, _I, _P, _P, _P]),
     "quant_weight_int8_per_channel": (_I, [_P, _I, _I, _P, _P, _P]),
     "qgemm_w8a8_int8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "qg_w8a8_dynamic_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "qg_w8a8_dynamic_kernel_for": (ctypes.c_char_p, [_I64, _I64, _I64]),
+    "qgemm_w8a8_fp8_dynamic": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "qgemm_w8a8_int8_dynamic": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -90,6 +94,14 @@ def w4a16_kernel_for(M, N, K):
 
 def w8a8_kernel_for(M, N, K):
     return _lib.qg_w8a8_kernel_for(M, N, K).decode()
+
+
+def w8a8_dynamic_kernel_for(M, N, K):
+    return _lib.qg_w8a8_dynamic_kernel_for(M, N, K).decode()
+
+
+def w8a8_dynamic_workspace_bytes(M, N, K):
+    return _lib.qg_w8a8_dynamic_workspace_bytes(M, N, K)
 
 
 def w4a16_workspace_bytes(M, N, K):
@@ -207,6 +219,20 @@ def qgemm_w8a8_int8(a_i8, a_scale, w_i8, w_scale, y_bf16, M, N, K, workspace=Non
                                                    _ptr(w_scale), _ptr(y_bf16), M, N, K,
                                                    _ptr(workspace), workspace_bytes,
                                                    _stream(stream)))
+
+
+def qgemm_w8a8_fp8_dynamic(a_bf16, w_e4m3, w_scale, y_bf16, M, N, K, workspace=None,
+                           workspace_bytes=0, stream=None):
+    _check("qgemm_w8a8_fp8_dynamic",
+           _lib.qgemm_w8a8_fp8_dynamic(_ptr(a_bf16), _ptr(w_e4m3), _ptr(w_scale), _ptr(y_bf16), M, N, K,
+                                       _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qgemm_w8a8_int8_dynamic(a_bf16, w_i8, w_scale, y_bf16, M, N, K, workspace=None,
+                            workspace_bytes=0, stream=None):
+    _check("qgemm_w8a8_int8_dynamic",
+           _lib.qgemm_w8a8_int8_dynamic(_ptr(a_bf16), _ptr(w_i8), _ptr(w_scale), _ptr(y_bf16), M, N, K,
+                                        _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 # ---- tensor-level helpers (allocate outputs with torch, then call the above) --
@@ -359,23 +385,27 @@ class W8A8Fp8Linear:
         self.w = weight
         self._ws = None
 
-    def workspace(self, M):
-        need = w8a8_workspace_bytes(M, self.w.N, self.w.K)
+    def workspace(self, M, dynamic=False):
+        need = (w8a8_dynamic_workspace_bytes if dynamic else w8a8_workspace_bytes)(M, self.w.N, self.w.K)
         if need and (self._ws is None or self._ws.numel() < need):
             # zero-filled once; every call resets the counters it uses
             self._ws = torch.zeros(need, dtype=torch.uint8, device=self.w.codes.device)
         return (self._ws, need) if need else (None, 0)
 
     def __call__(self, a, out=None, stream=None, qa=None, sa=None):
+        """Without qa / sa the activations are quantized inside the call
+        (qgemm_w8a8_fp8_dynamic); with them the GEMM runs on the given codes."""
         M, K = a.shape
         if K != self.w.K:
             raise ValueError(f"activation K={K} != weight K={self.w.K}")
-        if qa is None:
-            qa, sa = quantize_activations(a, stream)
         y = out if out is not None else torch.empty((M, self.w.N), dtype=torch.bfloat16,
                                                     device=a.device)
-        ws, need = self.workspace(M)
-        qgemm_w8a8_fp8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
+        ws, need = self.workspace(M, dynamic=qa is None)
+        if qa is None:
+            qgemm_w8a8_fp8_dynamic(_bf16(a), self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need,
+                                   stream)
+        else:
+            qgemm_w8a8_fp8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
         return y
 
 
@@ -426,20 +456,25 @@ class W8A8Int8Linear:
         self.w = weight
         self._ws = None
 
-    def workspace(self, M):
-        need = w8a8_int8_workspace_bytes(M, self.w.N, self.w.K)
+    def workspace(self, M, dynamic=False):
+        need = (w8a8_dynamic_workspace_bytes if dynamic else w8a8_int8_workspace_bytes)(
+            M, self.w.N, self.w.K)
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = torch.zeros(need, dtype=torch.uint8, device=self.w.codes.device)
         return (self._ws, need) if need else (None, 0)
 
     def __call__(self, a, out=None, stream=None, qa=None, sa=None):
+        """Without qa / sa the activations are quantized inside the call
+        (qgemm_w8a8_int8_dynamic); with them the GEMM runs on the given codes."""
         M, K = a.shape
         if K != self.w.K:
             raise ValueError(f"activation K={K} != weight K={self.w.K}")
-        if qa is None:
-            qa, sa = quantize_activations_int8(a, stream)
         y = out if out is not None else torch.empty((M, self.w.N), dtype=torch.bfloat16,
                                                     device=a.device)
-        ws, need = self.workspace(M)
-        qgemm_w8a8_int8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
+        ws, need = self.workspace(M, dynamic=qa is None)
+        if qa is None:
+            qgemm_w8a8_int8_dynamic(_bf16(a), self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need,
+                                    stream)
+        else:
+            qgemm_w8a8_int8(qa, sa, self.w.codes, self.w.scales, y, M, self.w.N, K, ws, need, stream)
         return y

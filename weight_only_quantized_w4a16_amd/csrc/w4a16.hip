@@ -923,12 +923,16 @@ __device__ __forceinline__ void large_m_tile(
                 for (int e = 0; e < 4; ++e) cinit[mi][4 * q + e] = c4[e];
             }
         }
+        // wave 0's scale / offset-term copy goes out before the MFMAs: issued
+        // between them, its wave-0 branch would split the k-steps' MFMA chain
+        // into two blocks that the scheduler cannot interleave across
+        copy(Dst, gnext, NCOPY);
         f32x16 acc[MI][NBW];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {            // 16-k steps of the group
             // the next stage's copies go out one per k-step, between the MFMAs,
             // so a wave does not stall on the copy queue before its math
-            if (j <= NCOPY) copy(Dst, gnext, j);
+            if (j < NCOPY) copy(Dst, gnext, j);
             bf16x8 bfr[NBW], af[MI];
 #pragma unroll
             for (int bb = 0; bb < NBW; ++bb) {

@@ -185,6 +185,25 @@ class Stack:
                 ws, nb = r["lin"].workspace(B)
                 ops.qgemm_w4a16(a, r["w"].packed, r["w"].scales, y, B, r["N"], r["K"], ws, nb)
 
+    def check_outputs(self, B, g, **step_args):
+        """Replays the timed step's graph once, then runs the same step eagerly:
+        every output must be finite and the two runs identical bit for bit (a
+        split-K slot read before its write, or any other race between the
+        step's launches, would show here).  Returns True when both hold."""
+        torch = self.torch
+        g.replay()
+        torch.cuda.synchronize()
+        first = [r["y"][:B].clone() for r in self.layers]
+        self.step(B, **step_args)
+        torch.cuda.synchronize()
+        finite = all(bool(torch.isfinite(f).all()) for f in first)
+        same = all(torch.equal(f, r["y"][:B]) for f, r in zip(first, self.layers))
+        del first
+        if not (finite and same):
+            print(f"[bench] B={B}: output check failed (finite {finite}, replay == eager {same})",
+                  file=sys.stderr, flush=True)
+        return finite and same
+
     def bytes(self, B, only=None):
         f = fp8_bytes if (self.fp8 or self.int8) else w4a16_bytes
         return sum(f(B, r["K"], r["N"]) for r in self.layers if only is None or only(r))
@@ -565,6 +584,7 @@ def run_decode(args, torch, ops, synth):
         g = graph_of(torch, lambda: stack.step(B))
         ms_g = time_graph(torch, g, args.steps, args.warmup)
         rec["step_ms_p10_p50_p90"] = replay_percentiles(torch, g)
+        rec["outputs_checked"] = stack.check_outputs(B, g)
         del g
         ms = ms_g
         rec.update({"ms_per_step": round(ms, 5), "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3),
@@ -751,6 +771,7 @@ def large_batch_part(args, torch, ops, synth, batches):
     for B in batches:
         g = graph_of(torch, lambda: stack.step(B))
         ms4 = time_graph(torch, g, steps, warmup)
+        checked = stack.check_outputs(B, g)
         del g
 
         def kn_step():
@@ -771,7 +792,8 @@ def large_batch_part(args, torch, ops, synth, batches):
         res[str(B)] = {"w4a16_ms": round(ms4, 4), "bf16_kn_ms": round(ms_kn, 4), "bf16_nk_ms": round(ms_nk, 4),
                        "w4a16_mfma_frac": frac(ms4), "bf16_kn_mfma_frac": frac(ms_kn),
                        "bf16_nk_mfma_frac": frac(ms_nk),
-                       "w4a16_TB_s": round(stack.bytes(B) / (ms4 * 1e-3) / 1e12, 3)}
+                       "w4a16_TB_s": round(stack.bytes(B) / (ms4 * 1e-3) / 1e12, 3),
+                       "outputs_checked": checked}
         print(f"[bench] large B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
     # the smallest measured batch from which W4A16 is not faster than the faster
     # dense layout at every larger measured batch
@@ -844,14 +866,17 @@ def run_fp8(args, torch, ops, synth, int8=False):
     for B in batches:
         g = graph_of(torch, lambda: stack.step(B))
         ms = time_graph(torch, g, args.steps, args.warmup)
+        checked = stack.check_outputs(B, g)
         del g
         g = graph_of(torch, lambda: stack.step(B, two_call=True))
         ms_two = time_graph(torch, g, args.steps, args.warmup)
+        checked = stack.check_outputs(B, g, two_call=True) and checked
         del g
         res[str(B)] = {"ms_per_step": round(ms, 4),
                        "TB_s": round(stack.bytes(B) / (ms * 1e-3) / 1e12, 3),
                        f"{fmt}_mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (peak * 1e12), 4),
                        "two_call_ms_per_step": round(ms_two, 4),
+                       "outputs_checked": checked,
                        "gemms_quantizing_inside": sum(
                            1 for r in stack.layers
                            if ops.w8a8_dynamic_kernel_for(B, r["N"], r["K"]).startswith("w8a8_small_m_dyn"))}
@@ -1078,10 +1103,12 @@ def run_70b(args, torch, ops, synth):
     for B in batches:
         g = graph_of(torch, lambda: stack.step(B))
         ms = time_graph(torch, g, args.steps, args.warmup)
+        checked = stack.check_outputs(B, g)
         del g
         res[str(B)] = {"ms_per_step": round(ms, 4),
                        "TB_s": round(stack.bytes(B) / (ms * 1e-3) / 1e12, 3),
-                       "mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+                       "mfma_frac": round(stack.flops(B) / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                       "outputs_checked": checked}
         print(f"[bench] 70b B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
     out = {"metric": "Llama-3-70B W4A16 decode-step ms vs batch (one GPU)", "value": res["1"]["TB_s"],
            "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

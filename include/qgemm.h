@@ -377,9 +377,12 @@ qg_status qgemm_w8a8_int8(const int8_t *a_i8, const float *a_scale,
  *   y_bf16            out [M, N].
  *   workspace         qg_w8a8_dynamic_workspace_bytes(M, N, K) bytes (NULL
  *                     when that is 0), 16-byte aligned, zero-filled before its
- *                     first use: the GEMM's workspace (counters first, the
- *                     rules of qgemm_w8a8_fp8) followed by room for the codes
- *                     and scales.  Calls sharing it must not overlap in time.
+ *                     first use: the GEMM's workspace (the 64 KiB counter
+ *                     region first, the rules of qgemm_w8a8_fp8), then the
+ *                     codes and scales, always past the counter region, so one
+ *                     workspace serves these calls and qgemm_w8a8_fp8 (_int8)
+ *                     of any shape in any order.  Calls sharing it must not
+ *                     overlap in time.
  *
  * Results equal quant_act_per_token (_int8) followed by qgemm_w8a8_fp8
  * (_int8) bit for bit.  For a few rows (up to four at K = 4096, one at

@@ -149,3 +149,30 @@ def test_dynamic_deterministic_and_workspace_reuse(ops, fmt):
         y1 = host_bits16(lin(a))
         y2 = host_bits16(lin(a))
         assert np.array_equal(y1, y_two) and np.array_equal(y2, y_two), (fmt, M)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_unfused_codes_leave_the_counters_alone(ops, fmt):
+    """One workspace, a bench step's order: 16 rows (unfused: codes in the
+    workspace, the GEMM itself needs none), then 200 rows at K = 14336 whose
+    GEMM splits K and counts arrivals in the counter region.  The codes must
+    never land in that region: it reads zero after the 16-row call, and the
+    split call matches the two-call path on a fresh workspace."""
+    announce(f"qgemm_w8a8_{fmt}_dynamic counter region after an unfused call")
+    _, Lin, quant, _, qmax = _fmt(ops, fmt)
+    K, N = 14336, 4096
+    wt, _ = _weight(ops, fmt, K, N)
+    lin = Lin(wt)
+    need = max(ops.w8a8_dynamic_workspace_bytes(M, N, K) for M in (16, 200))
+    lin._ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    assert "S=" in ops.w8a8_kernel_for(200, N, K) and not ops.w8a8_kernel_for(200, N, K).endswith("S=1")
+    for M in (16, 200, 16, 200):
+        a = dev_bf16(_activations(M, K, qmax, seed=500 + M))
+        y = host_bits16(lin(a))
+        torch.cuda.synchronize()
+        assert lin._ws.numel() == need
+        assert int(torch.count_nonzero(lin._ws[:65536])) == 0, f"counter region written (M={M})"
+        ref_lin = Lin(wt)
+        qa, sa = quant(a)
+        assert np.array_equal(y, host_bits16(ref_lin(a, qa=qa, sa=sa))), (fmt, M)
+

@@ -19,6 +19,8 @@
 
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -967,10 +969,17 @@ static bool w8a8_dyn_fused(int M, int N, int K) {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// unfused: the GEMM's own workspace first (counters at offset 0), then the codes and scales
+// unfused: the GEMM's own workspace first (counters at offset 0, then its
+// slots), then the codes and scales; the codes start after the counter region
+// even when the GEMM needs no workspace, so the counters stay zero for later
+// calls of other shapes on the same workspace
+static size_t dyn_codes_offset(int M, int N, int K) {
+    return std::max(align256(w8a8_workspace_bytes(M, N, K)), kCounterBytes);
+}
+
 size_t w8a8_dyn_workspace_bytes(int M, int N, int K) {
     if (M == 0 || w8a8_dyn_fused(M, N, K)) return 0;
-    return align256(w8a8_workspace_bytes(M, N, K)) + align256((size_t)M * K) + align256((size_t)M * 4);
+    return dyn_codes_offset(M, N, K) + align256((size_t)M * K) + align256((size_t)M * 4);
 }
 
 const char* w8a8_dyn_kernel_for(int M, int N, int K) {
@@ -1017,7 +1026,7 @@ static void launch_w8a8_dyn(const uint16_t* a, const uint8_t* w, const float* sw
         return;
     }
     char* base = static_cast<char*>(ws);
-    const size_t q_off = align256(w8a8_workspace_bytes(M, N, K));
+    const size_t q_off = dyn_codes_offset(M, N, K);
     uint8_t* q = reinterpret_cast<uint8_t*>(base + q_off);
     float* sa = reinterpret_cast<float*>(base + q_off + align256((size_t)M * K));
     launch_quant_act<Fmt>(a, M, K, q, sa, st);

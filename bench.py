@@ -186,23 +186,8 @@ class Stack:
                 ops.qgemm_w4a16(a, r["w"].packed, r["w"].scales, y, B, r["N"], r["K"], ws, nb)
 
     def check_outputs(self, B, g, **step_args):
-        """Replays the timed step's graph once, then runs the same step eagerly:
-        every output must be finite and the two runs identical bit for bit (a
-        split-K slot read before its write, or any other race between the
-        step's launches, would show here).  Returns True when both hold."""
-        torch = self.torch
-        g.replay()
-        torch.cuda.synchronize()
-        first = [r["y"][:B].clone() for r in self.layers]
-        self.step(B, **step_args)
-        torch.cuda.synchronize()
-        finite = all(bool(torch.isfinite(f).all()) for f in first)
-        same = all(torch.equal(f, r["y"][:B]) for f, r in zip(first, self.layers))
-        del first
-        if not (finite and same):
-            print(f"[bench] B={B}: output check failed (finite {finite}, replay == eager {same})",
-                  file=sys.stderr, flush=True)
-        return finite and same
+        return check_replay(self.torch, g, lambda: self.step(B, **step_args),
+                            [r["y"][:B] for r in self.layers], f"B={B}")
 
     def bytes(self, B, only=None):
         f = fp8_bytes if (self.fp8 or self.int8) else w4a16_bytes
@@ -210,6 +195,25 @@ class Stack:
 
     def flops(self, B):
         return sum(2 * B * r["K"] * r["N"] for r in self.layers)
+
+
+def check_replay(torch, g, step, outputs, what):
+    """Replays the timed step's graph once, then runs the same step eagerly:
+    every output must be finite and the two runs identical bit for bit (a
+    split-K slot read before its write, or any other race between the step's
+    launches, would show here).  Returns True when both hold."""
+    g.replay()
+    torch.cuda.synchronize()
+    first = [y.clone() for y in outputs]
+    step()
+    torch.cuda.synchronize()
+    finite = all(bool(torch.isfinite(f).all()) for f in first)
+    same = all(torch.equal(f, y) for f, y in zip(first, outputs))
+    del first
+    if not (finite and same):
+        print(f"[bench] {what}: output check failed (finite {finite}, replay == eager {same})",
+              file=sys.stderr, flush=True)
+    return finite and same
 
 
 def graph_of(torch, fn):
@@ -1057,10 +1061,12 @@ def run_moe(args, torch, ops, synth, w4a8=False):
                     gw(a[:T], off, out=y[:T])
         g = graph_of(torch, step)
         ms = time_graph(torch, g, args.steps, args.warmup)
+        checked = check_replay(torch, g, step, [y[:T] for (_, _, _, _, _, y, _) in gemms], f"moe B={B}")
         del g
         res[str(B)] = {"ms_per_step": round(ms, 4), "rows": T,
                        "active_experts": int(np.sum(np.diff(offsets) > 0)),
-                       "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3), "bytes": nbytes}
+                       "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3), "bytes": nbytes,
+                       "outputs_checked": checked}
         print(f"[bench] moe B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
     B = 16
     r = res[str(B)]

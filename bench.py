@@ -1052,21 +1052,33 @@ def run_moe(args, torch, ops, synth, w4a8=False):
         off = torch.from_numpy(offsets).to(dev)
         nbytes = sum(moe_bytes(offsets, K, N, w4a8) for (_, K, N, *_r) in gemms)
 
-        def step():
+        def step(two_call=False):
             for (_, K, N, gw, a, y, q) in gemms:
-                if w4a8:
+                if w4a8 and two_call:
                     ops.quant_act_per_token(a[:T], T, K, q[0][:T], q[1][:T])
                     gw.w4a8(q[0][:T], q[1][:T], off, out=y[:T])
+                elif w4a8:
+                    gw.w4a8_dynamic(a[:T], off, out=y[:T])
                 else:
                     gw(a[:T], off, out=y[:T])
+        outs = [y[:T] for (_, _, _, _, _, y, _) in gemms]
         g = graph_of(torch, step)
         ms = time_graph(torch, g, args.steps, args.warmup)
-        checked = check_replay(torch, g, step, [y[:T] for (_, _, _, _, _, y, _) in gemms], f"moe B={B}")
+        checked = check_replay(torch, g, step, outs, f"moe B={B}")
         del g
         res[str(B)] = {"ms_per_step": round(ms, 4), "rows": T,
                        "active_experts": int(np.sum(np.diff(offsets) > 0)),
-                       "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3), "bytes": nbytes,
-                       "outputs_checked": checked}
+                       "TB_s": round(nbytes / (ms * 1e-3) / 1e12, 3), "bytes": nbytes}
+        if w4a8:
+            # the same step with the separate quantization kernel before each GEMM
+            g = graph_of(torch, lambda: step(two_call=True))
+            res[str(B)]["two_call_ms_per_step"] = round(time_graph(torch, g, args.steps, args.warmup), 4)
+            checked = check_replay(torch, g, lambda: step(two_call=True), outs, f"moe two-call B={B}") and checked
+            del g
+            res[str(B)]["gemms_quantizing_inside"] = sum(
+                1 for (_, K, N, gw, *_r) in gemms
+                if ops.w4a8_grouped_dynamic_kernel_for(gw.E, T, N, K) == "w4a8_grouped_dyn_kernel")
+        res[str(B)]["outputs_checked"] = checked
         print(f"[bench] moe B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
     B = 16
     r = res[str(B)]
@@ -1087,7 +1099,7 @@ def run_moe(args, torch, ops, synth, w4a8=False):
            "by_batch": res,
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                        "kernel": ("quant_act_per_token + grouped_items_kernel + w4a8_grouped_kernel"
+                        "kernel": ("grouped_items_kernel + w4a8_grouped_dyn_kernel (the quantization inside)"
                                    if w4a8 else "grouped_items_kernel + w4a16_grouped_kernel")
                                   + " per GEMM (96 per step)",
                         "avg_launch_us": round(per_launch_us, 3)}}

@@ -334,6 +334,32 @@ qg_status qgemm_w4a8_fp8_grouped(const uint8_t *a_e4m3, const float *a_scale,
                                  qg_stream stream);
 
 /*
+ * qgemm_w4a8_fp8_grouped_dynamic -- qgemm_w4a8_fp8_grouped with the per-token
+ * e4m3 quantization of the routed rows inside the call: bf16 rows in, the
+ * result of quant_act_per_token followed by qgemm_w4a8_fp8_grouped, bit for bit.
+ * [P1, the mixture-of-experts section (INT4 expert weights with FP8
+ *  activations); P2 3.4 "W8A8-FP" (activation scales computed on the fly).]
+ *
+ *   a_bf16     in   [T, K] routed rows grouped by expert (as qgemm_w4a16_grouped).
+ *   offsets, packed, scales, y_bf16, E, T, N, K: as qgemm_w4a8_fp8_grouped.
+ *   workspace  qg_w4a8_grouped_dynamic_workspace_bytes(E, T, N, K) bytes,
+ *              16-byte aligned, no initial contents needed: the work items
+ *              first, then (when the quantization runs as its own kernel) the
+ *              codes and scales.  Calls sharing it must not overlap in time.
+ * With few routed rows (fewer than 48, items of up to 32 rows, K <= 2048; see
+ * qg_w4a8_grouped_dynamic_kernel_for) each workgroup quantizes its item's rows
+ * into LDS, so no codes reach memory and the call makes one launch fewer.
+ * Errors as qgemm_w4a8_fp8_grouped.
+ */
+size_t qg_w4a8_grouped_dynamic_workspace_bytes(int64_t E, int64_t T, int64_t N, int64_t K);
+const char *qg_w4a8_grouped_dynamic_kernel_for(int64_t E, int64_t T, int64_t N, int64_t K);
+qg_status qgemm_w4a8_fp8_grouped_dynamic(const uint16_t *a_bf16, const int32_t *offsets,
+                                         const uint32_t *packed, const uint16_t *scales,
+                                         uint16_t *y_bf16, int E, int T, int N, int K,
+                                         void *workspace, size_t workspace_bytes,
+                                         qg_stream stream);
+
+/*
  * W8A8-INT8 -- the integer sibling of the fp8 path.
  * [P2 3.4 "W8A8-INT": per-output-channel symmetric weights, s = max|w| / 127,
  *  codes in [-127, 127]; dynamic per-token activations (the scheme the page

@@ -97,6 +97,21 @@ int main() {
     EXPECT_STATUS(qgemm_w4a8_fp8_grouped(u8, f32, off_odd, w32, s16, y16, 3, 8, 32, 256, ws, gneed, nullptr),
                   QG_ERR_ALIGN);
 
+    // grouped W4A8 on bf16 rows (quantization inside the call)
+    const size_t gdneed = qg_w4a8_grouped_dynamic_workspace_bytes(3, 8, 32, 256);
+    EXPECT(gdneed >= gneed);
+    EXPECT_LAUNCH(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 8, 32, 256, ws, gdneed, nullptr));
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 8, 32, 256, ws, gdneed - 1, nullptr),
+                  QG_ERR_WORKSPACE);
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 8, 32, 256, nullptr, 0, nullptr),
+                  QG_ERR_NULL);
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16 + 1, i32, w32, s16, y16, 3, 8, 32, 256, ws, gdneed, nullptr),
+                  QG_ERR_ALIGN);
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 0, 8, 32, 256, ws, gdneed, nullptr),
+                  QG_ERR_SHAPE);
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 0, 32, 256, nullptr, 0, nullptr),
+                  QG_OK);
+
     // W8A8-FP8 and INT8
     EXPECT_LAUNCH(quant_act_per_token(a16, 4, 256, u8, f32, nullptr));
     EXPECT_STATUS(quant_act_per_token(a16, 4, 250, u8, f32, nullptr), QG_ERR_SHAPE);

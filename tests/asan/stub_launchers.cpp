@@ -33,6 +33,12 @@ void launch_qgemm_w4a8_fp8(const uint8_t*, const float*, const uint32_t*, const 
                            int, hipStream_t) { ++g_launches; }
 void launch_qgemm_w4a8_fp8_grouped(const uint8_t*, const float*, const int*, const uint32_t*, const uint16_t*,
                                    uint16_t*, int, int, int, int, void*, hipStream_t) { ++g_launches; }
+size_t w4a8_grouped_dyn_workspace_bytes(int E, int T, int, int K) {
+    return w4a16_grouped_workspace_bytes(E, T, K) + (T > 16 ? (size_t)T * K + (size_t)T * 4 : 0);
+}
+const char* w4a8_grouped_dyn_kernel_for(int, int, int, int) { return "stub"; }
+void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t*, const int*, const uint32_t*, const uint16_t*, uint16_t*,
+                                       int, int, int, int, void*, hipStream_t) { ++g_launches; }
 void launch_quant_act_per_token(const uint16_t*, int, int, uint8_t*, float*, hipStream_t) { ++g_launches; }
 void launch_quant_weight_fp8(const uint16_t*, int, int, uint8_t*, float*, hipStream_t) { ++g_launches; }
 void launch_quant_act_per_token_i8(const uint16_t*, int, int, int8_t*, float*, hipStream_t) { ++g_launches; }

@@ -242,6 +242,31 @@ qg_status qgemm_w4a8_fp8_grouped(const uint8_t* a_e4m3, const float* a_scale, co
     return launched();
 }
 
+size_t qg_w4a8_grouped_dynamic_workspace_bytes(int64_t E, int64_t T, int64_t N, int64_t K) {
+    if (!grouped_ok(E, T, N, K)) return 0;
+    return qg::w4a8_grouped_dyn_workspace_bytes((int)E, (int)T, (int)N, (int)K);
+}
+
+const char* qg_w4a8_grouped_dynamic_kernel_for(int64_t E, int64_t T, int64_t N, int64_t K) {
+    if (!grouped_ok(E, T, N, K)) return "";
+    return qg::w4a8_grouped_dyn_kernel_for((int)E, (int)T, (int)N, (int)K);
+}
+
+qg_status qgemm_w4a8_fp8_grouped_dynamic(const uint16_t* a_bf16, const int32_t* offsets, const uint32_t* packed,
+                                         const uint16_t* scales, uint16_t* y_bf16, int E, int T, int N, int K,
+                                         void* workspace, size_t workspace_bytes, qg_stream stream) {
+    if (!grouped_ok(E, T, N, K)) return QG_ERR_SHAPE;
+    if (T == 0) return QG_OK;
+    if (!a_bf16 || !offsets || !packed || !scales || !y_bf16 || !workspace) return QG_ERR_NULL;
+    if (!aligned(a_bf16, 16) || !aligned(offsets, 4) || !aligned(packed, 16) || !aligned(scales, 4) ||
+        !aligned(y_bf16, 16) || !aligned(workspace, 16))
+        return QG_ERR_ALIGN;
+    if (workspace_bytes < qg::w4a8_grouped_dyn_workspace_bytes(E, T, N, K)) return QG_ERR_WORKSPACE;
+    qg::launch_qgemm_w4a8_fp8_grouped_dyn(a_bf16, offsets, packed, scales, y_bf16, E, T, N, K, workspace,
+                                          as_stream(stream));
+    return launched();
+}
+
 // ---- W8A8-INT8: the same kernels with int8 codes and int32 accumulation ----
 
 size_t qg_w8a8_int8_workspace_bytes(int64_t M, int64_t N, int64_t K) {

@@ -67,6 +67,13 @@ void launch_qgemm_w4a8_fp8(const uint8_t* qa, const float* sa, const uint32_t* w
 void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int* offsets,
                                    const uint32_t* wq, const uint16_t* sc, uint16_t* y, int E, int T,
                                    int N, int K, void* ws, hipStream_t s);
+// bf16 routed rows in: the quantization inside the grouped GEMM for small
+// items, else quant_act_per_token into the workspace (after the items) first
+size_t w4a8_grouped_dyn_workspace_bytes(int E, int T, int N, int K);
+const char* w4a8_grouped_dyn_kernel_for(int E, int T, int N, int K);
+void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, const uint32_t* wq,
+                                       const uint16_t* sc, uint16_t* y, int E, int T, int N, int K, void* ws,
+                                       hipStream_t s);
 
 // W8A8-FP8 path (fp8.hip)
 void launch_quant_act_per_token(const uint16_t* a, int M, int K, uint8_t* q, float* s,

@@ -23,15 +23,18 @@
 // hold the same k in every byte position whatever order the MFMA sums in.
 
 #include "device_common.h"
+#include "formats.h"
 #include "launch.h"
 
 namespace qg {
 
-template <int MT, int CT, int NWAVE>
-__device__ __forceinline__ void w4a8_tile(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
-                                          const uint32_t* __restrict__ wq,
-                                          const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
-                                          int M, int N, int K, int nt0) {
+// aload(mt, off) returns the 8 code bytes at byte offset `off` (group g, k-step
+// t: 128 g + 32 t) of the lane's row 16 mt + col from its quarter's start
+// (8 q); ascale(m) is row m's activation scale.
+template <int MT, int CT, int NWAVE, class ALoad, class AScale>
+__device__ __forceinline__ void w4a8_tile_src(ALoad aload, AScale ascale, const uint32_t* __restrict__ wq,
+                                              const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
+                                              int M, int N, int K, int nt0) {
     const int G = K >> 7;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -46,10 +49,6 @@ __device__ __forceinline__ void w4a8_tile(const uint8_t* __restrict__ qa, const 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) total[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const uint8_t* arow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        arow[mt] = qa + (size_t)min(mt * 16 + col, M - 1) * K + 8 * q;   // rows >= M: discarded
     const u32x4* wp[CT];
     const uint16_t* sp[CT];
 #pragma unroll
@@ -76,8 +75,7 @@ __device__ __forceinline__ void w4a8_tile(const uint8_t* __restrict__ qa, const 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                b.a[mt][t] = *reinterpret_cast<const uint2*>(arow[mt] + (size_t)g * 128 + 32 * t);
+            for (int t = 0; t < 4; ++t) b.a[mt][t] = aload(mt, g * 128 + 32 * t);
     };
     auto compute = [&](const Buf& b) {
         i32x8 af[MT];
@@ -143,8 +141,24 @@ __device__ __forceinline__ void w4a8_tile(const uint8_t* __restrict__ qa, const 
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) sum += red[w][ct][mt][l][i];
         const int n = (nt0 + ct) * 16 + (l & 15);
-        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum * sa[m]);
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum * ascale(m));
     }
+}
+
+// the tile on e4m3 codes and scales in memory (rows >= M read row M - 1: discarded)
+template <int MT, int CT, int NWAVE>
+__device__ __forceinline__ void w4a8_tile(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                          const uint32_t* __restrict__ wq,
+                                          const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
+                                          int M, int N, int K, int nt0) {
+    const int lane = threadIdx.x & 63;
+    const uint8_t* arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        arow[mt] = qa + (size_t)min(mt * 16 + (lane & 15), M - 1) * K + 8 * (lane >> 4);
+    auto aload = [&](int mt, int off) { return *reinterpret_cast<const uint2*>(arow[mt] + off); };
+    auto ascale = [&](int m) { return sa[m]; };
+    w4a8_tile_src<MT, CT, NWAVE>(aload, ascale, wq, sc, y, M, N, K, nt0);
 }
 
 // dense: blockIdx.y takes rows [16 MT y, 16 MT (y + 1))
@@ -175,6 +189,85 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a8_grouped_kernel(
     const size_t nsc = (size_t)(K / 128) * N;
     w4a8_tile<MT, CT, NWAVE>(qa + (size_t)r0 * K, sa + r0, wq + e * words, sc + e * nsc,
                              y + (size_t)r0 * N, rows, N, K, blockIdx.x * CT);
+}
+
+// ---------------------------------------------------------------------------
+// Expert-grouped with the per-token e4m3 quantization inside the GEMM
+// (qgemm_w4a8_fp8_grouped_dynamic, bf16 routed rows in, up to 32 rows per
+// work item).  Each workgroup quantizes its item's rows into LDS first -- the
+// codes and scales of quant_act_per_token: the row's abs-max, the IEEE scale
+// quotient amax / 448 and the code quotient of formats.h (the code of the
+// IEEE quotient) -- with every wave taking whole rows (CPL 16-byte chunks per
+// lane hold a row of K <= 512 CPL), then runs the W4A8 tile on them.  The
+// tile, its k-order and its reduction are those of w4a8_grouped_kernel, so the
+// output equals quant_act_per_token + qgemm_w4a8_fp8_grouped bit for bit,
+// with one launch fewer.  Codes: rows of K + 16 bytes (the 16 rows of a
+// fragment read start 4 banks apart).
+// ---------------------------------------------------------------------------
+template <int MT, int CT, int NWAVE, int CPL>
+__global__ __launch_bounds__(NWAVE * 64) void w4a8_grouped_dyn_kernel(
+    const uint16_t* __restrict__ a, const int* __restrict__ items, const uint32_t* __restrict__ wq,
+    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N, int K) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char codes[];   // [rows][K + 16]
+    __shared__ float srow[16 * MT];
+    const int it = blockIdx.y;
+    if (it >= items[0]) return;
+    const int e = items[1 + 3 * it];
+    const int r0 = items[2 + 3 * it];
+    const int rows = items[3 + 3 * it];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rowb = K + 16;
+    const int cpr = K >> 3;                      // 16-byte chunks per row (<= 64 CPL)
+    for (int m = wave; m < rows; m += NWAVE) {
+        const u32x4* row = reinterpret_cast<const u32x4*>(a + (size_t)(r0 + m) * K);
+        u32x4 v[CPL];
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            v[i] = c < cpr ? row[c] : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mx = fmaxf(mx, fabsf(bf16_to_f32(w4[j] & 0xffffu)));
+                mx = fmaxf(mx, fabsf(bf16_to_f32(w4[j] >> 16)));
+            }
+        }
+        mx = wave_max(mx);
+        const float s = mx / FmtE4M3::qmax;      // IEEE fp32 quotient
+        const float r = 1.0f / s;
+        const bool fast = s >= 0x1p-100f && s < __builtin_inff();
+        if (lane == 0) srow[m] = s;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            if (c >= cpr) break;
+            uint2 o = make_uint2(0u, 0u);
+            if (s != 0.0f) {
+                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                uint32_t b[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    b[j] = FmtE4M3::encode2(dyn_quotient<FmtE4M3>(bf16_to_f32(w4[j] & 0xffffu), s, r, fast),
+                                            dyn_quotient<FmtE4M3>(bf16_to_f32(w4[j] >> 16), s, r, fast));
+                o.x = b[0] | (b[1] << 16);
+                o.y = b[2] | (b[3] << 16);
+            }
+            *reinterpret_cast<uint2*>(codes + (size_t)m * rowb + (size_t)c * 8) = o;
+        }
+    }
+    __syncthreads();
+    const unsigned char* arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        arow[mt] = codes + (size_t)min(mt * 16 + (lane & 15), rows - 1) * rowb + 8 * (lane >> 4);
+    auto aload = [&](int mt, int off) { return *reinterpret_cast<const uint2*>(arow[mt] + off); };
+    auto ascale = [&](int m) { return srow[m]; };
+    const size_t words = (size_t)(K / 8) * N;
+    const size_t nsc = (size_t)(K / 128) * N;
+    w4a8_tile_src<MT, CT, NWAVE>(aload, ascale, wq + e * words, sc + e * nsc, y + (size_t)r0 * N, rows, N,
+                                 K, blockIdx.x * CT);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,6 +545,94 @@ void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int
                            dim3(NT / decltype(ct)::value, max_items), dim3(W4A8_NWAVE * 64), 0, s, qa, sa,
                            items, wq, sc, y, N, K);
     });
+}
+
+// ---- bf16 routed rows in (per-token quantization inside the call) ----
+// Quantize inside the GEMM below this many routed rows.  Every workgroup of an
+// item repeats its rows' quantization and holds room for 16 MT rows of codes
+// in LDS (fewer workgroups per CU); measured on the Qwen3-30B-A3B step (96
+// grouped GEMMs, top-8 of 128 experts), fused vs separate quantization, ms:
+// B = 1 0.96 / 1.10, 2 1.14 / 1.30, 4 1.39 / 1.57, 6 1.81 / 1.81, 8 2.08 /
+// 2.08, 12 2.54 / 2.50, 16 2.99 / 2.65.
+#ifndef QG_W4A8_DYN_MAX_T
+#define QG_W4A8_DYN_MAX_T 48
+#endif
+
+static int w4a8_dyn_cpl(int K) { return K <= 512 ? 1 : K <= 1024 ? 2 : K <= 2048 ? 4 : 0; }
+
+// fused: the small-item path (not the large tile), at most 32 rows per item,
+// rows of at most 2048 values
+static bool w4a8_grouped_dyn_fused(int E, int T, int N, int K) {
+    if (T < 1 || T >= QG_W4A8_DYN_MAX_T || w4a8_grouped_large(E, T, N)) return false;
+    return w4a16_grouped_rows_per_item(E, T) <= 32 && w4a8_dyn_cpl(K) != 0 && K % 128 == 0;
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// the items (and what the grouped W4A16 path keeps there) first; unfused: the
+// codes and scales of the separate quantization after them
+size_t w4a8_grouped_dyn_workspace_bytes(int E, int T, int N, int K) {
+    const size_t items = w4a16_grouped_workspace_bytes(E, T, K);
+    if (T == 0 || w4a8_grouped_dyn_fused(E, T, N, K)) return items;
+    return align256(items) + align256((size_t)T * K) + align256((size_t)T * 4);
+}
+
+const char* w4a8_grouped_dyn_kernel_for(int E, int T, int N, int K) {
+    if (T == 0) return "none";
+    if (w4a8_grouped_dyn_fused(E, T, N, K)) return "w4a8_grouped_dyn_kernel";
+    return w4a8_grouped_large(E, T, N) ? "quant_act_per_token + w4a8_grouped_large_kernel"
+                                       : "quant_act_per_token + w4a8_grouped_kernel";
+}
+
+void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, const uint32_t* wq,
+                                       const uint16_t* sc, uint16_t* y, int E, int T, int N, int K, void* ws,
+                                       hipStream_t s) {
+    if (!w4a8_grouped_dyn_fused(E, T, N, K)) {
+        char* base = static_cast<char*>(ws);
+        const size_t q_off = align256(w4a16_grouped_workspace_bytes(E, T, K));
+        uint8_t* q = reinterpret_cast<uint8_t*>(base + q_off);
+        float* sa = reinterpret_cast<float*>(base + q_off + align256((size_t)T * K));
+        launch_quant_act_per_token(a, T, K, q, sa, s);
+        launch_qgemm_w4a8_fp8_grouped(q, sa, offsets, wq, sc, y, E, T, N, K, ws, s);
+        return;
+    }
+    const int NT = N / 16;
+    const int R = w4a16_grouped_rows_per_item(E, T);
+    const int max_items = w4a16_grouped_max_items(E, T);
+    int* items = static_cast<int*>(ws);
+    launch_grouped_items(offsets, E, T, R, max_items, items, s);
+    const int CT = w4a8_ct(NT);
+    const size_t lds = (size_t)R * (K + 16);
+    auto go = [&](auto mt, auto ct, auto nwave, auto cpl) {
+        constexpr int MT_ = decltype(mt)::value, CT_ = decltype(ct)::value;
+        constexpr int NW = decltype(nwave)::value, CPL_ = decltype(cpl)::value;
+        static std::atomic<uint64_t> lds_set{0};     // codes of up to 16 MT rows of 512 CPL values
+        allow_dynamic_lds(reinterpret_cast<const void*>(&w4a8_grouped_dyn_kernel<MT_, CT_, NW, CPL_>),
+                          16 * MT_ * (512 * CPL_ + 16), lds_set);
+        hipLaunchKernelGGL((w4a8_grouped_dyn_kernel<MT_, CT_, NW, CPL_>), dim3(NT / CT_, max_items),
+                           dim3(NW * 64), lds, s, a, items, wq, sc, y, N, K);
+    };
+    auto by_cpl = [&](auto mt, auto ct, auto nwave) {
+        switch (w4a8_dyn_cpl(K)) {
+            case 1: go(mt, ct, nwave, ic<1>{}); break;
+            case 2: go(mt, ct, nwave, ic<2>{}); break;
+            default: go(mt, ct, nwave, ic<4>{}); break;
+        }
+    };
+    // as the unfused launch: one wave per workgroup from QG_W4A8_ONE_WAVE_MIN_T rows
+    auto by_mt_ct = [&](auto nwave) {
+        auto by_ct = [&](auto mt) {
+            if (CT == 4) by_cpl(mt, ic<4>{}, nwave);
+            else if (CT == 2) by_cpl(mt, ic<2>{}, nwave);
+            else by_cpl(mt, ic<1>{}, nwave);
+        };
+        if (R <= 16) by_ct(ic<1>{});
+        else by_ct(ic<2>{});
+    };
+    if (T >= QG_W4A8_ONE_WAVE_MIN_T)
+        by_mt_ct(ic<1>{});
+    else
+        by_mt_ct(ic<W4A8_NWAVE>{});
 }
 
 }  // namespace qg

@@ -57,6 +57,9 @@ _SIGS = {
     "qg_w8a8_dynamic_kernel_for": (ctypes.c_char_p, [_I64, _I64, _I64]),
     "qgemm_w8a8_fp8_dynamic": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "qgemm_w8a8_int8_dynamic": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "qg_w4a8_grouped_dynamic_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "qg_w4a8_grouped_dynamic_kernel_for": (ctypes.c_char_p, [_I64, _I64, _I64, _I64]),
+    "qgemm_w4a8_fp8_grouped_dynamic": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -235,6 +238,22 @@ def qgemm_w8a8_int8_dynamic(a_bf16, w_i8, w_scale, y_bf16, M, N, K, workspace=No
                                         _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def w4a8_grouped_dynamic_workspace_bytes(E, T, N, K):
+    return _lib.qg_w4a8_grouped_dynamic_workspace_bytes(E, T, N, K)
+
+
+def w4a8_grouped_dynamic_kernel_for(E, T, N, K):
+    return _lib.qg_w4a8_grouped_dynamic_kernel_for(E, T, N, K).decode()
+
+
+def qgemm_w4a8_fp8_grouped_dynamic(a_bf16, offsets_i32, packed, scales, y_bf16, E, T, N, K, workspace,
+                                   workspace_bytes, stream=None):
+    _check("qgemm_w4a8_fp8_grouped_dynamic",
+           _lib.qgemm_w4a8_fp8_grouped_dynamic(_ptr(a_bf16), _ptr(offsets_i32), _ptr(packed), _ptr(scales),
+                                               _ptr(y_bf16), E, T, N, K, _ptr(workspace), workspace_bytes,
+                                               _stream(stream)))
+
+
 # ---- tensor-level helpers (allocate outputs with torch, then call the above) --
 
 def _bf16(t):
@@ -367,6 +386,19 @@ class GroupedInt4Weight:
             self._ws = torch.empty((need + 3) // 4, dtype=torch.int32, device=qa.device)
         qgemm_w4a8_fp8_grouped(qa, sa, offsets, self.packed, self.scales, y, self.E, T, self.N, K,
                                self._ws if need else None, need, stream)
+        return y
+
+    def w4a8_dynamic(self, a, offsets, out=None, stream=None):
+        """The W4A8-FP8 product on bf16 rows, quantized per token inside the call."""
+        T, K = a.shape
+        if K != self.K or offsets.numel() != self.E + 1 or offsets.dtype != torch.int32:
+            raise ValueError("grouped GEMM: activation K or offsets do not match the weights")
+        y = out if out is not None else torch.empty((T, self.N), dtype=torch.bfloat16, device=a.device)
+        need = w4a8_grouped_dynamic_workspace_bytes(self.E, T, self.N, K)
+        if need and (self._ws is None or self._ws.numel() * 4 < need):
+            self._ws = torch.empty((need + 3) // 4, dtype=torch.int32, device=a.device)
+        qgemm_w4a8_fp8_grouped_dynamic(_bf16(a), offsets, self.packed, self.scales, y, self.E, T, self.N, K,
+                                       self._ws if need else None, need, stream)
         return y
 
 

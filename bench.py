@@ -1082,6 +1082,7 @@ def run_moe(args, torch, ops, synth, w4a8=False):
         print(f"[bench] moe B={B}: {res[str(B)]}", file=sys.stderr, flush=True)
     B = 16
     r = res[str(B)]
+    _, K0, N0 = synth.QWEN3_MOE_SHAPES[0]
     per_launch_us = r["ms_per_step"] * 1e3 / len(gemms)
     achieved = r["bytes"] / len(gemms) / (per_launch_us * 1e-6) / 1e9
     fmt = "W4A8-FP8" if w4a8 else "W4A16"
@@ -1099,9 +1100,8 @@ def run_moe(args, torch, ops, synth, w4a8=False):
            "by_batch": res,
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                        "kernel": ("grouped_items_kernel + w4a8_grouped_dyn_kernel (the quantization inside)"
-                                   if w4a8 else "grouped_items_kernel + w4a16_grouped_kernel")
-                                  + " per GEMM (96 per step)",
+                        "kernel": (ops.w4a8_grouped_dynamic_kernel_for(E, B * k, N0, K0) if w4a8
+                                   else "w4a16_grouped_kernel") + " per GEMM (96 per step)",
                         "avg_launch_us": round(per_launch_us, 3)}}
     if not args.no_cpu_baseline:
         sec, threads = cpu_baseline_moe(B, w4a8)

@@ -236,9 +236,13 @@ qg_status qgemm_w4a16_noalloc(const uint16_t *a_bf16, const uint32_t *packed,
  *   y_bf16     out  [T, N]: row r = a[r] . w_hat_e for the expert e owning r.
  *   E          1 .. 1024.   T   routed rows (0: nothing to do).
  *   workspace  qg_w4a16_grouped_workspace_bytes(E, T, N, K) bytes (4-byte
- *              aligned): the call's work items (expert, row chunk), rebuilt by
- *              every call, so no initial contents are needed.  Calls that
- *              share a workspace must not overlap in time.
+ *              aligned), no initial contents needed; the size is 0 (NULL is
+ *              then accepted) unless the routed rows average 33 or more per
+ *              expert that has rows, where it holds the fp32 offset terms of
+ *              every routed row.  Calls that share a workspace must not
+ *              overlap in time.  The work items (expert, row chunk of up to
+ *              16, 32 or 64 rows) are derived on the device by each
+ *              workgroup and never stored.
  * Offsets are read on the device and clamped into [0, T] with
  * offsets[e] <= offsets[e+1] enforced per expert, so malformed offsets never
  * cause an access out of bounds; rows they leave unassigned keep their old
@@ -318,10 +322,10 @@ qg_status qgemm_w8a8_fp8(const uint8_t *a_e4m3, const float *a_scale,
  * e4m3 bytes (code c is the e4m3 value c * 2^-9) plus the folded offset.
  *
  * qgemm_w4a8_fp8: any M >= 0 (rows in chunks of 16, 32 or 64).
- * qgemm_w4a8_fp8_grouped: rows grouped by expert with device offsets, the
- *   weights and scales of E experts back to back, and the workspace exactly as
- *   qgemm_w4a16_grouped (qg_w4a16_grouped_workspace_bytes); a_scale is per
- *   routed row.
+ * qgemm_w4a8_fp8_grouped: rows grouped by expert with device offsets and the
+ *   weights and scales of E experts back to back, as qgemm_w4a16_grouped;
+ *   a_scale is per routed row.  It needs no workspace: `workspace` and
+ *   `workspace_bytes` are not read (NULL and 0 are fine).
  */
 qg_status qgemm_w4a8_fp8(const uint8_t *a_e4m3, const float *a_scale,
                          const uint32_t *packed, const uint16_t *scales,
@@ -343,13 +347,15 @@ qg_status qgemm_w4a8_fp8_grouped(const uint8_t *a_e4m3, const float *a_scale,
  *   a_bf16     in   [T, K] routed rows grouped by expert (as qgemm_w4a16_grouped).
  *   offsets, packed, scales, y_bf16, E, T, N, K: as qgemm_w4a8_fp8_grouped.
  *   workspace  qg_w4a8_grouped_dynamic_workspace_bytes(E, T, N, K) bytes,
- *              16-byte aligned, no initial contents needed: the work items
- *              first, then (when the quantization runs as its own kernel) the
- *              codes and scales.  Calls sharing it must not overlap in time.
+ *              16-byte aligned, no initial contents needed: 0 (NULL is then
+ *              accepted) when the quantization runs inside the GEMM, else the
+ *              codes and scales of the separate quantization.  Calls sharing
+ *              it must not overlap in time.
  * With few routed rows (fewer than 48, items of up to 32 rows, K <= 2048; see
  * qg_w4a8_grouped_dynamic_kernel_for) each workgroup quantizes its item's rows
  * into LDS, so no codes reach memory and the call makes one launch fewer.
- * Errors as qgemm_w4a8_fp8_grouped.
+ * Errors as qgemm_w4a16_grouped (a workspace that is needed but NULL:
+ * QG_ERR_NULL; smaller than the query: QG_ERR_WORKSPACE).
  */
 size_t qg_w4a8_grouped_dynamic_workspace_bytes(int64_t E, int64_t T, int64_t N, int64_t K);
 const char *qg_w4a8_grouped_dynamic_kernel_for(int64_t E, int64_t T, int64_t N, int64_t K);

@@ -80,34 +80,46 @@ int main() {
     // a shape whose workspace exceeds the scratch (the stub's size query says 64 MiB)
     EXPECT_STATUS(qgemm_w4a16_noalloc(a16, w32, s16, y16, 100, 128000, 256, nullptr), QG_ERR_WORKSPACE);
 
-    // grouped W4A16 and W4A8
+    // grouped W4A16 and W4A8: few rows per expert need no workspace (NULL is
+    // fine), many rows per expert (the large path) need one
     const int32_t off_ok[4] = {0, 3, 3, 8};
     for (int i = 0; i < 4; ++i) i32[i] = off_ok[i];
-    const size_t gneed = qg_w4a16_grouped_workspace_bytes(3, 8, 32, 256);
-    EXPECT(gneed > 0);
-    EXPECT_LAUNCH(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 3, 8, 32, 256, ws, gneed, nullptr));
-    EXPECT_STATUS(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 0, 8, 32, 256, ws, gneed, nullptr),
+    EXPECT(qg_w4a16_grouped_workspace_bytes(3, 8, 32, 256) == 0);
+    EXPECT_LAUNCH(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 3, 8, 32, 256, nullptr, 0, nullptr));
+    EXPECT_STATUS(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 0, 8, 32, 256, nullptr, 0, nullptr),
                   QG_ERR_SHAPE);
-    EXPECT_STATUS(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 3, 8, 32, 256, ws, gneed - 4, nullptr),
+    const size_t gneed = qg_w4a16_grouped_workspace_bytes(3, 200, 32, 256);
+    EXPECT(gneed > 0);
+    EXPECT_LAUNCH(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 3, 200, 32, 256, ws, gneed, nullptr));
+    EXPECT_STATUS(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 3, 200, 32, 256, ws, gneed - 4, nullptr),
                   QG_ERR_WORKSPACE);
+    EXPECT_STATUS(qgemm_w4a16_grouped(a16, i32, w32, s16, y16, 3, 200, 32, 256, nullptr, 0, nullptr),
+                  QG_ERR_NULL);
     EXPECT_LAUNCH(qgemm_w4a8_fp8(u8, f32, w32, s16, y16, 40, 32, 256, nullptr));
     EXPECT_STATUS(qgemm_w4a8_fp8(u8, nullptr, w32, s16, y16, 40, 32, 256, nullptr), QG_ERR_NULL);
-    EXPECT_LAUNCH(qgemm_w4a8_fp8_grouped(u8, f32, i32, w32, s16, y16, 3, 8, 32, 256, ws, gneed, nullptr));
+    EXPECT_LAUNCH(qgemm_w4a8_fp8_grouped(u8, f32, i32, w32, s16, y16, 3, 8, 32, 256, nullptr, 0, nullptr));
+    EXPECT_LAUNCH(qgemm_w4a8_fp8_grouped(u8, f32, i32, w32, s16, y16, 3, 200, 32, 256, nullptr, 0, nullptr));
     const auto* off_odd = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(i32) + 2);
-    EXPECT_STATUS(qgemm_w4a8_fp8_grouped(u8, f32, off_odd, w32, s16, y16, 3, 8, 32, 256, ws, gneed, nullptr),
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped(u8, f32, off_odd, w32, s16, y16, 3, 8, 32, 256, nullptr, 0, nullptr),
                   QG_ERR_ALIGN);
 
-    // grouped W4A8 on bf16 rows (quantization inside the call)
-    const size_t gdneed = qg_w4a8_grouped_dynamic_workspace_bytes(3, 8, 32, 256);
-    EXPECT(gdneed >= gneed);
-    EXPECT_LAUNCH(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 8, 32, 256, ws, gdneed, nullptr));
-    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 8, 32, 256, ws, gdneed - 1, nullptr),
+    // grouped W4A8 on bf16 rows (quantization inside the call): none when fused,
+    // the codes and scales otherwise
+    EXPECT(qg_w4a8_grouped_dynamic_workspace_bytes(3, 8, 32, 256) == 0);
+    EXPECT_LAUNCH(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 8, 32, 256, nullptr, 0, nullptr));
+    const size_t gdneed = qg_w4a8_grouped_dynamic_workspace_bytes(3, 40, 32, 256);
+    EXPECT(gdneed >= 40 * 256);
+    EXPECT_LAUNCH(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 40, 32, 256, ws, gdneed, nullptr));
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 40, 32, 256, ws, gdneed - 1, nullptr),
                   QG_ERR_WORKSPACE);
-    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 8, 32, 256, nullptr, 0, nullptr),
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 40, 32, 256, nullptr, 0, nullptr),
                   QG_ERR_NULL);
-    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16 + 1, i32, w32, s16, y16, 3, 8, 32, 256, ws, gdneed, nullptr),
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 40, 32, 256,
+                                                 reinterpret_cast<char*>(ws) + 4, gdneed, nullptr),
                   QG_ERR_ALIGN);
-    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 0, 8, 32, 256, ws, gdneed, nullptr),
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16 + 1, i32, w32, s16, y16, 3, 8, 32, 256, nullptr, 0, nullptr),
+                  QG_ERR_ALIGN);
+    EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 0, 8, 32, 256, nullptr, 0, nullptr),
                   QG_ERR_SHAPE);
     EXPECT_STATUS(qgemm_w4a8_fp8_grouped_dynamic(a16, i32, w32, s16, y16, 3, 0, 32, 256, nullptr, 0, nullptr),
                   QG_OK);

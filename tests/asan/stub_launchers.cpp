@@ -23,18 +23,20 @@ void launch_qgemm_w4a16(const uint16_t*, const uint32_t*, const uint16_t*, uint1
                         hipStream_t) { ++g_launches; }
 int w4a16_grouped_max_items(int E, int T) { return (T < E ? T : E) + (T + 15) / 16; }
 int w4a16_grouped_rows_per_item(int, int) { return 16; }
-void launch_grouped_items(const int*, int, int, int, int, int*, hipStream_t) { ++g_launches; }
-size_t w4a16_grouped_workspace_bytes(int E, int T, int) {
-    return T == 0 ? 0 : (size_t)(1 + 3 * w4a16_grouped_max_items(E, T)) * sizeof(int);
+// grouped: a workspace (the large path's offset terms) from a mean of 33 rows per expert
+size_t w4a16_grouped_workspace_bytes(int E, int T, int K) {
+    const int active = T < E ? T : E;
+    return active > 0 && T >= 33 * active ? (size_t)(K / 128) * (T + 128) * sizeof(float) : 0;
 }
 void launch_qgemm_w4a16_grouped(const uint16_t*, const int*, const uint32_t*, const uint16_t*, uint16_t*, int,
                                 int, int, int, void*, hipStream_t) { ++g_launches; }
 void launch_qgemm_w4a8_fp8(const uint8_t*, const float*, const uint32_t*, const uint16_t*, uint16_t*, int, int,
                            int, hipStream_t) { ++g_launches; }
 void launch_qgemm_w4a8_fp8_grouped(const uint8_t*, const float*, const int*, const uint32_t*, const uint16_t*,
-                                   uint16_t*, int, int, int, int, void*, hipStream_t) { ++g_launches; }
-size_t w4a8_grouped_dyn_workspace_bytes(int E, int T, int, int K) {
-    return w4a16_grouped_workspace_bytes(E, T, K) + (T > 16 ? (size_t)T * K + (size_t)T * 4 : 0);
+                                   uint16_t*, int, int, int, int, hipStream_t) { ++g_launches; }
+// grouped W4A8 on bf16 rows: fused (no workspace) below 17 rows, else codes and scales
+size_t w4a8_grouped_dyn_workspace_bytes(int, int T, int, int K) {
+    return T > 16 ? (size_t)T * K + (size_t)T * 4 : 0;
 }
 const char* w4a8_grouped_dyn_kernel_for(int, int, int, int) { return "stub"; }
 void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t*, const int*, const uint32_t*, const uint16_t*, uint16_t*,

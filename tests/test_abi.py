@@ -215,14 +215,16 @@ def test_grouped_entry_point_validates(lib):
     V, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     g = raw.qgemm_w4a16_grouped
     g.restype, g.argtypes = I, [V, V, V, V, V, I, I, I, I, V, S, V]
-    # E = 128 experts, T = 8 rows: one 16-row chunk per non-empty expert (at most
-    # 8) plus ceil(8 / 16) = 1 -> 9 items of 3 ints after the count
-    assert lib.w4a16_grouped_workspace_bytes(128, 8, 1536, 2048) == (1 + 3 * 9) * 4
+    # few rows per expert (E = 128, T = 8): no workspace; a mean of 64 rows per
+    # expert (E = 8, T = 512) runs the large path, whose workspace holds the
+    # fp32 offset terms of every 128-row group of each (padded) routed row
+    assert lib.w4a16_grouped_workspace_bytes(128, 8, 1536, 2048) == 0
     assert lib.w4a16_grouped_workspace_bytes(128, 0, 1536, 2048) == 0
     assert lib.w4a16_grouped_workspace_bytes(0, 8, 1536, 2048) == 0          # invalid E
-    need = lib.w4a16_grouped_workspace_bytes(128, 8, 1536, 2048)
+    need = lib.w4a16_grouped_workspace_bytes(8, 512, 1536, 2048)
+    assert need >= 16 * 512 * 4 and need % 256 == 0
     args = lambda **k: [k.get("a", FAKE), k.get("off", FAKE), k.get("w", FAKE), k.get("s", FAKE),
-                        k.get("y", FAKE), k.get("E", 128), k.get("T", 8), k.get("N", 1536),
+                        k.get("y", FAKE), k.get("E", 8), k.get("T", 512), k.get("N", 1536),
                         k.get("K", 2048), k.get("ws", FAKE), k.get("wsb", need), None]
     assert g(*args(E=0)) == QG_ERR_SHAPE
     assert g(*args(E=1025)) == QG_ERR_SHAPE
@@ -233,6 +235,7 @@ def test_grouped_entry_point_validates(lib):
     assert g(*args(ws=None)) == QG_ERR_NULL
     assert g(*args(off=FAKE + 2)) == QG_ERR_ALIGN
     assert g(*args(a=FAKE + 8)) == QG_ERR_ALIGN
+    assert g(*args(ws=FAKE + 2)) == QG_ERR_ALIGN
     assert g(*args(wsb=need - 4)) == QG_ERR_WORKSPACE
 
 

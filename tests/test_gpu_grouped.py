@@ -2,9 +2,11 @@
 
 Each expert's output rows: max |err| <= 2e-2 x RMS of that expert's fp64
 oracle rows.  Covers ragged and empty experts, the three row-chunk sizes,
-one expert owning every row, the Qwen3-30B-A3B expert shapes with 128 experts
-under seeded top-8 routing, repeat determinism, and malformed offsets staying
-inside the output."""
+one expert owning every row, up to 1000 experts (several per lane of the
+in-kernel work-item derivation), the Qwen3-30B-A3B expert shapes with 128
+experts under seeded top-8 routing, repeat determinism, and malformed offsets
+(clamped, or overlapping so that items past the grid's bound are dropped)
+staying inside the output."""
 import numpy as np
 import pytest
 import torch
@@ -57,6 +59,35 @@ def test_grouped_ragged(ops, sizes, K, N):
     a = synth.activations(T, K, seed=T + K)
     y, _ = _run(ops, w_list, a, offsets)
     _check(y, a, offsets, w_list)
+
+
+def skewed_sizes(E, T, seed):
+    """T routed rows over E experts: a skewed share per expert, about a third
+    of the experts without rows."""
+    rng = np.random.default_rng(seed)
+    p = rng.random(E) ** 3
+    p[rng.random(E) < 0.3] = 0.0
+    p[rng.integers(E)] += 1e-3
+    return rng.multinomial(T, p / p.sum())
+
+
+# E = 1000: 16 experts per lane of the work-item derivation; E = 300 and 65:
+# the last lanes partly or wholly empty; 16-row items, then the large tile
+@pytest.mark.parametrize("E,T,K,N", [(1000, 600, 128, 16), (300, 2000, 128, 32), (65, 64, 256, 64),
+                                     (300, 12000, 128, 272)])
+def test_grouped_many_experts(ops, E, T, K, N):
+    announce(f"qgemm_w4a16_grouped many experts E={E} T={T} K={K} N={N}")
+    sizes = skewed_sizes(E, T, seed=E + T)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    w_list = [synth.weights(K, N, seed=1000 + e) for e in range(E)]
+    a = synth.activations(T, K, seed=E)
+    gw = ops.GroupedInt4Weight.from_bf16(torch.stack([dev_bf16(x) for x in w_list]))
+    y_dev = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    gw(dev_bf16(a), torch.from_numpy(offsets).cuda(), out=y_dev)
+    y = host_bits16(y_dev)
+    assert not np.any(np.all(y == 0x40e0, axis=1)), "rows left unwritten"
+    nonempty = [e for e in range(E) if sizes[e] > 0]
+    _check(y, a, offsets, w_list, nonempty[:: max(1, len(nonempty) // 8)] + [nonempty[-1]])
 
 
 @pytest.mark.parametrize("B", [1, 16, 64, 256, 1024])
@@ -116,3 +147,22 @@ def test_grouped_malformed_offsets_stay_in_bounds(ops):
     assert torch.all(y[T:] == 7.0)
     # expert 0 owns [0, 24) after clamping: its rows are well defined
     _check(host_bits16(y[:T]), synth.activations(T, K, seed=6), np.array([0, T, T, T, T]), w_list, [0])
+
+
+@pytest.mark.parametrize("T", [64, 512])
+def test_grouped_overlapping_offsets_drop_items(ops, T):
+    """Offsets that go back to 0: experts 0, 2, 4 and 6 each own all T rows, so
+    the call has four times the items of a well-formed one and the items past
+    the grid's bound min(E, T) + ceil(T / R) are dropped (16-row items at
+    T = 64, the large tile at 512).  The call completes inside the output."""
+    announce(f"qgemm_w4a16_grouped overlapping offsets T={T}")
+    K, N, E = 256, 256, 8
+    w_list = [synth.weights(K, N, seed=500 + e) for e in range(E)]
+    gw = ops.GroupedInt4Weight.from_bf16(torch.stack([dev_bf16(x) for x in w_list]))
+    a = dev_bf16(synth.activations(T, K, seed=8))
+    y = torch.full((T + 8, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    bad = torch.tensor([0, T, 0, T, 0, T, 0, T, T], dtype=torch.int32, device="cuda")
+    gw(a, bad, out=y[:T])
+    torch.cuda.synchronize()
+    assert torch.all(y[T:] == 7.0)
+    assert torch.all(torch.isfinite(y[:T].float()))

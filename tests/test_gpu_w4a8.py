@@ -119,3 +119,31 @@ def test_w4a8_grouped_qwen3_shapes(ops, B, j):
         r0, r1 = offsets[e], offsets[e + 1]
         ref = w4a8.grouped_gemm_ref(qa, sa, offsets, {e: q4.quantize(host_bits16(w[e]))})[e]
         assert_close_rms(y[r0:r1], ref, what=f"w4a8 qwen3 B={B} expert {e}")
+
+
+# several experts per lane of the work-item derivation (E = 1000 and 300):
+# 16-row items, the quantization inside the call (fewer than 48 rows), and
+# the large tile
+@pytest.mark.parametrize("E,T,K,N", [(1000, 600, 128, 16), (1000, 40, 128, 16), (300, 12000, 128, 272)])
+def test_w4a8_grouped_many_experts(ops, E, T, K, N):
+    announce(f"qgemm_w4a8_fp8_grouped(_dynamic) many experts E={E} T={T} K={K} N={N}")
+    rng = np.random.default_rng(E + T)
+    p = rng.random(E) ** 3
+    p[rng.random(E) < 0.3] = 0.0
+    p[rng.integers(E)] += 1e-3
+    sizes = rng.multinomial(T, p / p.sum())
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    w_list = [synth.weights(K, N, seed=2000 + e) for e in range(E)]
+    a = synth.activations(T, K, seed=E + 1)
+    gw = ops.GroupedInt4Weight.from_bf16(torch.stack([dev_bf16(x) for x in w_list]))
+    off = torch.from_numpy(offsets).cuda()
+    qa_d, sa_d = ops.quantize_activations(dev_bf16(a))
+    y = host_bits16(gw.w4a8(qa_d, sa_d, off))
+    y_dyn = host_bits16(gw.w4a8_dynamic(dev_bf16(a), off))
+    assert np.array_equal(y_dyn, y)
+    qa, sa = f8.quant_act_per_token(a)
+    nonempty = [e for e in range(E) if sizes[e] > 0]
+    for e in nonempty[:: max(1, len(nonempty) // 8)] + [nonempty[-1]]:
+        r0, r1 = offsets[e], offsets[e + 1]
+        ref = w4a8.grouped_gemm_ref(qa, sa, offsets, {e: q4.quantize(w_list[e])})[e]
+        assert_close_rms(y[r0:r1], ref, what=f"w4a8 E={E} expert {e}")

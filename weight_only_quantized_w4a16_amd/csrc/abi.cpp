@@ -161,11 +161,16 @@ qg_status qgemm_w4a16_grouped(const uint16_t* a_bf16, const int32_t* offsets,
                               qg_stream stream) {
     if (!grouped_ok(E, T, N, K)) return QG_ERR_SHAPE;
     if (T == 0) return QG_OK;
-    if (!a_bf16 || !offsets || !packed || !scales || !y_bf16 || !workspace) return QG_ERR_NULL;
+    if (!a_bf16 || !offsets || !packed || !scales || !y_bf16) return QG_ERR_NULL;
     if (!aligned(a_bf16, 16) || !aligned(offsets, 4) || !aligned(packed, 16) ||
-        !aligned(scales, 4) || !aligned(y_bf16, 16) || !aligned(workspace, 4))
+        !aligned(scales, 4) || !aligned(y_bf16, 16))
         return QG_ERR_ALIGN;
-    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T, K)) return QG_ERR_WORKSPACE;
+    const size_t need = qg::w4a16_grouped_workspace_bytes(E, T, K);
+    if (need > 0) {
+        if (!workspace) return QG_ERR_NULL;
+        if (workspace_bytes < need) return QG_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return QG_ERR_ALIGN;
+    }
     qg::launch_qgemm_w4a16_grouped(a_bf16, offsets, packed, scales, y_bf16, E, T, N, K, workspace,
                                    as_stream(stream));
     return launched();
@@ -227,18 +232,16 @@ qg_status qgemm_w4a8_fp8(const uint8_t* a_e4m3, const float* a_scale, const uint
 
 qg_status qgemm_w4a8_fp8_grouped(const uint8_t* a_e4m3, const float* a_scale, const int32_t* offsets,
                                  const uint32_t* packed, const uint16_t* scales, uint16_t* y_bf16,
-                                 int E, int T, int N, int K, void* workspace, size_t workspace_bytes,
+                                 int E, int T, int N, int K, void* /*workspace*/, size_t /*workspace_bytes*/,
                                  qg_stream stream) {
     if (!grouped_ok(E, T, N, K)) return QG_ERR_SHAPE;
     if (T == 0) return QG_OK;
-    if (!a_e4m3 || !a_scale || !offsets || !packed || !scales || !y_bf16 || !workspace)
-        return QG_ERR_NULL;
+    if (!a_e4m3 || !a_scale || !offsets || !packed || !scales || !y_bf16) return QG_ERR_NULL;
     if (!aligned(a_e4m3, 16) || !aligned(a_scale, 4) || !aligned(offsets, 4) || !aligned(packed, 16) ||
-        !aligned(scales, 4) || !aligned(y_bf16, 16) || !aligned(workspace, 4))
+        !aligned(scales, 4) || !aligned(y_bf16, 16))
         return QG_ERR_ALIGN;
-    if (workspace_bytes < qg::w4a16_grouped_workspace_bytes(E, T, K)) return QG_ERR_WORKSPACE;
     qg::launch_qgemm_w4a8_fp8_grouped(a_e4m3, a_scale, offsets, packed, scales, y_bf16, E, T, N, K,
-                                      workspace, as_stream(stream));
+                                      as_stream(stream));
     return launched();
 }
 
@@ -257,11 +260,16 @@ qg_status qgemm_w4a8_fp8_grouped_dynamic(const uint16_t* a_bf16, const int32_t* 
                                          void* workspace, size_t workspace_bytes, qg_stream stream) {
     if (!grouped_ok(E, T, N, K)) return QG_ERR_SHAPE;
     if (T == 0) return QG_OK;
-    if (!a_bf16 || !offsets || !packed || !scales || !y_bf16 || !workspace) return QG_ERR_NULL;
+    if (!a_bf16 || !offsets || !packed || !scales || !y_bf16) return QG_ERR_NULL;
     if (!aligned(a_bf16, 16) || !aligned(offsets, 4) || !aligned(packed, 16) || !aligned(scales, 4) ||
-        !aligned(y_bf16, 16) || !aligned(workspace, 16))
+        !aligned(y_bf16, 16))
         return QG_ERR_ALIGN;
-    if (workspace_bytes < qg::w4a8_grouped_dyn_workspace_bytes(E, T, N, K)) return QG_ERR_WORKSPACE;
+    const size_t need = qg::w4a8_grouped_dyn_workspace_bytes(E, T, N, K);
+    if (need > 0) {
+        if (!workspace) return QG_ERR_NULL;
+        if (workspace_bytes < need) return QG_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QG_ERR_ALIGN;
+    }
     qg::launch_qgemm_w4a8_fp8_grouped_dyn(a_bf16, offsets, packed, scales, y_bf16, E, T, N, K, workspace,
                                           as_stream(stream));
     return launched();

@@ -213,6 +213,72 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// ---- expert-grouped work items ----------------------------------------------
+// An expert-grouped call (E experts, T routed rows, expert e owning rows
+// offsets[e] .. offsets[e+1] - 1) is cut into work items of at most R rows:
+// each expert's rows in chunks of R, the items numbered in expert order and in
+// row order within an expert.  Offsets are clamped into [0, T] with
+// r0 <= r1 per expert, so malformed offsets stay in bounds.  The GEMM grid
+// holds one workgroup row per item up to the bound min(E, T) + ceil(T / R),
+// which well-formed offsets never exceed; items past it are dropped.
+//
+// Every wave finds the item `it` of its workgroup on its own, with no launch
+// and no memory round trip before the GEMM: the experts are taken 64 at a
+// time, expert 64 j + lane on lane `lane` (one coalesced pair of offset loads
+// per block, the next block's in flight while this one is counted); a wave
+// prefix sum of the blocks' chunk counts numbers the items, and the block and
+// lane holding item `it` supply (expert, first row, rows), read into scalar
+// registers.  All waves of a workgroup reach the same answer (measured:
+// cheaper than one wave deriving it and handing it over through LDS behind a
+// barrier).  false: fewer than it + 1 items (nothing to do).
+constexpr int GROUPED_MAX_E = 1024;
+
+struct GroupedItem {
+    int e, r0, rows;
+};
+
+template <int R>
+__device__ __forceinline__ bool grouped_item(const int* __restrict__ offsets, int E, int T, int it,
+                                             GroupedItem& item) {
+    const int lane = threadIdx.x & 63;
+    const int nblk = (E + 63) >> 6;
+    int a = offsets[min(lane, E)];
+    int b = offsets[min(lane + 1, E)];
+    int carry = 0;                                   // items of the blocks before
+    for (int j = 0; j < nblk; ++j) {
+        const int e = 64 * j + lane;
+        int na = 0, nb = 0;
+        if (j + 1 < nblk) {
+            na = offsets[min(e + 64, E)];
+            nb = offsets[min(e + 65, E)];
+        }
+        const int lo = e < E ? min(max(a, 0), T) : 0;
+        const int hi = e < E ? min(max(b, lo), T) : 0;
+        const int c = (hi - lo + R - 1) / R;
+        int incl = c;                                // inclusive prefix over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        incl += carry;
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (it < total) {                            // uniform; carry <= it, so one lane owns it
+            const int first = incl - c;
+            const int src = __builtin_ctzll(__ballot(it >= first && it < incl));
+            const int r0 = lo + (it - first) * R;
+            item.e = __builtin_amdgcn_readlane(e, src);
+            item.r0 = __builtin_amdgcn_readlane(r0, src);
+            item.rows = __builtin_amdgcn_readlane(min(R, hi - r0), src);
+            return true;
+        }
+        carry = total;
+        a = na;
+        b = nb;
+    }
+    return false;
+}
+
 // Offset terms of a staged activation slice: corr[g * 16 + m] = -136 * (sum of
 // row m's 128 activations of group g).  Above 8 rows on the MFMA: the staged
 // fragments (arow: this lane's row min(col, M-1), k-quarter kq) times a B

@@ -54,8 +54,6 @@ void launch_qgemm_w4a16(const uint16_t* a, const uint32_t* packed, const uint16_
 constexpr int kGroupedMaxExperts = 1024;
 int w4a16_grouped_max_items(int E, int T);
 int w4a16_grouped_rows_per_item(int E, int T);
-void launch_grouped_items(const int* offsets, int E, int T, int R, int max_items, int* items,
-                          hipStream_t s);
 size_t w4a16_grouped_workspace_bytes(int E, int T, int K);
 void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
                                 const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
@@ -66,9 +64,9 @@ void launch_qgemm_w4a8_fp8(const uint8_t* qa, const float* sa, const uint32_t* w
                            const uint16_t* sc, uint16_t* y, int M, int N, int K, hipStream_t s);
 void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int* offsets,
                                    const uint32_t* wq, const uint16_t* sc, uint16_t* y, int E, int T,
-                                   int N, int K, void* ws, hipStream_t s);
+                                   int N, int K, hipStream_t s);
 // bf16 routed rows in: the quantization inside the grouped GEMM for small
-// items, else quant_act_per_token into the workspace (after the items) first
+// items, else quant_act_per_token into the workspace first
 size_t w4a8_grouped_dyn_workspace_bytes(int E, int T, int N, int K);
 const char* w4a8_grouped_dyn_kernel_for(int E, int T, int N, int K);
 void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, const uint32_t* wq,

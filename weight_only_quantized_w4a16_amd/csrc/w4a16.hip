@@ -390,71 +390,24 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a16_small_m_kernel(
 // routed rows arrive grouped by expert, expert e owning rows
 // [offsets[e], offsets[e+1]), and the E expert weights lie back to back in
 // the native layout.  Work items are the R-row chunks of the non-empty
-// experts, numbered expert by expert.  A one-wave pass reads the offsets
-// (each lane loads those of its 16 experts, all in flight at once), counts
-// the chunks, numbers them with a wave prefix sum and writes the items
-// (expert, first row, rows) to the workspace; the GEMM grid then takes one
-// item per blockIdx.y (scalar loads) and runs the small-M tile over that
-// expert's weight.  Experts without rows cost nothing, and an expert's
-// weights are streamed once per chunk.  Offsets are clamped into [0, T]
-// (r0 <= r1), so malformed offsets stay in bounds; items past the bound
-// min(E, T) + ceil(T / R) are dropped.
+// experts, numbered expert by expert; blockIdx.y is the item, which every
+// wave derives from the offsets itself (grouped_item), and the small-M tile
+// runs over that expert's weight.  Experts without rows cost nothing, and an
+// expert's weights are streamed once per chunk.
 // ---------------------------------------------------------------------------
-constexpr int GROUPED_MAX_E = 1024;
-
-__global__ __launch_bounds__(64) void grouped_items_kernel(const int* __restrict__ offsets, int E,
-                                                           int T, int R, int max_items,
-                                                           int* __restrict__ items) {
-    constexpr int PER = GROUPED_MAX_E / 64;          // experts per lane
-    const int lane = threadIdx.x;
-    const int e0 = lane * PER;
-    int bound[PER + 1];
-#pragma unroll
-    for (int i = 0; i <= PER; ++i) bound[i] = offsets[min(e0 + i, E)];
-    int r0[PER], r1[PER], cnt[PER];
-    int local = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const bool ok = e0 + i < E;
-        r0[i] = ok ? min(max(bound[i], 0), T) : 0;
-        r1[i] = ok ? min(max(bound[i + 1], r0[i]), T) : 0;
-        cnt[i] = (r1[i] - r0[i] + R - 1) / R;
-        local += cnt[i];
-    }
-    int incl = local;                                // inclusive prefix over the lanes
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
-    }
-    int first = incl - local;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        for (int c = 0; c < cnt[i]; ++c) {
-            const int it = first + c;
-            if (it >= max_items) break;
-            items[1 + 3 * it] = e0 + i;
-            items[2 + 3 * it] = r0[i] + c * R;
-            items[3 + 3 * it] = min(R, r1[i] - r0[i] - c * R);
-        }
-        first += cnt[i];
-    }
-    if (lane == 63) items[0] = min(incl, max_items);
-}
+static_assert(GROUPED_MAX_E == kGroupedMaxExperts, "expert bound of the item derivation");
 
 template <int MT, int CT, int NWAVE, int U, bool PIPE>
 __global__ __launch_bounds__(NWAVE * 64) void w4a16_grouped_kernel(
-    const uint16_t* __restrict__ a, const int* __restrict__ items, const uint32_t* __restrict__ wq,
-    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N, int K) {
-    const int it = blockIdx.y;
-    if (it >= items[0]) return;
-    const int e = items[1 + 3 * it];
-    const int row0 = items[2 + 3 * it];
-    const int rows = items[3 + 3 * it];
+    const uint16_t* __restrict__ a, const int* __restrict__ offsets, int E, int T,
+    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N,
+    int K) {
+    GroupedItem item;
+    if (!grouped_item<16 * MT>(offsets, E, T, blockIdx.y, item)) return;
     const size_t words = (size_t)(K / 8) * N;        // one expert's packed words
     const size_t nsc = (size_t)(K / 128) * N;        // one expert's scales
-    small_m_tile<MT, CT, NWAVE, U, PIPE>(a + (size_t)row0 * K, wq + e * words, sc + e * nsc,
-                                         y + (size_t)row0 * N, rows, N, K, blockIdx.x * CT);
+    small_m_tile<MT, CT, NWAVE, U, PIPE>(a + (size_t)item.r0 * K, wq + item.e * words, sc + item.e * nsc,
+                                         y + (size_t)item.r0 * N, item.rows, N, K, blockIdx.x * CT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1065,18 +1018,15 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
 // padded so that a 128-row read from any item start stays inside).
 template <int NS, int NB, int BM>
 __global__ __launch_bounds__(512) void w4a16_grouped_large_kernel(
-    const uint16_t* __restrict__ a, const int* __restrict__ items, const uint32_t* __restrict__ wq,
-    const uint16_t* __restrict__ sc, const float* __restrict__ corr, uint16_t* __restrict__ y,
-    int Tp, int N, int K) {
-    const int it = blockIdx.y;
-    if (it >= items[0]) return;
-    const int e = items[1 + 3 * it];
-    const int r0 = items[2 + 3 * it];
-    const int rows = items[3 + 3 * it];
+    const uint16_t* __restrict__ a, const int* __restrict__ offsets, int E, int T,
+    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, const float* __restrict__ corr,
+    uint16_t* __restrict__ y, int Tp, int N, int K) {
+    GroupedItem item;
+    if (!grouped_item<BM>(offsets, E, T, blockIdx.y, item)) return;   // uniform: the whole workgroup leaves
     const size_t words = (size_t)(K / 8) * N;
     const size_t nsc = (size_t)(K / 128) * N;
-    large_m_tile<NS, NB, BM>(a + (size_t)r0 * K, wq + e * words, sc + e * nsc, corr + r0,
-                         y + (size_t)r0 * N, rows, Tp, N, K, 1, nullptr, nullptr, gridDim.x, 0,
+    large_m_tile<NS, NB, BM>(a + (size_t)item.r0 * K, wq + item.e * words, sc + item.e * nsc, corr + item.r0,
+                         y + (size_t)item.r0 * N, item.rows, Tp, N, K, 1, nullptr, nullptr, gridDim.x, 0,
                          xcd_tile(blockIdx.x, gridDim.x));
 }
 
@@ -1222,31 +1172,29 @@ static size_t grouped_corr_bytes(int E, int T, int K) {
     return ((size_t)(K / 128) * grouped_tp(T) * sizeof(float) + 255) / 256 * 256;
 }
 
-// corr (large path only) then the items; the item bound of the small tiles is
-// the larger one, so the same size serves every grouped path
+// the offset terms of the large path; the small tiles need none
 size_t w4a16_grouped_workspace_bytes(int E, int T, int K) {
     if (T == 0) return 0;
-    return grouped_corr_bytes(E, T, K) + (size_t)(1 + 3 * grouped_max_items(E, T)) * sizeof(int);
+    return grouped_corr_bytes(E, T, K);
 }
 
+struct GroupedArgs {
+    const int* offsets;
+    int E, T, max_items;
+};
+
 template <int MT, int CT>
-static void launch_grouped_mt(const uint16_t* a, const int* items, const uint32_t* wq,
-                              const uint16_t* sc, uint16_t* y, int N, int K, int max_items,
-                              hipStream_t s) {
+static void launch_grouped_mt(const uint16_t* a, const GroupedArgs& g, const uint32_t* wq,
+                              const uint16_t* sc, uint16_t* y, int N, int K, hipStream_t s) {
     constexpr int NWAVE = QG_GR_NWAVE;
     constexpr int U = MT == 1 ? QG_SM_U : 1;
     constexpr bool PIPE = MT <= 2 && CT <= 2;
-    hipLaunchKernelGGL((w4a16_grouped_kernel<MT, CT, NWAVE, U, PIPE>), dim3(N / 16 / CT, max_items),
-                       dim3(NWAVE * 64), 0, s, a, items, wq, sc, y, N, K);
+    hipLaunchKernelGGL((w4a16_grouped_kernel<MT, CT, NWAVE, U, PIPE>), dim3(N / 16 / CT, g.max_items),
+                       dim3(NWAVE * 64), 0, s, a, g.offsets, g.E, g.T, wq, sc, y, N, K);
 }
 
 int w4a16_grouped_rows_per_item(int E, int T) { return 16 * grouped_mt(E, T); }
 
-void launch_grouped_items(const int* offsets, int E, int T, int R, int max_items, int* items,
-                          hipStream_t s) {
-    hipLaunchKernelGGL(grouped_items_kernel, dim3(1), dim3(64), 0, s, offsets, E, T, R, max_items,
-                       items);
-}
 
 void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
                                 const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,
@@ -1255,25 +1203,22 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
         const int Tp = grouped_tp(T);
         const int G = K / 128;
         float* corr = static_cast<float*>(ws);
-        int* items = reinterpret_cast<int*>(static_cast<char*>(ws) + grouped_corr_bytes(E, T, K));
         constexpr int R = QG_GR_BM;              // rows per item = tile rows
         const int max_items = (T < E ? T : E) + (T + R - 1) / R;
         const size_t n = (size_t)G * Tp * 16;      // 16 lanes per (group, row)
         hipLaunchKernelGGL(w4a16_group_rowsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            a, T, Tp, K, corr);
-        launch_grouped_items(offsets, E, T, R, max_items, items, s);
         if (N >= 1024)
             hipLaunchKernelGGL((w4a16_grouped_large_kernel<QG_LM_NS, 2, R>), dim3((N + 255) / 256, max_items),
-                               dim3(512), 0, s, a, items, wq, sc, corr, y, Tp, N, K);
+                               dim3(512), 0, s, a, offsets, E, T, wq, sc, corr, y, Tp, N, K);
         else
             hipLaunchKernelGGL((w4a16_grouped_large_kernel<QG_LM_NS, 1, R>), dim3((N + 127) / 128, max_items),
-                               dim3(512), 0, s, a, items, wq, sc, corr, y, Tp, N, K);
+                               dim3(512), 0, s, a, offsets, E, T, wq, sc, corr, y, Tp, N, K);
         return;
     }
     const int MT = grouped_mt(E, T);
     const int max_items = grouped_max_items(E, T);
-    int* items = static_cast<int*>(ws);
-    launch_grouped_items(offsets, E, T, 16 * MT, max_items, items, s);
+    const GroupedArgs g{offsets, E, T, max_items};
     const int NT = N / 16;
     int ct = QG_GR_CT ? QG_GR_CT : small_ct(NT);
     while (NT % ct) ct >>= 1;
@@ -1282,10 +1227,10 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
         // the LDS reduction holds NWAVE * CT * MT KiB
         constexpr bool fits8 = QG_GR_NWAVE * 8 * M_T <= 64;
         if (ct == 8 && fits8)
-            launch_grouped_mt<M_T, fits8 ? 8 : 4>(a, items, wq, sc, y, N, K, max_items, s);
-        else if (ct >= 4) launch_grouped_mt<M_T, 4>(a, items, wq, sc, y, N, K, max_items, s);
-        else if (ct == 2) launch_grouped_mt<M_T, 2>(a, items, wq, sc, y, N, K, max_items, s);
-        else              launch_grouped_mt<M_T, 1>(a, items, wq, sc, y, N, K, max_items, s);
+            launch_grouped_mt<M_T, fits8 ? 8 : 4>(a, g, wq, sc, y, N, K, s);
+        else if (ct >= 4) launch_grouped_mt<M_T, 4>(a, g, wq, sc, y, N, K, s);
+        else if (ct == 2) launch_grouped_mt<M_T, 2>(a, g, wq, sc, y, N, K, s);
+        else              launch_grouped_mt<M_T, 1>(a, g, wq, sc, y, N, K, s);
     };
     if (MT == 1) go(ic<1>{});
     else if (MT == 2) go(ic<2>{});

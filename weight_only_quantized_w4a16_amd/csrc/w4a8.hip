@@ -39,7 +39,6 @@ __device__ __forceinline__ void w4a8_tile_src(ALoad aload, AScale ascale, const 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
-    const int q = lane >> 4;
     const int g_begin = (G * wave) / NWAVE;
     const int g_end = (G * (wave + 1)) / NWAVE;
 
@@ -173,22 +172,19 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a8_kernel(const uint8_t* __restr
                              min(16 * MT, M - row0), N, K, blockIdx.x * CT);
 }
 
-// expert-grouped: one work item (expert, first row, rows) of the W4A16 grouped
-// path's item list per blockIdx.y
+// expert-grouped: one work item (expert, first row, rows) of 16 MT rows per
+// blockIdx.y, as the grouped W4A16 path numbers them (grouped_item)
 template <int MT, int CT, int NWAVE>
 __global__ __launch_bounds__(NWAVE * 64) void w4a8_grouped_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const int* __restrict__ items,
-    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const int* __restrict__ offsets, int E,
+    int T, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
     int N, int K) {
-    const int it = blockIdx.y;
-    if (it >= items[0]) return;
-    const int e = items[1 + 3 * it];
-    const int r0 = items[2 + 3 * it];
-    const int rows = items[3 + 3 * it];
+    GroupedItem item;
+    if (!grouped_item<16 * MT>(offsets, E, T, blockIdx.y, item)) return;
     const size_t words = (size_t)(K / 8) * N;
     const size_t nsc = (size_t)(K / 128) * N;
-    w4a8_tile<MT, CT, NWAVE>(qa + (size_t)r0 * K, sa + r0, wq + e * words, sc + e * nsc,
-                             y + (size_t)r0 * N, rows, N, K, blockIdx.x * CT);
+    w4a8_tile<MT, CT, NWAVE>(qa + (size_t)item.r0 * K, sa + item.r0, wq + item.e * words, sc + item.e * nsc,
+                             y + (size_t)item.r0 * N, item.rows, N, K, blockIdx.x * CT);
 }
 
 // ---------------------------------------------------------------------------
@@ -206,15 +202,16 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a8_grouped_kernel(
 // ---------------------------------------------------------------------------
 template <int MT, int CT, int NWAVE, int CPL>
 __global__ __launch_bounds__(NWAVE * 64) void w4a8_grouped_dyn_kernel(
-    const uint16_t* __restrict__ a, const int* __restrict__ items, const uint32_t* __restrict__ wq,
-    const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N, int K) {
+    const uint16_t* __restrict__ a, const int* __restrict__ offsets, int E, int T,
+    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N,
+    int K) {
     extern __shared__ __attribute__((aligned(16))) unsigned char codes[];   // [rows][K + 16]
     __shared__ float srow[16 * MT];
-    const int it = blockIdx.y;
-    if (it >= items[0]) return;
-    const int e = items[1 + 3 * it];
-    const int r0 = items[2 + 3 * it];
-    const int rows = items[3 + 3 * it];
+    GroupedItem item;
+    if (!grouped_item<16 * MT>(offsets, E, T, blockIdx.y, item)) return;
+    const int e = item.e;
+    const int r0 = item.r0;
+    const int rows = item.rows;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rowb = K + 16;
@@ -292,8 +289,8 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a8_grouped_dyn_kernel(
 // ---------------------------------------------------------------------------
 template <int NS, int BM>
 __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const int* __restrict__ items,
-    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N,
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const int* __restrict__ offsets, int E,
+    int T, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N,
     int K) {
     constexpr int NTB = 16;                      // column tiles per workgroup (256 columns)
     constexpr int NI = 4;                        // column tiles per wave
@@ -316,11 +313,11 @@ __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
         else return S3x[0];
     };
 
-    const int it = blockIdx.y;
-    if (it >= items[0]) return;                  // uniform: the whole workgroup leaves
-    const int e = items[1 + 3 * it];
-    const int r0 = items[2 + 3 * it];
-    const int rows = items[3 + 3 * it];
+    GroupedItem item;
+    if (!grouped_item<BM>(offsets, E, T, blockIdx.y, item)) return;   // uniform: the whole workgroup leaves
+    const int e = item.e;
+    const int r0 = item.r0;
+    const int rows = item.rows;
     const int G = K >> 7;
     const int NT = N >> 4;
     const int tid = threadIdx.x;
@@ -510,23 +507,18 @@ void launch_qgemm_w4a8_fp8(const uint8_t* qa, const float* sa, const uint32_t* w
 
 void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int* offsets,
                                    const uint32_t* wq, const uint16_t* sc, uint16_t* y, int E, int T,
-                                   int N, int K, void* ws, hipStream_t s) {
+                                   int N, int K, hipStream_t s) {
     const int NT = N / 16;
     if (w4a8_grouped_large(E, T, N)) {
-        // many rows per expert: 64-row items on the large tile (the workspace
-        // of qgemm_w4a16_grouped holds at least min(E, T) + ceil(T / 64) items)
+        // many rows per expert: 64-row items on the large tile
         constexpr int R = QG_W4A8_LARGE_BM;
         const int max_items = (T < E ? T : E) + (T + R - 1) / R;
-        int* items = static_cast<int*>(ws);
-        launch_grouped_items(offsets, E, T, R, max_items, items, s);
         hipLaunchKernelGGL((w4a8_grouped_large_kernel<QG_W4A8_LARGE_NS, R>), dim3((N + 255) / 256, max_items),
-                           dim3(512), 0, s, qa, sa, items, wq, sc, y, N, K);
+                           dim3(512), 0, s, qa, sa, offsets, E, T, wq, sc, y, N, K);
         return;
     }
     const int R = w4a16_grouped_rows_per_item(E, T);
     const int max_items = w4a16_grouped_max_items(E, T);
-    int* items = static_cast<int*>(ws);
-    launch_grouped_items(offsets, E, T, R, max_items, items, s);
     const int CT = w4a8_ct(NT);
     if (T >= QG_W4A8_ONE_WAVE_MIN_T) {
         // many routed rows: one wave per workgroup over the whole K (no K split,
@@ -535,15 +527,15 @@ void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int
         // handful of workgroups, is 26 % slower this way)
         w4a8_dispatch(R / 16, CT, [&](auto mt, auto ct) {
             hipLaunchKernelGGL((w4a8_grouped_kernel<decltype(mt)::value, decltype(ct)::value, 1>),
-                               dim3(NT / decltype(ct)::value, max_items), dim3(64), 0, s, qa, sa, items, wq,
-                               sc, y, N, K);
+                               dim3(NT / decltype(ct)::value, max_items), dim3(64), 0, s, qa, sa, offsets,
+                               E, T, wq, sc, y, N, K);
         });
         return;
     }
     w4a8_dispatch(R / 16, CT, [&](auto mt, auto ct) {
         hipLaunchKernelGGL((w4a8_grouped_kernel<decltype(mt)::value, decltype(ct)::value, W4A8_NWAVE>),
                            dim3(NT / decltype(ct)::value, max_items), dim3(W4A8_NWAVE * 64), 0, s, qa, sa,
-                           items, wq, sc, y, N, K);
+                           offsets, E, T, wq, sc, y, N, K);
     });
 }
 
@@ -569,12 +561,10 @@ static bool w4a8_grouped_dyn_fused(int E, int T, int N, int K) {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// the items (and what the grouped W4A16 path keeps there) first; unfused: the
-// codes and scales of the separate quantization after them
+// fused: none; unfused: the codes and scales of the separate quantization
 size_t w4a8_grouped_dyn_workspace_bytes(int E, int T, int N, int K) {
-    const size_t items = w4a16_grouped_workspace_bytes(E, T, K);
-    if (T == 0 || w4a8_grouped_dyn_fused(E, T, N, K)) return items;
-    return align256(items) + align256((size_t)T * K) + align256((size_t)T * 4);
+    if (T == 0 || w4a8_grouped_dyn_fused(E, T, N, K)) return 0;
+    return align256((size_t)T * K) + align256((size_t)T * 4);
 }
 
 const char* w4a8_grouped_dyn_kernel_for(int E, int T, int N, int K) {
@@ -588,19 +578,15 @@ void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, co
                                        const uint16_t* sc, uint16_t* y, int E, int T, int N, int K, void* ws,
                                        hipStream_t s) {
     if (!w4a8_grouped_dyn_fused(E, T, N, K)) {
-        char* base = static_cast<char*>(ws);
-        const size_t q_off = align256(w4a16_grouped_workspace_bytes(E, T, K));
-        uint8_t* q = reinterpret_cast<uint8_t*>(base + q_off);
-        float* sa = reinterpret_cast<float*>(base + q_off + align256((size_t)T * K));
+        uint8_t* q = static_cast<uint8_t*>(ws);
+        float* sa = reinterpret_cast<float*>(q + align256((size_t)T * K));
         launch_quant_act_per_token(a, T, K, q, sa, s);
-        launch_qgemm_w4a8_fp8_grouped(q, sa, offsets, wq, sc, y, E, T, N, K, ws, s);
+        launch_qgemm_w4a8_fp8_grouped(q, sa, offsets, wq, sc, y, E, T, N, K, s);
         return;
     }
     const int NT = N / 16;
     const int R = w4a16_grouped_rows_per_item(E, T);
     const int max_items = w4a16_grouped_max_items(E, T);
-    int* items = static_cast<int*>(ws);
-    launch_grouped_items(offsets, E, T, R, max_items, items, s);
     const int CT = w4a8_ct(NT);
     const size_t lds = (size_t)R * (K + 16);
     auto go = [&](auto mt, auto ct, auto nwave, auto cpl) {
@@ -610,7 +596,7 @@ void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, co
         allow_dynamic_lds(reinterpret_cast<const void*>(&w4a8_grouped_dyn_kernel<MT_, CT_, NW, CPL_>),
                           16 * MT_ * (512 * CPL_ + 16), lds_set);
         hipLaunchKernelGGL((w4a8_grouped_dyn_kernel<MT_, CT_, NW, CPL_>), dim3(NT / CT_, max_items),
-                           dim3(NW * 64), lds, s, a, items, wq, sc, y, N, K);
+                           dim3(NW * 64), lds, s, a, offsets, E, T, wq, sc, y, N, K);
     };
     auto by_cpl = [&](auto mt, auto ct, auto nwave) {
         switch (w4a8_dyn_cpl(K)) {

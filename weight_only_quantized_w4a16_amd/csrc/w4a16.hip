@@ -916,8 +916,11 @@ __device__ __forceinline__ void large_m_tile(
         load_all(s);
         __builtin_amdgcn_sched_barrier(0);
     });
+    // a wave whose rows all lie past M (the last row tile of a ragged M) only
+    // copies and synchronises: its SIMD partner then has the MFMA and VALU alone
+    const bool rows_live = m0 + wm * WROWS < M;
     for (int g = 0; g < G; g += NS)
-        static_for<NS>([&](auto s) { step(s, g + decltype(s)::value < G); });
+        static_for<NS>([&](auto s) { step(s, rows_live && g + decltype(s)::value < G); });
 
     if (S == 1) {
 #pragma unroll

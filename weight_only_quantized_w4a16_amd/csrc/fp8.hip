@@ -659,8 +659,11 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
         ++ld_kt;
         __builtin_amdgcn_sched_barrier(0);
     });
+    // a wave whose rows all lie past M (the last row tile of a ragged M) only
+    // copies and synchronises
+    const bool rows_live = m0 + wm * (BM / 2) < M;
     for (int kt = 0; kt < KT; kt += NS)
-        static_for<NS>([&](auto s) { step(s, kt + decltype(s)::value < KT); });
+        static_for<NS>([&](auto s) { step(s, rows_live && kt + decltype(s)::value < KT); });
 
     if (S == 1) {
 #pragma unroll

@@ -440,8 +440,10 @@ __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
         ++ld_g;
         __builtin_amdgcn_sched_barrier(0);
     });
+    // a wave whose rows all lie past the item's rows only copies and synchronises
+    const bool rows_live = wm * (BM / 2) < rows;
     for (int g = 0; g < G; g += NS)
-        static_for<NS>([&](auto st) { step(st, g + decltype(st)::value < G); });
+        static_for<NS>([&](auto st) { step(st, rows_live && g + decltype(st)::value < G); });
 
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {

@@ -76,10 +76,12 @@ def test_w4a8_llama3_shapes_sampled(ops, B, j, name, K, N):
     assert_close_rms(y[:, cols], w4a8.gemm_ref(qa, sa, codes, s), what=f"w4a8 {name} B={B}")
 
 
-# means of 23, 2.5 and 61 rows per non-empty expert: 16-, 32- and 64-row items;
-# from a mean of 33 rows and N >= 256 the 64-row items run on the large tile
-# (64 x 256, K through LDS stages): N = 272 leaves a last workgroup with one
-# 16-column tile, K = 640 five groups (not a multiple of the three stages)
+# means of 17, 2 and 44 routed rows per expert (T / min(E, T)): 32- and 16-row
+# items on the small tiles (N < 256), then, from a mean of 17 rows and
+# N >= 256, 64-row items on the large tile (64 x 256, K through LDS stages):
+# N = 272 leaves a last workgroup with one 16-column tile, K = 640 five groups
+# (not a multiple of the three stages); items of 1, 7 and 33 rows leave the
+# second row of waves without rows
 @pytest.mark.parametrize("sizes,K,N", [([0, 1, 17, 0, 40, 3, 70, 5], 256, 64),
                                        ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48),
                                        ([0, 65, 33, 0, 128, 7, 70], 384, 256),

@@ -470,7 +470,8 @@ constexpr int W4A8_NWAVE = 4;
 static int w4a8_ct(int NT) { return NT % 4 == 0 ? 4 : (NT % 2 == 0 ? 2 : 1); }
 
 #ifndef QG_W4A8_LARGE_MIN          // grouped: the large tile from this mean of rows per non-empty expert
-#define QG_W4A8_LARGE_MIN 33
+#define QG_W4A8_LARGE_MIN 17       // measured, ms small / large: mean 20 rows 5.60 / 5.40, 24 6.24 / 5.67,
+                                   // 28 7.19 / 5.87, 32 8.09 / 6.06
 #endif
 #ifndef QG_W4A8_LARGE_BM           // rows per item and tile of the grouped large path
 #define QG_W4A8_LARGE_BM 64

@@ -1525,7 +1525,11 @@ static int large_m_bm(int M, int N, int K) {
     const int tiles128 = (N + 128 * nb - 1) / (128 * nb) * ((M + LM_BM - 1) / LM_BM);
     const int cus = device_cu_count();
     const bool long_k = K / 128 >= QG_LM_SPLIT_MIN_G;
-    return (long_k ? 4 * tiles128 <= cus : 2 * tiles128 <= cus) ? 64 : LM_BM;
+    if (long_k ? 4 * tiles128 <= cus : 2 * tiles128 <= cus) return 64;
+    // short K, one round either way: a round of 64-row tiles is shorter (qkv at
+    // M = 256 / 272: 28 us on 192 tiles of 64 rows, 36 us on 144 of 128 rows)
+    const int tiles64 = (N + 128 * nb - 1) / (128 * nb) * ((M + 63) / 64);
+    return !long_k && tiles128 <= cus && tiles64 <= cus ? 64 : LM_BM;
 }
 
 static int large_m_nb(int M, int N, int bm) {

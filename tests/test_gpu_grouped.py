@@ -51,6 +51,8 @@ def _check(y, a_bits, offsets, w_list, experts=None):
     ([100, 60, 0], 384, 272),                          # mean 54 -> 128-row items; 60 rows: second half idle
     ([90, 33, 0, 65, 128], 128, 16),                   # mean 79 -> 128-row large-M items
     ([0, 0, 200, 0], 512, 272),                        # one expert owns every row (large-M)
+    ([5], 256, 48),                                    # a single expert, few rows
+    ([300], 256, 272),                                 # a single expert, 128-row items (last one 44 rows)
     ([300, 0, 129, 40, 7], 1024, 1040),                # large-M: multi-chunk expert, ragged N
 ])
 def test_grouped_ragged(ops, sizes, K, N):

@@ -149,3 +149,25 @@ def test_w4a8_grouped_many_experts(ops, E, T, K, N):
         r0, r1 = offsets[e], offsets[e + 1]
         ref = w4a8.grouped_gemm_ref(qa, sa, offsets, {e: q4.quantize(w_list[e])})[e]
         assert_close_rms(y[r0:r1], ref, what=f"w4a8 E={E} expert {e}")
+
+
+@pytest.mark.parametrize("T", [40, 64, 512])
+def test_w4a8_grouped_overlapping_offsets_drop_items(ops, T):
+    """Offsets that go back to 0 (experts 0, 2, 4 and 6 each own all T rows):
+    four times the items of well-formed offsets, the items past the grid's
+    bound dropped.  The two-call and the bf16-input entry points (quantization
+    inside the GEMM at 40 rows, on the large tile at 512) complete inside the
+    output."""
+    announce(f"qgemm_w4a8_fp8_grouped(_dynamic) overlapping offsets T={T}")
+    K, N, E = 256, 256, 8
+    gw = ops.GroupedInt4Weight.from_bf16(torch.stack([dev_bf16(synth.weights(K, N, seed=700 + e))
+                                                      for e in range(E)]))
+    a = dev_bf16(synth.activations(T, K, seed=9))
+    bad = torch.tensor([0, T, 0, T, 0, T, 0, T, T], dtype=torch.int32, device="cuda")
+    qa, sa = ops.quantize_activations(a)
+    for call in (lambda out: gw.w4a8(qa, sa, bad, out=out), lambda out: gw.w4a8_dynamic(a, bad, out=out)):
+        y = torch.full((T + 8, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        call(y[:T])
+        torch.cuda.synchronize()
+        assert torch.all(y[T:] == 7.0)
+        assert torch.all(torch.isfinite(y[:T].float()))

@@ -93,10 +93,11 @@ def test_qwen3_dynamic_equals_two_calls(ops, B, j):
 @pytest.mark.parametrize("sizes,K,N", [([0, 1, 17, 0, 3, 5], 256, 64), ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48),
                                        ([40, 0, 5], 1024, 272), ([0, 20, 25, 0], 2048, 64),
                                        ([0, 9, 33, 0, 16, 7], 1024, 272), ([0, 65, 33, 0, 128, 7, 70], 640, 272),
-                                       ([1, 2, 3], 4096, 64)])
+                                       ([1, 2, 3], 4096, 64), ([7], 512, 64), ([300], 256, 272)])
 def test_ragged_dynamic_equals_two_calls(ops, sizes, K, N):
     """Fused items of 1..16 rows and of up to 32 rows (an expert of 40 rows in two
-    items), then unfused: 65 routed rows, the large tile, rows of 4096."""
+    items), then unfused: 65 routed rows, the large tile, rows of 4096; a single
+    expert with few rows (fused) and with 300 (the large tile)."""
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     T = int(offsets[-1])
     E = len(sizes)

@@ -713,6 +713,9 @@ __global__ __launch_bounds__(256) void w4a16_group_rowsum_kernel(const uint16_t*
 // XCD's L2 instead of fetching it once per XCD.
 // ---------------------------------------------------------------------------
 constexpr int LM_BM = 128;
+#ifndef QG_LM_STAGGER              // 1: the two rows of waves scale their group sums half a step apart
+#define QG_LM_STAGGER 1
+#endif
 
 // The work of one workgroup: output tile `tile` (of `tiles`) of K slice `split`.
 // BM = 128 rows (two 32-row blocks per wave) or 64 (one block per wave: half
@@ -825,6 +828,22 @@ __device__ __forceinline__ void large_m_tile(
             for (int i = 0; i < 16; ++i) total[mi][bb][i] = 0.f;
 
     const Int4Unpacker unpack;
+    // Staggered scaling (two rows of waves): the second row of waves scales a
+    // group's sums into the total at the start of the next group step, the
+    // first row at the end of the step, so the two waves that share a SIMD run
+    // their scaling FMAs while the other one issues MFMAs.
+    constexpr bool STAGGER = QG_LM_STAGGER && WR == 2;
+    f32x16 acc[MI][NBW];
+    float sprev[NBW];
+    bool pend = false;                           // the second row: a group's sums await scaling
+    auto scale_into_total = [&](const float* sg) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int bb = 0; bb < NBW; ++bb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) total[mi][bb][i] = fmaf(sg[bb], acc[mi][bb][i], total[mi][bb][i]);
+    };
     auto step = [&](auto slot, bool live) {
         // every step issues NCOPY copies per thread (one more in wave 0): once
         // at most (NS - 2) steps' copies are outstanding this stage has landed;
@@ -846,6 +865,10 @@ __device__ __forceinline__ void large_m_tile(
 #pragma unroll
             for (int i = 0; i <= NCOPY; ++i) copy(Dst, gnext, i);
             return;
+        }
+        if (STAGGER && wm == 1 && pend) {
+            scale_into_total(sprev);
+            __builtin_amdgcn_sched_barrier(0);
         }
         const Stage& S = stage(slot);
         // 32-column block b of the wave = native tiles 4wn+2b, 4wn+2b+1; lane l
@@ -880,7 +903,6 @@ __device__ __forceinline__ void large_m_tile(
         // between them, its wave-0 branch would split the k-steps' MFMA chain
         // into two blocks that the scheduler cannot interleave across
         copy(Dst, gnext, NCOPY);
-        f32x16 acc[MI][NBW];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {            // 16-k steps of the group
             // the next stage's copies go out one per k-step, between the MFMAs,
@@ -904,12 +926,14 @@ __device__ __forceinline__ void large_m_tile(
                 for (int bb = 0; bb < NBW; ++bb)
                     acc[mi][bb] = mfma_bf16_32x32x16(af[mi], bfr[bb], j == 0 ? cinit[mi] : acc[mi][bb]);
         }
+        if (STAGGER && wm == 1) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int bb = 0; bb < NBW; ++bb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) total[mi][bb][i] = fmaf(scur[bb], acc[mi][bb][i], total[mi][bb][i]);
+            for (int bb = 0; bb < NBW; ++bb) sprev[bb] = scur[bb];
+            pend = true;
+        } else {
+            scale_into_total(scur);
+            if (STAGGER) __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     static_for<NS - 1>([&](auto s) {
@@ -921,6 +945,7 @@ __device__ __forceinline__ void large_m_tile(
     const bool rows_live = m0 + wm * WROWS < M;
     for (int g = 0; g < G; g += NS)
         static_for<NS>([&](auto s) { step(s, rows_live && g + decltype(s)::value < G); });
+    if (STAGGER && pend) scale_into_total(sprev);
 
     if (S == 1) {
 #pragma unroll

@@ -828,11 +828,12 @@ __device__ __forceinline__ void large_m_tile(
             for (int i = 0; i < 16; ++i) total[mi][bb][i] = 0.f;
 
     const Int4Unpacker unpack;
-    // Staggered scaling (two rows of waves): the second row of waves scales a
-    // group's sums into the total at the start of the next group step, the
-    // first row at the end of the step, so the two waves that share a SIMD run
-    // their scaling FMAs while the other one issues MFMAs.
-    constexpr bool STAGGER = QG_LM_STAGGER && WR == 2;
+    // Staggered scaling: waves 4..7 scale a group's sums into the total at the
+    // start of the next group step, waves 0..3 at the end of the step, so the
+    // two waves that share a SIMD (w and w + 4) run their scaling FMAs while
+    // the other one issues MFMAs.
+    constexpr bool STAGGER = QG_LM_STAGGER;
+    const bool late = wave >= 4;                 // the wave that scales at the next step's start
     f32x16 acc[MI][NBW];
     float sprev[NBW];
     bool pend = false;                           // the second row: a group's sums await scaling
@@ -866,7 +867,7 @@ __device__ __forceinline__ void large_m_tile(
             for (int i = 0; i <= NCOPY; ++i) copy(Dst, gnext, i);
             return;
         }
-        if (STAGGER && wm == 1 && pend) {
+        if (STAGGER && late && pend) {
             scale_into_total(sprev);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -926,7 +927,7 @@ __device__ __forceinline__ void large_m_tile(
                 for (int bb = 0; bb < NBW; ++bb)
                     acc[mi][bb] = mfma_bf16_32x32x16(af[mi], bfr[bb], j == 0 ? cinit[mi] : acc[mi][bb]);
         }
-        if (STAGGER && wm == 1) {
+        if (STAGGER && late) {
 #pragma unroll
             for (int bb = 0; bb < NBW; ++bb) sprev[bb] = scur[bb];
             pend = true;

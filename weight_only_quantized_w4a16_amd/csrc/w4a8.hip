@@ -468,6 +468,9 @@ constexpr int W4A8_NWAVE = 4;
 #endif
 
 static int w4a8_ct(int NT) { return NT % 4 == 0 ? 4 : (NT % 2 == 0 ? 2 : 1); }
+#ifndef QG_W4A8_CT_COVER           // 1: grouped tiles halve their columns for few experts' rows
+#define QG_W4A8_CT_COVER 1
+#endif
 
 #ifndef QG_W4A8_LARGE_MIN          // grouped: the large tile from this mean of rows per non-empty expert
 #define QG_W4A8_LARGE_MIN 17       // measured, ms small / large: mean 20 rows 5.60 / 5.40, 24 6.24 / 5.67,
@@ -522,7 +525,7 @@ void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int
     }
     const int R = w4a16_grouped_rows_per_item(E, T);
     const int max_items = w4a16_grouped_max_items(E, T);
-    const int CT = w4a8_ct(NT);
+    const int CT = QG_W4A8_CT_COVER ? grouped_small_ct(NT, E, T, w4a8_ct(NT)) : w4a8_ct(NT);
     if (T >= QG_W4A8_ONE_WAVE_MIN_T) {
         // many routed rows: one wave per workgroup over the whole K (no K split,
         // no LDS reduction) and many more workgroups in flight; measured at top-8
@@ -590,7 +593,7 @@ void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, co
     const int NT = N / 16;
     const int R = w4a16_grouped_rows_per_item(E, T);
     const int max_items = w4a16_grouped_max_items(E, T);
-    const int CT = w4a8_ct(NT);
+    const int CT = QG_W4A8_CT_COVER ? grouped_small_ct(NT, E, T, w4a8_ct(NT)) : w4a8_ct(NT);
     const size_t lds = (size_t)R * (K + 16);
     auto go = [&](auto mt, auto ct, auto nwave, auto cpl) {
         constexpr int MT_ = decltype(mt)::value, CT_ = decltype(ct)::value;

@@ -94,12 +94,14 @@ def test_grouped_many_experts(ops, E, T, K, N):
     _check(y, a, offsets, w_list, nonempty[:: max(1, len(nonempty) // 8)] + [nonempty[-1]])
 
 
-@pytest.mark.parametrize("B", [1, 16, 64, 256, 1024])
+@pytest.mark.parametrize("B", [1, 2, 4, 5, 16, 64, 256, 1024])
 @pytest.mark.parametrize("name,K,N", synth.QWEN3_MOE_SHAPES)
 def test_grouped_qwen3_moe_shapes(ops, B, name, K, N):
     """128 experts of the real shape, seeded top-8 routing of B tokens; the
     weights are drawn on the device and the checked experts' bf16 bits copied
-    back for the oracle."""
+    back for the oracle.  B = 1 .. 5 cross the launch rules of the small tiles
+    (two column tiles per workgroup for one or two tokens, two waves per
+    workgroup once the grid covers the CUs)."""
     E, k = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK
     announce(f"qgemm_w4a16_grouped qwen3 {name} B={B} E={E} K={K} N={N}")
     token, offsets = synth.moe_routing(B, E, k, seed=B)

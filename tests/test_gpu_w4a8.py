@@ -104,7 +104,7 @@ def test_w4a8_grouped_ragged(ops, sizes, K, N):
 
 
 @pytest.mark.parametrize("j", [0, 1])
-@pytest.mark.parametrize("B", [1, 16, 64, 1024])
+@pytest.mark.parametrize("B", [1, 8, 16, 64, 1024])
 def test_w4a8_grouped_qwen3_shapes(ops, B, j):
     E, k = synth.QWEN3_MOE_EXPERTS, synth.QWEN3_MOE_TOPK
     name, K, N = synth.QWEN3_MOE_SHAPES[j]

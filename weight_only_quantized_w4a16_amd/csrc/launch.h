@@ -55,6 +55,7 @@ constexpr int kGroupedMaxExperts = 1024;
 int w4a16_grouped_max_items(int E, int T);
 int w4a16_grouped_rows_per_item(int E, int T);
 int grouped_small_ct(int NT, int E, int T, int ct);   // column tiles per small grouped workgroup
+bool grouped_two_waves(int wg_per_expert, int E, int T);   // two waves per small grouped workgroup
 size_t w4a16_grouped_workspace_bytes(int E, int T, int K);
 void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uint32_t* wq,
                                 const uint16_t* sc, uint16_t* y, int E, int T, int N, int K,

@@ -1219,10 +1219,9 @@ struct GroupedArgs {
     int E, T, max_items;
 };
 
-template <int MT, int CT>
+template <int MT, int CT, int NWAVE>
 static void launch_grouped_mt(const uint16_t* a, const GroupedArgs& g, const uint32_t* wq,
                               const uint16_t* sc, uint16_t* y, int N, int K, hipStream_t s) {
-    constexpr int NWAVE = QG_GR_NWAVE;
     constexpr int U = MT == 1 ? QG_SM_U : 1;
     constexpr bool PIPE = MT <= 2 && CT <= 2;
     hipLaunchKernelGGL((w4a16_grouped_kernel<MT, CT, NWAVE, U, PIPE>), dim3(N / 16 / CT, g.max_items),
@@ -1246,6 +1245,22 @@ int grouped_small_ct(int NT, int E, int T, int ct) {
     if (ct >= 4 && NT % (ct / 2) == 0 && (long long)(NT / ct) * active < (long long)QG_GR_CT_COVER * device_cu_count())
         return ct / 2;
     return ct;
+}
+
+// Two waves per workgroup (each half of K) instead of four once the grid holds
+// at least QG_GR_NW2_COVER / 2 workgroups per CU: with that many workgroups the
+// wider K split buys no parallelism and costs its LDS reduction.  Measured on
+// the same step (top-8 of 128), 4 vs 2 waves, ms: gate_up at B = 4 / 5 / 8
+// 0.60 / 0.72 / 0.95 vs 0.67 / 0.70 / 0.90 (24 workgroups per expert: 3, 3.75
+// and 6 per CU), down 0.39 / 0.51 / 0.62 vs 0.37 / 0.42 / 0.57; the whole step
+// at B = 16 / 64 / 128 / 256 / 320 -2 / -9 / -6 / -2 / -5 %.
+#ifndef QG_GR_NW2_COVER
+#define QG_GR_NW2_COVER 7
+#endif
+bool grouped_two_waves(int wg_per_expert, int E, int T) {
+    const long long active = T < E ? T : E;
+    return QG_GR_NW2_COVER > 0 &&
+           2LL * wg_per_expert * active >= (long long)QG_GR_NW2_COVER * device_cu_count();
 }
 
 
@@ -1280,18 +1295,20 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
     const int max_items = grouped_max_items(E, T);
     const GroupedArgs g{offsets, E, T, max_items};
     const int NT = N / 16;
-    int ct = QG_GR_CT ? QG_GR_CT : small_ct(NT);
+    int ct = std::min(QG_GR_CT ? QG_GR_CT : small_ct(NT), 4);
     while (NT % ct) ct >>= 1;
     ct = grouped_small_ct(NT, E, T, ct);
+    const bool two = grouped_two_waves(NT / ct, E, T);
     auto go = [&](auto mt) {
         constexpr int M_T = decltype(mt)::value;
-        // the LDS reduction holds NWAVE * CT * MT KiB
-        constexpr bool fits8 = QG_GR_NWAVE * 8 * M_T <= 64;
-        if (ct == 8 && fits8)
-            launch_grouped_mt<M_T, fits8 ? 8 : 4>(a, g, wq, sc, y, N, K, s);
-        else if (ct >= 4) launch_grouped_mt<M_T, 4>(a, g, wq, sc, y, N, K, s);
-        else if (ct == 2) launch_grouped_mt<M_T, 2>(a, g, wq, sc, y, N, K, s);
-        else              launch_grouped_mt<M_T, 1>(a, g, wq, sc, y, N, K, s);
+        auto by_nw = [&](auto nw) {
+            constexpr int NW = decltype(nw)::value;
+            if (ct >= 4) launch_grouped_mt<M_T, 4, NW>(a, g, wq, sc, y, N, K, s);
+            else if (ct == 2) launch_grouped_mt<M_T, 2, NW>(a, g, wq, sc, y, N, K, s);
+            else              launch_grouped_mt<M_T, 1, NW>(a, g, wq, sc, y, N, K, s);
+        };
+        if (two) by_nw(ic<2>{});
+        else by_nw(ic<QG_GR_NWAVE>{});
     };
     if (MT == 1) go(ic<1>{});
     else if (MT == 2) go(ic<2>{});

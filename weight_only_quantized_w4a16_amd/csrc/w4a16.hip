@@ -1189,7 +1189,7 @@ int w4a16_grouped_max_items(int E, int T) { return T == 0 ? 0 : grouped_max_item
 // routed-expert step, 64- vs 128-row items: mean 40 rows 6.35 / 6.64 ms,
 // 48 7.74 / 7.46, 64 8.88 / 8.64, 96 11.75 / 10.39, 128 14.5 / 13.6.
 #ifndef QG_GR_LARGE_MIN            // mean rows per non-empty expert from which it runs
-#define QG_GR_LARGE_MIN 25         // measured: mean 28 / 32 rows 6.0 / 7.07 ms small, 5.79 / 6.13 large
+#define QG_GR_LARGE_MIN 30         // measured (two-wave small tiles): mean 25 / 28 / 32 rows 5.42 / 5.70 / 6.65 ms small, 5.55 / 5.78 / 6.05 large
 #endif
 #ifndef QG_GR_BM128_MIN            // mean rows per non-empty expert from which items hold 128 rows
 #define QG_GR_BM128_MIN 48

@@ -464,8 +464,8 @@ __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
 
 constexpr int W4A8_NWAVE = 4;
 #ifndef QG_W4A8_ONE_WAVE_MIN_T     // grouped: one wave per workgroup from this many routed rows
-#define QG_W4A8_ONE_WAVE_MIN_T 128
-#endif
+#define QG_W4A8_ONE_WAVE_MIN_T 256     // against two waves, ms: B = 16 / 32 / 64 / 128 2.33 / 2.91 / 3.19 / 3.68
+#endif                                 // vs 2.24 / 2.90 / 3.22 / 3.76
 
 static int w4a8_ct(int NT) { return NT % 4 == 0 ? 4 : (NT % 2 == 0 ? 2 : 1); }
 // Below QG_W4A8_ONE_WAVE_MIN_T routed rows the grouped tiles run two waves per
@@ -536,8 +536,8 @@ void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int
     if (T >= QG_W4A8_ONE_WAVE_MIN_T) {
         // many routed rows: one wave per workgroup over the whole K (no K split,
         // no LDS reduction) and many more workgroups in flight; measured at top-8
-        // over 128 experts: B = 16 / 64 / 1024 -4 / -8 / -27 % (B = 1, with a
-        // handful of workgroups, is 26 % slower this way)
+        // over 128 experts, against four waves: B = 16 / 64 / 1024 -4 / -8 / -27 %
+        // (B = 1, with a handful of workgroups, is 26 % slower this way)
         w4a8_dispatch(R / 16, CT, [&](auto mt, auto ct) {
             hipLaunchKernelGGL((w4a8_grouped_kernel<decltype(mt)::value, decltype(ct)::value, 1>),
                                dim3(NT / decltype(ct)::value, max_items), dim3(64), 0, s, qa, sa, offsets,

@@ -463,15 +463,14 @@ __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
 }
 
 constexpr int W4A8_NWAVE = 4;
-#ifndef QG_W4A8_ONE_WAVE_MIN_T     // grouped: one wave per workgroup from this many routed rows
-#define QG_W4A8_ONE_WAVE_MIN_T 256     // against two waves, ms: B = 16 / 32 / 64 / 128 2.33 / 2.91 / 3.19 / 3.68
-#endif                                 // vs 2.24 / 2.90 / 3.22 / 3.76
 
 static int w4a8_ct(int NT) { return NT % 4 == 0 ? 4 : (NT % 2 == 0 ? 2 : 1); }
-// Below QG_W4A8_ONE_WAVE_MIN_T routed rows the grouped tiles run two waves per
-// workgroup instead of four once the grid covers the CUs (the rule of the W4A16
-// grouped tiles); measured on the Qwen3-30B-A3B W4A8 step, ms: B = 5 / 8
-// 1.45 / 1.78 -> 1.41 / 1.69.
+// The grouped tiles run two waves per workgroup instead of four once the grid
+// covers the CUs (the rule of the W4A16 grouped tiles).  Measured on the
+// Qwen3-30B-A3B W4A8 step, ms, four waves / two: B = 5 / 8 1.45 / 1.78 vs
+// 1.41 / 1.69; one wave per workgroup (no K split) / two: B = 16 / 32 / 64 /
+// 128 / 192 / 256 2.33 / 2.91 / 3.19 / 3.68 / 4.57 / 5.64 vs 2.24 / 2.90 /
+// 3.22 / 3.76 / 4.46 / 5.34.
 #ifndef QG_W4A8_NW2
 #define QG_W4A8_NW2 1
 #endif
@@ -480,8 +479,8 @@ static int w4a8_ct(int NT) { return NT % 4 == 0 ? 4 : (NT % 2 == 0 ? 2 : 1); }
 #endif
 
 #ifndef QG_W4A8_LARGE_MIN          // grouped: the large tile from this mean of rows per non-empty expert
-#define QG_W4A8_LARGE_MIN 17       // measured, ms small / large: mean 20 rows 5.60 / 5.40, 24 6.24 / 5.67,
-                                   // 28 7.19 / 5.87, 32 8.09 / 6.06
+#define QG_W4A8_LARGE_MIN 16       // measured (two-wave small tiles), ms small / large: mean 13 rows
+                                   // 4.61 / 4.88, 14 4.87 / 5.01, 15 4.97 / 5.02, 16 5.34 / 5.10
 #endif
 #ifndef QG_W4A8_LARGE_BM           // rows per item and tile of the grouped large path
 #define QG_W4A8_LARGE_BM 64
@@ -533,18 +532,6 @@ void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int
     const int R = w4a16_grouped_rows_per_item(E, T);
     const int max_items = w4a16_grouped_max_items(E, T);
     const int CT = QG_W4A8_CT_COVER ? grouped_small_ct(NT, E, T, w4a8_ct(NT)) : w4a8_ct(NT);
-    if (T >= QG_W4A8_ONE_WAVE_MIN_T) {
-        // many routed rows: one wave per workgroup over the whole K (no K split,
-        // no LDS reduction) and many more workgroups in flight; measured at top-8
-        // over 128 experts, against four waves: B = 16 / 64 / 1024 -4 / -8 / -27 %
-        // (B = 1, with a handful of workgroups, is 26 % slower this way)
-        w4a8_dispatch(R / 16, CT, [&](auto mt, auto ct) {
-            hipLaunchKernelGGL((w4a8_grouped_kernel<decltype(mt)::value, decltype(ct)::value, 1>),
-                               dim3(NT / decltype(ct)::value, max_items), dim3(64), 0, s, qa, sa, offsets,
-                               E, T, wq, sc, y, N, K);
-        });
-        return;
-    }
     if (QG_W4A8_NW2 && grouped_two_waves(NT / CT, E, T)) {
         w4a8_dispatch(R / 16, CT, [&](auto mt, auto ct) {
             hipLaunchKernelGGL((w4a8_grouped_kernel<decltype(mt)::value, decltype(ct)::value, 2>),
@@ -626,7 +613,7 @@ void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, co
             default: go(mt, ct, nwave, ic<4>{}); break;
         }
     };
-    // as the unfused launch: one wave per workgroup from QG_W4A8_ONE_WAVE_MIN_T rows
+    // as the unfused launch: two waves per workgroup once the grid covers the CUs
     auto by_mt_ct = [&](auto nwave) {
         auto by_ct = [&](auto mt) {
             if (CT == 4) by_cpl(mt, ic<4>{}, nwave);
@@ -636,9 +623,7 @@ void launch_qgemm_w4a8_fp8_grouped_dyn(const uint16_t* a, const int* offsets, co
         if (R <= 16) by_ct(ic<1>{});
         else by_ct(ic<2>{});
     };
-    if (T >= QG_W4A8_ONE_WAVE_MIN_T)
-        by_mt_ct(ic<1>{});
-    else if (QG_W4A8_NW2 && grouped_two_waves(NT / CT, E, T))
+    if (QG_W4A8_NW2 && grouped_two_waves(NT / CT, E, T))
         by_mt_ct(ic<2>{});
     else
         by_mt_ct(ic<W4A8_NWAVE>{});

@@ -46,7 +46,8 @@ def _check(y, a_bits, offsets, w_list, experts=None):
 
 @pytest.mark.parametrize("sizes,K,N", [
     ([0, 1, 17, 0, 40, 3, 70, 5], 256, 64),          # mean 17 rows -> 32-row chunks
-    ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48),        # mean <= 16 -> 16-row chunks
+    ([2, 0, 0, 5, 1, 0, 3, 0, 0, 4], 384, 48),        # mean <= 12 -> 16-row chunks
+    ([13, 0, 20, 13, 19], 256, 64),                    # mean 13 -> 32-row chunks (every expert one item)
     ([31, 0, 60, 29, 30], 256, 1040),                  # mean 30 -> 64-row large-M items, 29..31 rows: half idle
     ([31, 0, 45, 20, 29], 256, 1040),                  # mean 25 -> 32-row chunks on the small tiles
     ([100, 60, 0], 384, 272),                          # mean 54 -> 128-row items; 60 rows: second half idle

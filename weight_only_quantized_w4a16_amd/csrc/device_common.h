@@ -207,6 +207,40 @@ __device__ __forceinline__ int xcd_tile(int id, int total) {
     return id < per * NUM_XCD ? (id % NUM_XCD) * per + id / NUM_XCD : id;
 }
 
+// Expert-grouped large tiles on a 1-D grid of NX column tiles x items (items
+// rounded up to a multiple of NUM_XCD): workgroup L takes column tile x and
+// item y such that every column tile of an item runs on one XCD (the one
+// workgroup L % NUM_XCD is dealt to), so the item's activation rows are
+// fetched into one L2 and read by its NX workgroups from there.
+__device__ __forceinline__ void grouped_xcd_item(int L, int NX, int& x, int& y) {
+    const int q = L / NUM_XCD;
+    x = q % NX;
+    y = (q / NX) * NUM_XCD + L % NUM_XCD;
+}
+
+// Column tile x and item y of an expert-grouped workgroup: on a 1-D grid of
+// NX x (items rounded up to NUM_XCD) workgroups through grouped_xcd_item
+// (xcd != 0), else on the 2-D grid (NX, items).
+__device__ __forceinline__ void grouped_xy(int xcd, int NX, int& x, int& y) {
+    if (xcd) {
+        grouped_xcd_item(blockIdx.x, NX, x, y);
+    } else {
+        x = blockIdx.x;
+        y = blockIdx.y;
+    }
+}
+
+// whether the 1-D grid of grouped_xy fits a dispatch (fewer than 2^32 work-items)
+inline int grouped_xcd_fits(int NX, int items, int threads) {
+    const unsigned long long wg = (unsigned long long)NX * ((items + NUM_XCD - 1) / NUM_XCD * NUM_XCD);
+    return wg * (unsigned long long)threads < (1ull << 32) ? 1 : 0;
+}
+
+// the grid of grouped_xy
+inline dim3 grouped_grid(int xcd, int NX, int items) {
+    return xcd ? dim3((unsigned)(NX * ((items + NUM_XCD - 1) / NUM_XCD * NUM_XCD))) : dim3(NX, items);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -1041,22 +1041,31 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
     large_m_tile<NS, NB, BM, WR>(a, wq, sc, corr, y, M, Mp, N, K, S, part, cnt, tiles, split, tile);
 }
 
-// Expert-grouped, many rows per expert: one work item (expert, up to BM rows)
-// per blockIdx.y, the expert's BM x 128·NB column tiles along blockIdx.x; the
-// offset terms of all routed rows come from one pre-pass (corr[g][row], rows
+// Expert-grouped, many rows per expert: each workgroup takes one work item
+// (expert, up to BM rows) and one of the expert's BM x 128·NB column tiles
+// (grouped_xy); the offset terms of all routed rows come from one pre-pass (corr[g][row], rows
 // padded so that a 128-row read from any item start stays inside).
+// The column tiles of an item run on one XCD (grouped_xy), which then reads
+// the item's activation rows into its L2 once: MoE W4A16 step at B = 480 /
+// 512 / 768 / 1024 -3 to -5 % (W4A8 large tiles -1.5 to -3 %; the small
+// grouped tiles gain nothing this way, and lose 5 % at B = 1).
+#ifndef QG_GR_XCD
+#define QG_GR_XCD 1
+#endif
 template <int NS, int NB, int BM>
 __global__ __launch_bounds__(512) void w4a16_grouped_large_kernel(
     const uint16_t* __restrict__ a, const int* __restrict__ offsets, int E, int T,
     const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, const float* __restrict__ corr,
-    uint16_t* __restrict__ y, int Tp, int N, int K) {
+    uint16_t* __restrict__ y, int Tp, int N, int K, int NX, int xcd) {
+    int tx, ty;
+    grouped_xy(xcd, NX, tx, ty);
+    if (!xcd) tx = xcd_tile(tx, NX);
     GroupedItem item;
-    if (!grouped_item<BM>(offsets, E, T, blockIdx.y, item)) return;   // uniform: the whole workgroup leaves
+    if (!grouped_item<BM>(offsets, E, T, ty, item)) return;   // uniform: the whole workgroup leaves
     const size_t words = (size_t)(K / 8) * N;
     const size_t nsc = (size_t)(K / 128) * N;
     large_m_tile<NS, NB, BM>(a + (size_t)item.r0 * K, wq + item.e * words, sc + item.e * nsc, corr + item.r0,
-                         y + (size_t)item.r0 * N, item.rows, Tp, N, K, 1, nullptr, nullptr, gridDim.x, 0,
-                         xcd_tile(blockIdx.x, gridDim.x));
+                         y + (size_t)item.r0 * N, item.rows, Tp, N, K, 1, nullptr, nullptr, NX, 0, tx);
 }
 
 // ---------------------------------------------------------------------------
@@ -1287,9 +1296,10 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
                            a, T, Tp, K, corr);
         auto go = [&](auto nb, auto bm) {
             constexpr int NB = decltype(nb)::value, BM = decltype(bm)::value;
-            hipLaunchKernelGGL((w4a16_grouped_large_kernel<QG_LM_NS, NB, BM>),
-                               dim3((N + 128 * NB - 1) / (128 * NB), max_items), dim3(512), 0, s, a, offsets, E, T,
-                               wq, sc, corr, y, Tp, N, K);
+            const int NX = (N + 128 * NB - 1) / (128 * NB);
+            const int xcd = QG_GR_XCD && grouped_xcd_fits(NX, max_items, 512);
+            hipLaunchKernelGGL((w4a16_grouped_large_kernel<QG_LM_NS, NB, BM>), grouped_grid(xcd, NX, max_items),
+                               dim3(512), 0, s, a, offsets, E, T, wq, sc, corr, y, Tp, N, K, NX, xcd);
         };
         if (N >= 1024) {
             if (R == 128) go(ic<2>{}, ic<128>{});

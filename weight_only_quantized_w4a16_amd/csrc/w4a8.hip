@@ -287,11 +287,14 @@ __global__ __launch_bounds__(NWAVE * 64) void w4a8_grouped_dyn_kernel(
 // byte 0x88 gives the offset term of each 16-row block, each 16x16 block's
 // group sum starts from it, and 512 * s_g scales it into the fp32 total.
 // ---------------------------------------------------------------------------
+#ifndef QG_W4A8_XCD                // 1: the column tiles of an item share an XCD (grouped_xy)
+#define QG_W4A8_XCD 1
+#endif
 template <int NS, int BM>
 __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa, const int* __restrict__ offsets, int E,
     int T, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ sc, uint16_t* __restrict__ y, int N,
-    int K) {
+    int K, int NX, int xcd) {
     constexpr int NTB = 16;                      // column tiles per workgroup (256 columns)
     constexpr int NI = 4;                        // column tiles per wave
     constexpr int MI = BM / 32;                  // 16-row blocks per wave
@@ -313,8 +316,11 @@ __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
         else return S3x[0];
     };
 
+    int tx, ty;
+    grouped_xy(xcd, NX, tx, ty);
+    if (!xcd) tx = xcd_tile(tx, NX);
     GroupedItem item;
-    if (!grouped_item<BM>(offsets, E, T, blockIdx.y, item)) return;   // uniform: the whole workgroup leaves
+    if (!grouped_item<BM>(offsets, E, T, ty, item)) return;   // uniform: the whole workgroup leaves
     const int e = item.e;
     const int r0 = item.r0;
     const int rows = item.rows;
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(512) void w4a8_grouped_large_kernel(
     const int wn = wave & 3;                     // 0..3: 64-column quarter
     const int col = lane & 15;
     const int q = lane >> 4;
-    const int nt0 = xcd_tile(blockIdx.x, gridDim.x) * NTB;
+    const int nt0 = tx * NTB;
     const uint8_t* a = qa + (size_t)r0 * K;
     const uint32_t* w = wq + (size_t)e * ((size_t)(K / 8) * N);
     const uint16_t* s = sc + (size_t)e * ((size_t)G * N);
@@ -525,8 +531,10 @@ void launch_qgemm_w4a8_fp8_grouped(const uint8_t* qa, const float* sa, const int
         // many rows per expert: 64-row items on the large tile
         constexpr int R = QG_W4A8_LARGE_BM;
         const int max_items = (T < E ? T : E) + (T + R - 1) / R;
-        hipLaunchKernelGGL((w4a8_grouped_large_kernel<QG_W4A8_LARGE_NS, R>), dim3((N + 255) / 256, max_items),
-                           dim3(512), 0, s, qa, sa, offsets, E, T, wq, sc, y, N, K);
+        const int NX = (N + 255) / 256;
+        const int xcd = QG_W4A8_XCD && grouped_xcd_fits(NX, max_items, 512);
+        hipLaunchKernelGGL((w4a8_grouped_large_kernel<QG_W4A8_LARGE_NS, R>), grouped_grid(xcd, NX, max_items),
+                           dim3(512), 0, s, qa, sa, offsets, E, T, wq, sc, y, N, K, NX, xcd);
         return;
     }
     const int R = w4a16_grouped_rows_per_item(E, T);

@@ -748,7 +748,20 @@ __global__ __launch_bounds__(512) void w8a8_large_m_kernel(
     if (tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-static int f8_small_ct(int NT) { return (NT % 2 == 0 && NT >= 1024) ? 2 : 1; }
+#ifndef QG_F8_CT2_MIN              // two column tiles per small-M workgroup from this many tiles
+#define QG_F8_CT2_MIN 1024
+#endif
+#ifndef QG_F8_SM_NWAVE             // waves per small-M workgroup (measured: 4 loses 1-7 % from B = 4)
+#define QG_F8_SM_NWAVE 8
+#endif
+// k-tiles per pipelined item of one 16-row block; measured on the FP8 decode
+// step (129 GEMMs, per-token quantization included), ms, U = 1 / 2 / 4 / 8:
+// B = 1 1.87 / 1.76 / 1.84 / 2.35, B = 4 2.23 / 2.13 / 2.20 / 2.47,
+// B = 16 2.51 / 2.49 / 2.52 / 2.68
+#ifndef QG_F8_SM_U1
+#define QG_F8_SM_U1 2
+#endif
+static int f8_small_ct(int NT) { return (NT % 2 == 0 && NT >= QG_F8_CT2_MIN) ? 2 : 1; }
 
 
 // Large-M plan: tile width, K split and workspace layout (slots | counters).
@@ -842,8 +855,8 @@ size_t w8a8_workspace_bytes(int M, int N, int K) {
 template <class Fmt, int MT, int CT>
 static void launch_small(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                          uint16_t* y, int M, int N, int K, hipStream_t st) {
-    constexpr int NWAVE = 8;
-    constexpr int U = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
+    constexpr int NWAVE = QG_F8_SM_NWAVE;
+    constexpr int U = MT == 1 ? QG_F8_SM_U1 : (MT == 2 ? 2 : 1);
     hipLaunchKernelGGL((w8a8_small_m_kernel<Fmt, MT, CT, NWAVE, U>), dim3(N / 16 / CT),
                        dim3(NWAVE * 64), 0, st, a, sa, w, sw, y, M, N, K);
 }
@@ -953,8 +966,8 @@ const char* w8a8_dyn_kernel_for(int M, int N, int K) {
 template <class Fmt, int CT, int CPT>
 static void launch_dyn_cpt(const uint16_t* a, const uint8_t* w, const float* sw, uint16_t* y, int M, int N,
                            int K, hipStream_t st) {
-    constexpr int NWAVE = 8;
-    constexpr int U = 4;                     // as the small-M launch for one m-tile
+    constexpr int NWAVE = QG_F8_SM_NWAVE;
+    constexpr int U = QG_F8_SM_U1;           // as the small-M launch for one m-tile
     static std::atomic<uint64_t> lds_set{0};
     allow_dynamic_lds(reinterpret_cast<const void*>(&w8a8_small_m_dyn_kernel<Fmt, CT, NWAVE, U, CPT>),
                       CPT * 8 * 64 * 8 + 16 * DYN_MAX_M, lds_set);   // M * K <= CPT * 4096 codes

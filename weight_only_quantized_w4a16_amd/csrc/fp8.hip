@@ -134,18 +134,21 @@ __global__ __launch_bounds__(256) void quant_act_per_token_reg_kernel(const uint
     }
 }
 
-// rows up to 64 x 16 chunks (K <= 8192) on one wave each, up to 256 x 16
-// chunks (K <= 32768) on one workgroup each, longer rows on the two-pass kernel
+// rows up to 64 x 2 chunks (K <= 1024) on one wave each, up to 256 x 16
+// chunks (K <= 32768) on one 4-wave workgroup each (measured against one wave
+// per row up to K = 8192: FP8 decode step with the separate quantization,
+// B = 16 / 64 / 256, 2.48 / 4.15 / 4.97 -> 2.34 / 4.00 / 4.81 ms), longer
+// rows on the two-pass kernel
 template <class Fmt>
 static void launch_quant_act(const uint16_t* a, int M, int K, uint8_t* q, float* s, hipStream_t st) {
     const int chunks = K / 8;
     const dim3 blk(256);
-    if (chunks <= 64 * 4)
-        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 64, 4>), dim3((M + 3) / 4), blk, 0, st, a, M, K, q, s);
-    else if (chunks <= 64 * 8)
-        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 64, 8>), dim3((M + 3) / 4), blk, 0, st, a, M, K, q, s);
-    else if (chunks <= 64 * 16)
-        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 64, 16>), dim3((M + 3) / 4), blk, 0, st, a, M, K, q, s);
+    if (chunks <= 64 * 2)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 64, 2>), dim3((M + 3) / 4), blk, 0, st, a, M, K, q, s);
+    else if (chunks <= 256 * 2)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 256, 2>), dim3(M), blk, 0, st, a, M, K, q, s);
+    else if (chunks <= 256 * 4)
+        hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 256, 4>), dim3(M), blk, 0, st, a, M, K, q, s);
     else if (chunks <= 256 * 8)
         hipLaunchKernelGGL((quant_act_per_token_reg_kernel<Fmt, 256, 8>), dim3(M), blk, 0, st, a, M, K, q, s);
     else if (chunks <= 256 * 16)

@@ -50,7 +50,8 @@ def _check(y, a_bits, offsets, w_list, experts=None):
     ([13, 0, 20, 13, 19], 256, 64),                    # mean 13 -> 32-row chunks (every expert one item)
     ([31, 0, 60, 29, 30], 256, 1040),                  # mean 30 -> 64-row large-M items, 29..31 rows: half idle
     ([31, 0, 45, 20, 29], 256, 1040),                  # mean 25 -> 32-row chunks on the small tiles
-    ([100, 60, 0], 384, 272),                          # mean 54 -> 128-row items; 60 rows: second half idle
+    ([100, 60, 0], 384, 272),                          # mean 54 -> 64-row items on 64 x 128 tiles, ragged N
+    ([160, 60, 0], 384, 272),                          # mean 74 -> 128-row items; 60 / 32 rows: second half idle
     ([90, 33, 0, 65, 128], 128, 16),                   # mean 79 -> 128-row large-M items
     ([0, 0, 200, 0], 512, 272),                        # one expert owns every row (large-M)
     ([5], 256, 48),                                    # a single expert, few rows

@@ -1052,6 +1052,7 @@ __global__ __launch_bounds__(512) void w4a16_large_m_kernel(
 #ifndef QG_GR_XCD
 #define QG_GR_XCD 1
 #endif
+
 template <int NS, int NB, int BM>
 __global__ __launch_bounds__(512) void w4a16_grouped_large_kernel(
     const uint16_t* __restrict__ a, const int* __restrict__ offsets, int E, int T,
@@ -1198,19 +1199,20 @@ static int grouped_max_items(int E, int T) {
 
 int w4a16_grouped_max_items(int E, int T) { return T == 0 ? 0 : grouped_max_items(E, T); }
 
-// Many rows per expert: the large-M tile (64 or 128 x 256 per workgroup, the
-// activation tile shared by 256 columns) instead of the small-M tile, whose
-// workgroups each re-read all of their rows' activations for 64 columns.
-// Items of 64 rows up to a mean of 47 rows per expert, then of 128 rows: an
-// expert's weights are then streamed once for up to 128 rows, and the waves
-// of an item's empty second half only copy.  Measured on the Qwen3-30B-A3B
-// routed-expert step, 64- vs 128-row items: mean 40 rows 6.35 / 6.64 ms,
-// 48 7.74 / 7.46, 64 8.88 / 8.64, 96 11.75 / 10.39, 128 14.5 / 13.6.
+// Many rows per expert: the large-M tile (64 x 128 or 128 x 256 per
+// workgroup, the activation tile shared by its columns) instead of the small-M
+// tile, whose workgroups each re-read all of their rows' activations for 64
+// columns.  Items of 64 rows up to a mean of 71 rows per expert, then of 128
+// rows: an expert's weights are then streamed once for up to 128 rows, and the
+// waves of an item's empty second half only copy.  Measured on the
+// Qwen3-30B-A3B routed-expert step, ms, 64-row (64 x 128 tiles) vs 128-row
+// items: mean 48 rows 7.12 / 7.51, 56 7.53 / 7.82, 64 8.84 / 8.93, 72 9.52 /
+// 9.57 (with 64 x 256 tiles the 64-row items lost from a mean of 48).
 #ifndef QG_GR_LARGE_MIN            // mean rows per non-empty expert from which it runs
 #define QG_GR_LARGE_MIN 30         // measured (two-wave small tiles): mean 25 / 28 / 32 rows 5.42 / 5.70 / 6.65 ms small, 5.55 / 5.78 / 6.05 large
 #endif
 #ifndef QG_GR_BM128_MIN            // mean rows per non-empty expert from which items hold 128 rows
-#define QG_GR_BM128_MIN 48
+#define QG_GR_BM128_MIN 72
 #endif
 static bool grouped_large(int E, int T) {
     const int active = T < E ? T : E;
@@ -1301,13 +1303,13 @@ void launch_qgemm_w4a16_grouped(const uint16_t* a, const int* offsets, const uin
             hipLaunchKernelGGL((w4a16_grouped_large_kernel<QG_LM_NS, NB, BM>), grouped_grid(xcd, NX, max_items),
                                dim3(512), 0, s, a, offsets, E, T, wq, sc, corr, y, Tp, N, K, NX, xcd);
         };
-        if (N >= 1024) {
-            if (R == 128) go(ic<2>{}, ic<128>{});
-            else go(ic<2>{}, ic<64>{});
-        } else {
-            if (R == 128) go(ic<1>{}, ic<128>{});
-            else go(ic<1>{}, ic<64>{});
-        }
+        // 128-row items on 256-column tiles from N = 1024; 64-row items on
+        // 128-column tiles (twice the workgroups per item, the same work per
+        // weight unpacked): MoE step at B = 480 / 640 / 704 / 768 / 896 -3 / -4 /
+        // -13 / -5 / -4 % against 64 x 256 tiles and 128-row items from 48 rows
+        if (R == 128 && N >= 1024) go(ic<2>{}, ic<128>{});
+        else if (R == 128) go(ic<1>{}, ic<128>{});
+        else go(ic<1>{}, ic<64>{});
         return;
     }
     const int MT = grouped_mt(E, T);

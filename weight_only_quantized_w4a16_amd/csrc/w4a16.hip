@@ -1407,6 +1407,12 @@ void* noalloc_scratch() {
 #ifndef QG_DK_MAX_U               // groups per request (the ring holds D * U KiB per wave)
 #define QG_DK_MAX_U 2
 #endif
+#ifndef QG_DK_ONE_D               // ring depth, whole-K wide outputs with one strip per CU
+#define QG_DK_ONE_D 4
+#endif
+#ifndef QG_DK_ONE_MAX_U           // groups per request, the same launches
+#define QG_DK_ONE_MAX_U 1
+#endif
 #ifndef QG_DK_LDS_BUDGET
 #define QG_DK_LDS_BUDGET (144 * 1024)
 #endif
@@ -1497,8 +1503,13 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
             }
             if (per_cu < 1) continue;
             c.S = 1; c.KW = kw; c.NS = NS;
-            c.D = kw == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D;
-            c.U = largest_u(G / kw, ring_umax(c.D));
+            // one wave per tile: with one strip per CU (a wave streams one or
+            // two tiles) one group per request in a 4-deep ring, else two in a
+            // 3-deep one (measured: gate_up at B = 1..16 -2 to -4 %, 70B gate_up
+            // at B = 1 -1 %; the LM heads, two strips per CU, lose 1 % with it)
+            const bool one = kw == 1 && per_cu == 1;
+            c.D = one ? QG_DK_ONE_D : kw == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D;
+            c.U = largest_u(G / kw, one ? std::min(ring_umax(c.D), QG_DK_ONE_MAX_U) : ring_umax(c.D));
             c.lds = lds; c.ok = true;
             return c;
         }
@@ -1586,7 +1597,10 @@ static void launch_decode(const uint16_t* a, const uint32_t* wq, const uint16_t*
         case 8: launch_decode_u<8, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
         case 4: launch_decode_u<4, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
         case 2: launch_decode_u<2, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
-        default: launch_decode_u<1, QG_DK_WIDE_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        default:
+            if (c.D == QG_DK_ONE_D) launch_decode_u<1, QG_DK_ONE_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            else launch_decode_u<1, QG_DK_WIDE_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            break;
     }
 }
 
@@ -1730,8 +1744,7 @@ const char* w4a16_kernel_for(int M, int N, int K) {
     const DecodeCfg dc = decode_cfg(M, N, K);
     if (dc.ok) {
         const int u = dc.U > 16 / dc.D ? 1 : dc.U;   // the instantiation launch_decode_u picks
-        snprintf(buf, sizeof buf, "w4a16_decode_kernel<%d, %d, %d> S=%d", dc.KW, u,
-                 dc.KW == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D, dc.S);
+        snprintf(buf, sizeof buf, "w4a16_decode_kernel<%d, %d, %d> S=%d", dc.KW, u, dc.D, dc.S);
     } else if (M <= 64 && !use_large_m(M, N, K)) {
         snprintf(buf, sizeof buf, "w4a16_small_m_kernel<%d, %d>", M <= 16 ? 1 : M <= 32 ? 2 : 4,
                  small_ct(N / 16));

@@ -1407,6 +1407,12 @@ void* noalloc_scratch() {
 #ifndef QG_DK_MAX_U               // groups per request (the ring holds D * U KiB per wave)
 #define QG_DK_MAX_U 2
 #endif
+#ifndef QG_DK_WIDE_KW_D           // ring depth, whole-K wide outputs with several waves per tile
+#define QG_DK_WIDE_KW_D 3
+#endif
+#ifndef QG_DK_ONE_MAX_TPC         // one strip per CU below this many column tiles per CU
+#define QG_DK_ONE_MAX_TPC 32
+#endif
 #ifndef QG_DK_ONE_D               // ring depth, whole-K wide outputs with one strip per CU
 #define QG_DK_ONE_D 4
 #endif
@@ -1489,10 +1495,11 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
         for (int kw = kw0; kw >= 1; kw >>= 1) {
             if (G % kw) continue;
             // strips: as many as the LDS allows resident, up to WIDE_PER_CU per CU;
-            // one per CU when each CU gets 4..15 tiles (measured: gate_up at
-            // B = 4 / 8 -4 / -7 %; the LM head with 31 tiles per CU and 70B qkv
-            // with 2.5 lose 1-26 %)
-            int per_cu = (NT >= 4 * cus && NT < 16 * cus) ? 1 : QG_DK_WIDE_PER_CU;
+            // one per CU when each CU gets 4..31 tiles (measured: gate_up at
+            // B = 4 / 8 -4 / -7 %; 70B qkv with 2.5 tiles per CU loses up to 26 %;
+            // the LM heads, 31 tiles per CU, -1.5 to -4 % at B = 1..8 once the
+            // one-strip launches stream one group per request)
+            int per_cu = (NT >= 4 * cus && NT < QG_DK_ONE_MAX_TPC * cus) ? 1 : QG_DK_WIDE_PER_CU;
             size_t lds = 0;
             int NS = 0;
             for (; per_cu >= 1; --per_cu) {
@@ -1507,8 +1514,11 @@ static DecodeCfg decode_cfg(int M, int N, int K) {
             // two tiles) one group per request in a 4-deep ring, else two in a
             // 3-deep one (measured: gate_up at B = 1..16 -2 to -4 %, 70B gate_up
             // at B = 1 -1 %; the LM heads, two strips per CU, lose 1 % with it)
+            // several waves per tile (70B qkv / o / down at B = 1): a 3-deep ring
+            // (measured -3 / -4 / -9 % on 70B down / qkv / o; the K-split
+            // launches lose 2-5 % with it and keep 4)
             const bool one = kw == 1 && per_cu == 1;
-            c.D = one ? QG_DK_ONE_D : kw == 1 ? QG_DK_WIDE_D : QG_DK_NARROW_D;
+            c.D = one ? QG_DK_ONE_D : kw == 1 ? QG_DK_WIDE_D : QG_DK_WIDE_KW_D;
             c.U = largest_u(G / kw, one ? std::min(ring_umax(c.D), QG_DK_ONE_MAX_U) : ring_umax(c.D));
             c.lds = lds; c.ok = true;
             return c;
@@ -1594,9 +1604,18 @@ static void launch_decode(const uint16_t* a, const uint32_t* wq, const uint16_t*
                           int M, int N, int K, const DecodeCfg& c, void* ws, hipStream_t s) {
     const int NS = c.NS;
     switch (c.KW) {
-        case 8: launch_decode_u<8, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
-        case 4: launch_decode_u<4, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
-        case 2: launch_decode_u<2, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s); break;
+        case 8:
+            if (c.D == QG_DK_WIDE_KW_D) launch_decode_u<8, QG_DK_WIDE_KW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            else launch_decode_u<8, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            break;
+        case 4:
+            if (c.D == QG_DK_WIDE_KW_D) launch_decode_u<4, QG_DK_WIDE_KW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            else launch_decode_u<4, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            break;
+        case 2:
+            if (c.D == QG_DK_WIDE_KW_D) launch_decode_u<2, QG_DK_WIDE_KW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            else launch_decode_u<2, QG_DK_NARROW_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
+            break;
         default:
             if (c.D == QG_DK_ONE_D) launch_decode_u<1, QG_DK_ONE_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);
             else launch_decode_u<1, QG_DK_WIDE_D>(a, wq, sc, y, M, N, K, c, NS, ws, s);

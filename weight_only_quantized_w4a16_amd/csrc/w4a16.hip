@@ -1239,11 +1239,25 @@ struct GroupedArgs {
     int E, T, max_items;
 };
 
+#ifndef QG_GR_PIPE_MAX_CT          // double-buffered items up to this many column tiles
+#define QG_GR_PIPE_MAX_CT 2
+#endif
+#ifndef QG_GR_U                    // groups per item, 16-row grouped items
+#define QG_GR_U QG_SM_U
+#endif
+// double-buffered items (one or two column tiles: a batch of a few tokens)
+// take one group each; measured on the MoE step, W4A16, ms: B = 1 / 2 / 3 / 4
+// 0.535 / 0.726 / 0.90 / 0.99 -> 0.509 / 0.699 / 0.90 / 0.99 (one group per
+// four-tile item instead of two: B = 2..64 +11 to +40 %; four-tile items
+// double-buffered: B = 16 / 64 +9 / +13 %)
+#ifndef QG_GR_PIPE_U
+#define QG_GR_PIPE_U 1
+#endif
 template <int MT, int CT, int NWAVE>
 static void launch_grouped_mt(const uint16_t* a, const GroupedArgs& g, const uint32_t* wq,
                               const uint16_t* sc, uint16_t* y, int N, int K, hipStream_t s) {
-    constexpr int U = MT == 1 ? QG_SM_U : 1;
-    constexpr bool PIPE = MT <= 2 && CT <= 2;
+    constexpr bool PIPE = MT <= 2 && CT <= QG_GR_PIPE_MAX_CT;
+    constexpr int U = MT == 1 ? (PIPE ? QG_GR_PIPE_U : QG_GR_U) : 1;
     hipLaunchKernelGGL((w4a16_grouped_kernel<MT, CT, NWAVE, U, PIPE>), dim3(N / 16 / CT, g.max_items),
                        dim3(NWAVE * 64), 0, s, a, g.offsets, g.E, g.T, wq, sc, y, N, K);
 }
